@@ -1,0 +1,37 @@
+"""Plain CPU oracle for chunked prefill attention over a paged KV cache.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path (the HIP library and
+its Python binding) imports, calls or links this package; only the tests,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` do.
+
+It computes, in float64 with numpy, exactly what the pages define:
+
+* ``attention``: gather pages into contiguous K/V through the block table,
+  then causal softmax(Q K^T / sqrt(d)) V with grouped-query heads
+  (issue "Metal: paged-KV prefill is 4.43x slower than contiguous KV at 32K",
+  TL;DR and "Results": paged and contiguous KV are the same computation, only
+  the storage differs).
+* the split form: the key axis cut into ranges, one partial per range, merged
+  by log-sum-exp (PR "perf: scale prefill attention splits with GPU cores on
+  Apple7/8", "What changed" and "Testing": the reduce sums S partials).
+* ``rules``: the page's split-count rule and piece-size rule, transcribed from
+  the same PR ("What changed" and the explanatory note below "Testing").
+
+Every function is pinned by ``tests/test_oracle_pins.py`` against brute force,
+closed forms, torch's CPU attention with an explicit mask, invariants, and the
+values the PR prints for its split and piece tables.
+"""
+
+from .attention import (  # noqa: F401
+    decode_f16,
+    decode_bf16,
+    gather_pages,
+    causal_attention,
+    paged_causal_attention,
+    page_aligned_split_ranges,
+    split_partials,
+    merge_partials,
+    split_causal_attention,
+    causal_attention_rows,
+)
+from .rules import page_split_rule, page_piece_rows  # noqa: F401

@@ -1,0 +1,136 @@
+"""Seeded synthetic inputs for chunked prefill attention over a paged KV cache.
+
+This module only draws and lays out inputs; it holds none of the attention
+arithmetic.  The tests, the benchmark and the smoke check feed the same
+arrays to the HIP library and to the CPU oracle.
+
+Recipe (one ``numpy.random.default_rng(seed)`` per case, draws in this order):
+  1. Q  [R][Hq][d]      float32 N(0, 1) * value_scale
+  2. K  [ctx][Hkv][d]   float32 N(0, 1) * value_scale   (logical token order)
+  3. V  [ctx][Hkv][d]   float32 N(0, 1) * value_scale
+  4. the block table: a permutation of the pool ("permute"), the identity
+     ("identity"), or ceil(ctx/ps) pages drawn without replacement from a
+     larger pool ("scatter").
+Values are rounded to fp16 or bf16 (round to nearest even) and both sides
+consume the rounded values.  Pool pages that no logical page uses, and page
+slots past ctx, hold 0xFFFF, a NaN in both fp16 and bf16: a kernel that reads
+them into its result produces NaN.
+"""
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+POISON = np.uint16(0xFFFF)
+
+
+def encode_f16(x):
+    """float32 -> IEEE binary16 bit patterns, round to nearest even."""
+    return np.asarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def encode_bf16(x):
+    """float32 -> bfloat16 bit patterns, round to nearest even (finite inputs)."""
+    bits = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (bits + np.uint64(0x7FFF) + ((bits >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
+    return rounded.astype(np.uint16)
+
+
+ENCODERS = {"f16": encode_f16, "bf16": encode_bf16}
+
+
+@dataclass
+class Case:
+    """One synthetic workload: raw 16-bit patterns plus its shape."""
+    name: str
+    history: int
+    rows: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    page_size: int
+    dtype: str
+    q: np.ndarray            # uint16 [R][Hq][d]
+    k_pages: np.ndarray      # uint16 [pool][ps][Hkv][d]
+    v_pages: np.ndarray      # uint16 [pool][ps][Hkv][d]
+    block_table: np.ndarray  # int32 [ceil(ctx/ps)]
+    k_contig: np.ndarray     # uint16 [ctx][Hkv][d]
+    v_contig: np.ndarray     # uint16 [ctx][Hkv][d]
+    piece_rows: int = 0      # 0: the chunk is one call
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def ctx(self):
+        return self.history + self.rows
+
+
+def make_case(name, history, rows, n_q_heads, n_kv_heads, head_dim, page_size, dtype,
+              seed, value_scale=1.0, table="permute", pool_pages=None, piece_rows=0):
+    """Draw one case following the module recipe."""
+    rng = np.random.default_rng(seed)
+    ctx = history + rows
+    enc = ENCODERS[dtype]
+    q = enc(rng.standard_normal((rows, n_q_heads, head_dim), dtype=np.float32) * np.float32(value_scale))
+    k = enc(rng.standard_normal((ctx, n_kv_heads, head_dim), dtype=np.float32) * np.float32(value_scale))
+    v = enc(rng.standard_normal((ctx, n_kv_heads, head_dim), dtype=np.float32) * np.float32(value_scale))
+    n_pages = -(-ctx // page_size)
+    if table == "identity":
+        pool = n_pages if pool_pages is None else pool_pages
+        bt = np.arange(n_pages, dtype=np.int32)
+    elif table == "permute":
+        pool = n_pages if pool_pages is None else pool_pages
+        bt = rng.permutation(pool)[:n_pages].astype(np.int32)
+    elif table == "scatter":
+        pool = pool_pages
+        bt = rng.choice(pool, size=n_pages, replace=False).astype(np.int32)
+    else:
+        raise ValueError(table)
+    k_pages = lay_out_pages(k, bt, pool, page_size)
+    v_pages = lay_out_pages(v, bt, pool, page_size)
+    return Case(name, history, rows, n_q_heads, n_kv_heads, head_dim, page_size, dtype,
+                q, k_pages, v_pages, bt, k, v, piece_rows)
+
+
+def lay_out_pages(tokens, block_table, pool_pages, page_size):
+    """Scatter logical tokens [ctx][Hkv][d] into a NaN-poisoned page pool."""
+    ctx = tokens.shape[0]
+    pages = np.full((pool_pages, page_size) + tokens.shape[1:], POISON, dtype=np.uint16)
+    n_full = ctx // page_size
+    if n_full:
+        pages[block_table[:n_full]] = tokens[:n_full * page_size].reshape((n_full, page_size) + tokens.shape[1:])
+    tail = ctx - n_full * page_size
+    if tail:
+        pages[block_table[n_full], :tail] = tokens[n_full * page_size:]
+    return pages
+
+
+# The five workloads: shapes, history lengths and piece sizes of the pages'
+# measurements (a 16 Q / 2 KV head, d 256 attention layer; a 2048-row chunk
+# at 32K-128K history in production pieces), with random values standing in
+# for a real model's activations.
+SWEEP_HISTORIES = (1024, 2048, 4096, 8192, 16384, 32768)
+
+
+def config_case(name):
+    if name == "tiny":
+        return make_case(name, 512, 64, 4, 1, 64, 16, "f16", seed=0)
+    if name == "qwen_like":
+        return make_case(name, 8192, 512, 16, 2, 256, 16, "f16", seed=1, value_scale=0.5)
+    if name.startswith("sweep_"):
+        history = int(name.split("_")[1])
+        return make_case(name, history, 2048, 16, 2, 256, 16, "f16", seed=2)
+    if name == "piece_64k":
+        return make_case(name, 65536, 2048, 32, 4, 128, 16, "bf16", seed=3, piece_rows=256)
+    if name == "long_128k":
+        return make_case(name, 131072, 2048, 16, 2, 256, 16, "bf16", seed=4,
+                         table="scatter", pool_pages=65536, piece_rows=128)
+    raise KeyError(name)
+
+
+CONFIG_NAMES = ("tiny", "qwen_like") + tuple(f"sweep_{h}" for h in SWEEP_HISTORIES) + ("piece_64k", "long_128k")
+
+
+def exact_flops(history, rows, n_q_heads, head_dim):
+    """Attention FLOPs of one chunk call, counting each row's visible keys:
+    4 * d * Hq * sum_i (H + i + 1) = 4 d Hq (R H + R (R + 1) / 2)."""
+    return 4 * head_dim * n_q_heads * (rows * history + rows * (rows + 1) // 2)

@@ -1,0 +1,354 @@
+"""Checks that pin the oracle to facts other than itself.
+
+Each ``pin_*`` takes an oracle module (the real one, or a mutated copy in
+``test_oracle_mutants.py``) and raises AssertionError when the oracle
+disagrees with brute force, a closed form, torch's CPU attention with an
+explicit causal mask, an invariant of the definition, or a value the pages
+print.  Inputs are float64 so that only the oracle's arithmetic is on trial.
+"""
+
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ---------------------------------------------------------------- inputs
+def paged_inputs(rng, rows, history, n_q_heads, n_kv_heads, d, ps, extra_pool=3, scale=1.0):
+    """float64 paged inputs with a permuted block table; unused pool pages and
+    page tails are NaN, so reading them poisons the result."""
+    ctx = history + rows
+    n_pages = -(-ctx // ps)
+    q = rng.standard_normal((rows, n_q_heads, d)) * scale
+    k = rng.standard_normal((ctx, n_kv_heads, d)) * scale
+    v = rng.standard_normal((ctx, n_kv_heads, d)) * scale
+    pool = n_pages + extra_pool
+    bt = rng.permutation(pool)[:n_pages].astype(np.int32)
+    k_pages = np.full((pool, ps, n_kv_heads, d), np.nan)
+    v_pages = np.full((pool, ps, n_kv_heads, d), np.nan)
+    for j in range(ctx):
+        k_pages[bt[j // ps], j % ps] = k[j]
+        v_pages[bt[j // ps], j % ps] = v[j]
+    return q, k, v, k_pages, v_pages, bt
+
+
+def brute_force(q, k_pages, v_pages, bt, history, ps):
+    """Definition written out with Python loops and math.fsum: no max
+    subtraction, no vector ops, per-token page lookup."""
+    rows, n_q_heads, d = q.shape
+    n_kv_heads = k_pages.shape[2]
+    group = n_q_heads // n_kv_heads
+    out = np.zeros((rows, n_q_heads, d))
+    for i in range(rows):
+        for h in range(n_q_heads):
+            g = h // group
+            keys = list(range(history + i + 1))
+            kv = [(k_pages[bt[j // ps], j % ps, g], v_pages[bt[j // ps], j % ps, g]) for j in keys]
+            e = [math.exp(math.fsum(float(q[i, h, t]) * float(kj[t]) for t in range(d)) / math.sqrt(d))
+                 for kj, _ in kv]
+            z = math.fsum(e)
+            for c in range(d):
+                out[i, h, c] = math.fsum(ej * float(vj[c]) for ej, (_, vj) in zip(e, kv)) / z
+    return out
+
+
+BRUTE_SHAPES = [
+    # rows, history, Hq, Hkv, d, ps
+    (5, 11, 2, 1, 4, 2),
+    (8, 40, 4, 2, 8, 4),
+    (3, 0, 3, 1, 5, 4),
+    (7, 13, 6, 3, 3, 2),
+]
+
+
+def max_rel(a, b):
+    a = np.asarray(a)
+    b = np.asarray(b)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+# ---------------------------------------------------------------- pins
+def pin_decoders(orc):
+    """Bit patterns with known values (IEEE binary16 and bfloat16 encodings),
+    plus torch's own bfloat16/float16 conversion of random patterns."""
+    import torch
+    f16 = np.array([0x3C00, 0xC000, 0x7BFF, 0x0001, 0x3555, 0x0000, 0x8000], dtype=np.uint16)
+    f16_val = [1.0, -2.0, 65504.0, 2.0 ** -24, 0.333251953125, 0.0, -0.0]
+    got = orc.decode_f16(f16)
+    assert np.array_equal(got, np.array(f16_val)), got
+    bf = np.array([0x3F80, 0xC000, 0x7F7F, 0x3EAB, 0x0001, 0x4049], dtype=np.uint16)
+    bf_val = [1.0, -2.0, 3.3895313892515355e38, 0.333984375, 2.0 ** -133, 3.140625]
+    got = orc.decode_bf16(bf)
+    assert np.array_equal(got, np.array(bf_val)), got
+    rng = np.random.default_rng(7)
+    raw = rng.integers(0, 0x7F00, size=4096, dtype=np.uint16)  # finite positive patterns
+    ref_bf = torch.from_numpy(raw.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(orc.decode_bf16(raw), ref_bf)
+    raw16 = rng.integers(0, 0x7C00, size=4096, dtype=np.uint16)
+    ref_f16 = torch.from_numpy(raw16.view(np.int16)).view(torch.float16).to(torch.float64).numpy()
+    assert np.array_equal(orc.decode_f16(raw16), ref_f16)
+
+
+def pin_gather(orc):
+    """Gather through a permuted table equals the logical token order; the
+    NaN-poisoned slots are never read."""
+    rng = np.random.default_rng(11)
+    for rows, history, hq, hkv, d, ps in BRUTE_SHAPES:
+        q, k, v, kp, vp, bt = paged_inputs(rng, rows, history, hq, hkv, d, ps)
+        got = orc.gather_pages(kp, bt, history + rows, ps)
+        assert np.array_equal(got, k)
+
+
+def pin_brute_force(orc):
+    rng = np.random.default_rng(12)
+    for rows, history, hq, hkv, d, ps in BRUTE_SHAPES:
+        q, k, v, kp, vp, bt = paged_inputs(rng, rows, history, hq, hkv, d, ps)
+        ref = brute_force(q, kp, vp, bt, history, ps)
+        got = orc.paged_causal_attention(q, kp, vp, bt, history, ps)
+        assert np.all(np.isfinite(got))
+        assert np.max(np.abs(got - ref)) <= 1e-13, (rows, history, np.max(np.abs(got - ref)))
+
+
+def pin_closed_forms(orc):
+    rng = np.random.default_rng(13)
+    rows, history, hq, hkv, d = 6, 9, 4, 2, 8
+    ctx = history + rows
+    group = hq // hkv
+    # q = 0: uniform weights, out[i] = mean of V over keys 0 .. H + i
+    q = np.zeros((rows, hq, d))
+    k = rng.standard_normal((ctx, hkv, d))
+    v = rng.standard_normal((ctx, hkv, d))
+    got = orc.causal_attention(q, k, v, history)
+    for i in range(rows):
+        for h in range(hq):
+            ref = v[:history + i + 1, h // group].mean(axis=0)
+            assert np.max(np.abs(got[i, h] - ref)) <= 1e-14
+    # every key equal: uniform weights again, whatever q is
+    q = rng.standard_normal((rows, hq, d))
+    k_same = np.broadcast_to(rng.standard_normal((1, hkv, d)), (ctx, hkv, d)).copy()
+    got = orc.causal_attention(q, k_same, v, history)
+    for i in range(rows):
+        for h in range(hq):
+            ref = v[:history + i + 1, h // group].mean(axis=0)
+            assert np.max(np.abs(got[i, h] - ref)) <= 1e-14
+    # constant V: the output is that constant
+    const = rng.standard_normal((hkv, d))
+    v_const = np.broadcast_to(const[None], (ctx, hkv, d)).copy()
+    got = orc.causal_attention(q, k, v_const, history)
+    for h in range(hq):
+        assert np.max(np.abs(got[:, h] - const[h // group][None])) <= 1e-14
+    # no history: the first row sees only key 0
+    got = orc.causal_attention(q, k, v, 0)
+    for h in range(hq):
+        assert np.max(np.abs(got[0, h] - v[0, h // group])) <= 1e-15
+    # one key with a score margin of about 60 dominates every row
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    q_same = np.broadcast_to(u * math.sqrt(d), (rows, hq, d)).copy()
+    k_small = rng.standard_normal((ctx, hkv, d)) * 0.01
+    star = 3
+    k_small[star] = u * 60.0
+    got = orc.causal_attention(q_same, k_small, v, history)
+    for i in range(rows):
+        for h in range(hq):
+            assert np.max(np.abs(got[i, h] - v[star, h // group])) <= 1e-15
+
+
+def pin_weights(orc):
+    """V = identity rows recovers the softmax weights: each row sums to 1,
+    keys past H + i get exactly 0, and the weights match brute force."""
+    rng = np.random.default_rng(14)
+    rows, history, hq, hkv = 5, 7, 2, 1
+    ctx = history + rows
+    d = ctx + 3
+    q = rng.standard_normal((rows, hq, d))
+    k = rng.standard_normal((ctx, hkv, d))
+    v = np.zeros((ctx, hkv, d))
+    for j in range(ctx):
+        v[j, 0, j] = 1.0
+    p = orc.causal_attention(q, k, v, history)
+    for i in range(rows):
+        for h in range(hq):
+            w = p[i, h]
+            assert abs(w.sum() - 1.0) <= 1e-12
+            assert np.all(w >= 0.0)
+            assert np.all(w[history + i + 1:] == 0.0)
+            s = [float(q[i, h] @ k[j, 0]) / math.sqrt(d) for j in range(history + i + 1)]
+            e = [math.exp(x) for x in s]
+            z = math.fsum(e)
+            assert np.max(np.abs(w[:history + i + 1] - np.array(e) / z)) <= 1e-14
+
+
+def pin_torch_sdpa(orc):
+    """torch's CPU scaled_dot_product_attention in float64 with an explicit
+    bottom-right causal mask (not is_causal, which aligns top-left when the
+    query and key lengths differ) and KV heads repeated for GQA."""
+    import torch
+    rng = np.random.default_rng(15)
+    for rows, history, hq, hkv, d in [(37, 100, 8, 2, 32), (16, 0, 4, 4, 16), (9, 61, 6, 2, 24)]:
+        ctx = history + rows
+        q = rng.standard_normal((rows, hq, d))
+        k = rng.standard_normal((ctx, hkv, d))
+        v = rng.standard_normal((ctx, hkv, d))
+        tq = torch.from_numpy(q).permute(1, 0, 2)
+        tk = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)
+        tv = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)
+        mask = torch.arange(ctx)[None, :] <= (history + torch.arange(rows))[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask)
+        ref = ref.permute(1, 0, 2).numpy()
+        got = orc.causal_attention(q, k, v, history)
+        assert np.max(np.abs(got - ref)) <= 1e-12, np.max(np.abs(got - ref))
+
+
+def pin_layout_invariance(orc):
+    """Identity, permuted and pool-scattered block tables and contiguous KV
+    give bitwise-identical outputs (the gather is exact)."""
+    rng = np.random.default_rng(16)
+    rows, history, hq, hkv, d, ps = 11, 45, 4, 2, 8, 4
+    q, k, v, kp, vp, bt = paged_inputs(rng, rows, history, hq, hkv, d, ps, extra_pool=20)
+    ctx = history + rows
+    n_pages = -(-ctx // ps)
+    ident = np.arange(n_pages, dtype=np.int32)
+    kpi = np.full((n_pages, ps, hkv, d), np.nan)
+    vpi = np.full((n_pages, ps, hkv, d), np.nan)
+    for j in range(ctx):
+        kpi[j // ps, j % ps] = k[j]
+        vpi[j // ps, j % ps] = v[j]
+    a = orc.paged_causal_attention(q, kp, vp, bt, history, ps)
+    b = orc.paged_causal_attention(q, kpi, vpi, ident, history, ps)
+    c = orc.causal_attention(q, k, v, history)
+    assert np.array_equal(a, b) and np.array_equal(a, c)
+
+
+def pin_split_invariance(orc):
+    """The split form with any number of page-aligned ranges, empty ones
+    included, equals the direct form."""
+    rng = np.random.default_rng(17)
+    for rows, history, hq, hkv, d, ps in [(12, 50, 4, 1, 8, 4), (5, 0, 2, 2, 4, 2), (9, 33, 6, 2, 8, 8)]:
+        ctx = history + rows
+        q = rng.standard_normal((rows, hq, d))
+        k = rng.standard_normal((ctx, hkv, d))
+        v = rng.standard_normal((ctx, hkv, d))
+        ref = orc.causal_attention(q, k, v, history)
+        for n_splits in (1, 2, 3, 4, 7, 16, 32):
+            ranges = orc.page_aligned_split_ranges(ctx, ps, n_splits)
+            covered = sorted((a, b) for a, b in ranges if b > a)
+            assert covered[0][0] == 0 and covered[-1][1] == ctx
+            assert all(covered[t][1] == covered[t + 1][0] for t in range(len(covered) - 1))
+            assert all(a % ps == 0 for a, b in ranges if b > a)
+            got = orc.split_causal_attention(q, k, v, history, ranges)
+            assert max_rel(got, ref) <= 1e-13, (n_splits, max_rel(got, ref))
+
+
+def pin_split_partials(orc):
+    """A range no row can see yields lse = -inf and O = 0; one full range
+    yields lse = log of the softmax denominator (brute force)."""
+    rng = np.random.default_rng(18)
+    rows, history, hq, hkv, d = 4, 6, 2, 1, 4
+    ctx = history + rows
+    q = rng.standard_normal((rows, hq, d))
+    k = rng.standard_normal((ctx, hkv, d))
+    v = rng.standard_normal((ctx, hkv, d))
+    # keys [history + 1, ctx) are invisible to row 0
+    o_part, lse = orc.split_partials(q, k, v, history, [(0, history + 1), (history + 1, ctx)])
+    assert np.all(lse[1, 0] == -np.inf) and np.all(o_part[1, 0] == 0.0)
+    for i in range(1, rows):
+        assert np.all(np.isfinite(lse[1, i]))
+    o_full, lse_full = orc.split_partials(q, k, v, history, [(0, ctx)])
+    for i in range(rows):
+        for h in range(hq):
+            s = [float(q[i, h] @ k[j, 0]) / math.sqrt(d) for j in range(history + i + 1)]
+            assert abs(lse_full[0, i, h] - math.log(math.fsum(math.exp(x) for x in s))) <= 1e-13
+
+
+def pin_piece_invariance(orc):
+    """Cutting the chunk into pieces (call i: rows [iP, (i+1)P) at history
+    H + iP over the same K/V) equals one call."""
+    rng = np.random.default_rng(19)
+    rows, history, hq, hkv, d = 32, 21, 4, 2, 8
+    ctx = history + rows
+    q = rng.standard_normal((rows, hq, d))
+    k = rng.standard_normal((ctx, hkv, d))
+    v = rng.standard_normal((ctx, hkv, d))
+    ref = orc.causal_attention(q, k, v, history)
+    for piece in (1, 5, 8, 16):
+        parts = [orc.causal_attention(q[s:s + piece], k, v, history + s) for s in range(0, rows, piece)]
+        assert max_rel(np.concatenate(parts), ref) <= 1e-13
+
+
+def pin_causality(orc):
+    """Changing K/V after position H + i leaves row i bit-for-bit unchanged and
+    changes later rows."""
+    rng = np.random.default_rng(20)
+    rows, history, hq, hkv, d = 8, 10, 2, 1, 4
+    ctx = history + rows
+    q = rng.standard_normal((rows, hq, d))
+    k = rng.standard_normal((ctx, hkv, d))
+    v = rng.standard_normal((ctx, hkv, d))
+    base = orc.causal_attention(q, k, v, history)
+    i = 3
+    k2, v2 = k.copy(), v.copy()
+    k2[history + i + 1:] += 5.0
+    v2[history + i + 1:] -= 3.0
+    pert = orc.causal_attention(q, k2, v2, history)
+    assert np.array_equal(pert[:i + 1], base[:i + 1])
+    assert np.all(np.abs(pert[i + 1:] - base[i + 1:]).max(axis=(1, 2)) > 1e-6)
+
+
+def pin_gqa_is_mha_with_repeated_kv(orc):
+    rng = np.random.default_rng(21)
+    rows, history, hq, hkv, d = 6, 14, 6, 2, 8
+    ctx = history + rows
+    q = rng.standard_normal((rows, hq, d))
+    k = rng.standard_normal((ctx, hkv, d))
+    v = rng.standard_normal((ctx, hkv, d))
+    gqa = orc.causal_attention(q, k, v, history)
+    mha = orc.causal_attention(q, np.repeat(k, hq // hkv, axis=1), np.repeat(v, hq // hkv, axis=1), history)
+    assert max_rel(gqa, mha) <= 1e-13
+    # and the head map is h -> h div G: swapping the two KV heads swaps the outputs of the groups
+    swapped = orc.causal_attention(q[:, ::-1].copy(), k[:, ::-1].copy(), v[:, ::-1].copy(), history)
+    assert max_rel(swapped[:, ::-1], gqa) <= 1e-13
+
+
+def pin_row_subset(orc):
+    rng = np.random.default_rng(22)
+    rows, history, hq, hkv, d = 40, 30, 4, 1, 8
+    ctx = history + rows
+    q = rng.standard_normal((rows, hq, d))
+    k = rng.standard_normal((ctx, hkv, d))
+    v = rng.standard_normal((ctx, hkv, d))
+    full = orc.causal_attention(q, k, v, history)
+    sel = np.array([39, 0, 17, 5])
+    got = orc.causal_attention_rows(q, k, v, history, sel)
+    assert max_rel(got, full[sel]) <= 1e-13
+
+
+def load_golden(name):
+    out = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                out.append([int(x) for x in line.split()])
+    return out
+
+
+def pin_page_split_table(rules):
+    for cores, kv_heads, piece_rows, tiles, splits in load_golden("page_split_table.txt"):
+        assert tiles == piece_rows // 8
+        assert rules.page_split_rule(cores, kv_heads, tiles) == splits, (cores, kv_heads, piece_rows)
+
+
+def pin_page_piece_rows(rules):
+    for history, piece in load_golden("page_piece_rows.txt"):
+        assert rules.page_piece_rows(history) == piece, history
+
+
+ATTENTION_PINS = [
+    pin_decoders, pin_gather, pin_brute_force, pin_closed_forms, pin_weights, pin_torch_sdpa,
+    pin_layout_invariance, pin_split_invariance, pin_split_partials, pin_piece_invariance,
+    pin_causality, pin_gqa_is_mha_with_repeated_kv, pin_row_subset,
+]
+RULE_PINS = [pin_page_split_table, pin_page_piece_rows]

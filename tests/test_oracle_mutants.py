@@ -1,0 +1,102 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check
+that at least one pin catches each of them: the pins are strong enough to
+trust the oracle."""
+
+import os
+import types
+
+import pytest
+
+import _pins
+
+ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
+
+ATTENTION_MUTANTS = [
+    ("scale 1/d instead of 1/sqrt(d)",
+     "    scale = 1.0 / math.sqrt(d)\n    out = np.empty", "    scale = 1.0 / d\n    out = np.empty"),
+    ("exclusive causal diagonal",
+     "visible = np.arange(n_keys)[None, :] <= last_visible[:, None]",
+     "visible = np.arange(n_keys)[None, :] < last_visible[:, None]"),
+    ("one key too many",
+     "last_visible = history_len + np.repeat(rb, group)",
+     "last_visible = history_len + 1 + np.repeat(rb, group)"),
+    ("rows and heads of a group interleaved the wrong way",
+     "last_visible = history_len + np.repeat(rb, group)",
+     "last_visible = history_len + np.tile(rb, group)"),
+    ("wrong KV head",
+     "scores = (qb @ k[:n_keys, g, :].T) * scale",
+     "scores = (qb @ k[:n_keys, (g + 1) % n_kv_heads, :].T) * scale"),
+    ("K used in place of V",
+     "(weights @ v[:n_keys, g, :])", "(weights @ k[:n_keys, g, :])"),
+    ("normalised over the wrong axis",
+     "weights = weights / weights.sum(axis=1, keepdims=True)",
+     "weights = weights / weights.sum(axis=0, keepdims=True)"),
+    ("block table ignored",
+     "out[j] = pages[pool_page, j % page_size]", "out[j] = pages[j // page_size, j % page_size]"),
+    ("page and slot swapped",
+     "pool_page = block_table[j // page_size]", "pool_page = block_table[j % page_size]"),
+    ("merge without the log-sum-exp normaliser",
+     "weights = np.exp(lse - total[None])", "weights = np.exp(lse - top[None])"),
+    ("wrong sign of ln l in lse",
+     "m + np.log(safe_l)", "m - np.log(safe_l)"),
+    ("exclusive diagonal in the split partials",
+     "visible = np.arange(a, b)[None, :] <= last_visible[:, None]",
+     "visible = np.arange(a, b)[None, :] < last_visible[:, None]"),
+    ("split ranges drop their last key",
+     "end = min((s + 1) * per * page_size, ctx)", "end = min((s + 1) * per * page_size - 1, ctx)"),
+    ("partials not divided by their own sum",
+     "o = (weights @ v[a:b, g, :]) / safe_l[:, None]", "o = (weights @ v[a:b, g, :])"),
+    ("bfloat16 decoded with the wrong shift",
+     "<< np.uint32(16)", "<< np.uint32(15)"),
+    ("float16 decoded as bfloat16",
+     "return np.asarray(raw, dtype=np.uint16).view(np.float16).astype(np.float64)",
+     "return (np.asarray(raw, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)"),
+    ("row subset ignored",
+     "rb = rows[b:b + block]\n", "rb = np.arange(len(rows))[b:b + block]\n"),
+]
+
+RULE_MUTANTS = [
+    ("floor division replaced by the cap", "return min(max(per_head // tiles, 1), max_splits)",
+     "return min(max(slot_cap // tiles, 1), max_splits)"),
+    ("cores not divided by KV heads", "(per_core * gpu_cores) // kv_heads", "(per_core * gpu_cores)"),
+    ("no clamp to max splits", "return min(max(per_head // tiles, 1), max_splits)",
+     "return max(per_head // tiles, 1)"),
+    ("piece budget off by a factor 2", "budget=1 << 25", "budget=1 << 26"),
+    ("piece rule on history only", "rows * (history_len + rows) > budget", "rows * history_len > budget"),
+]
+
+
+def _mutated_module(filename, old, new):
+    with open(os.path.join(ORACLE_DIR, filename)) as f:
+        src = f.read()
+    assert src.count(old) >= 1, f"mutation target not found: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new), filename, "exec"), mod.__dict__)
+    return mod
+
+
+def _caught(mod, pins):
+    for pin in pins:
+        try:
+            pin(mod)
+        except Exception:
+            return True
+    return False
+
+
+@pytest.mark.parametrize("label,old,new", ATTENTION_MUTANTS, ids=[m[0] for m in ATTENTION_MUTANTS])
+def test_attention_mutant_is_caught(label, old, new):
+    mod = _mutated_module("attention.py", old, new)
+    assert _caught(mod, _pins.ATTENTION_PINS), f"no pin caught: {label}"
+
+
+@pytest.mark.parametrize("label,old,new", RULE_MUTANTS, ids=[m[0] for m in RULE_MUTANTS])
+def test_rule_mutant_is_caught(label, old, new):
+    mod = _mutated_module("rules.py", old, new)
+    assert _caught(mod, _pins.RULE_PINS), f"no pin caught: {label}"
+
+
+def test_unmutated_copy_passes_every_pin():
+    mod = _mutated_module("attention.py", "import math", "import math")
+    for pin in _pins.ATTENTION_PINS:
+        pin(mod)
