@@ -1,0 +1,188 @@
+/*
+ * paged_prefill.h -- C ABI of chunked prefill attention over a paged KV cache
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (issue "Metal: paged-KV prefill is 4.43x slower than
+ * contiguous KV at 32K", TL;DR and "Results"; PR "perf: scale prefill
+ * attention splits with GPU cores on Apple7/8", "What changed"):
+ *
+ *   A chunk of R query rows sits at absolute positions H .. H+R-1 after a
+ *   history of H tokens.  Its own K/V are already stored, so the cache holds
+ *   ctx = H + R tokens.  Row i attends to keys 0 .. H+i (inclusive): the whole
+ *   history plus the chunk causally.  Query head h uses KV head h / (Hq/Hkv)
+ *   (grouped-query attention).  For every row i and query head h:
+ *
+ *       out[i][h] = sum_j softmax_j( q[i][h] . K[j][g] / sqrt(d) ) V[j][g]
+ *
+ *   with the softmax taken over j = 0 .. H+i and g = h / (Hq/Hkv).  The
+ *   history is cut into splits, each split writes a partial output and its
+ *   log-sum-exp, and a merge kernel combines them (the PR's split-KV prefill
+ *   attention and its reduce).  Inputs are fp16 or bf16; scores, the running
+ *   max m, the running sum l and the output accumulator are fp32; out is
+ *   rounded to the input type, to nearest even.
+ *
+ * Layouts (row-major, element = 2 bytes):
+ *   q           [R][Hq][d]
+ *   k_pages     [n_pool_pages][page_size][Hkv][d]    (v_pages likewise)
+ *   block_table int32, >= ceil(ctx / page_size) entries; logical page j of
+ *               the sequence is pool page block_table[j]; token t is slot
+ *               t % page_size of logical page t / page_size
+ *   k, v        [>= ctx][Hkv][d]  (contiguous entry point: this is the paged
+ *               layout with an identity block table)
+ *   out         [R][Hq][d]
+ *
+ * Ownership: every pointer is caller-owned device memory that must stay
+ * valid until `stream` has executed the enqueued work; the library keeps no
+ * pointer after a call returns.  The library owns one grow-only split
+ * workspace per (device, stream), allocated on first need (that first call
+ * blocks in hipMalloc) and released by paged_prefill_release_workspaces().
+ *
+ * Execution: asynchronous, ordered on `stream` (0 = the null stream).  `out`
+ * is valid once the stream has synchronised.  Results are deterministic for a
+ * given plan: no atomics; partials merge in a fixed order; identity, permuted
+ * and scattered block tables give bit-identical outputs.
+ *
+ * Errors: 0 on success, a negative PPA_ERR_* code otherwise.  On any argument
+ * error nothing is enqueued.  Slots past ctx in the last page may hold any
+ * bits (NaN included): they never reach the output.  Block-table entries are
+ * not range-checked on the device (the signature carries no pool size): use
+ * paged_prefill_check_block_table() on a host copy, or set PPA_VALIDATE=1 to
+ * make every paged call copy the table to the host and check it first (slow).
+ *
+ * Thread safety: concurrent calls on different streams are safe; calls on the
+ * same stream are ordered by the stream.
+ */
+#ifndef PAGED_PREFILL_H
+#define PAGED_PREFILL_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* ppa_stream_t; /* a hipStream_t */
+
+enum ppa_dtype { PPA_F16 = 0, PPA_BF16 = 1 };
+
+enum ppa_status {
+  PPA_OK = 0,
+  PPA_ERR_NULL_PTR = -1,    /* a required pointer is NULL */
+  PPA_ERR_BAD_SHAPE = -2,   /* R < 0, H < 0, heads < 1, Hq % Hkv != 0, piece_rows < 0 */
+  PPA_ERR_UNSUPPORTED = -3, /* head_dim not 64/128/256, page_size not a power of two in [1, 1024] */
+  PPA_ERR_BAD_DTYPE = -4,   /* dtype not PPA_F16 / PPA_BF16 */
+  PPA_ERR_WORKSPACE = -5,   /* split workspace above PPA_MAX_WORKSPACE_BYTES or hipMalloc failed */
+  PPA_ERR_HIP = -6,         /* a HIP runtime call or kernel launch failed */
+  PPA_ERR_BLOCK_TABLE = -7, /* a block-table entry is outside [0, n_pool_pages) (checks only) */
+  PPA_ERR_ALIGNMENT = -8,   /* a tensor pointer is not 16-byte aligned */
+  PPA_ERR_ALIAS = -9,       /* out overlaps q */
+  PPA_ERR_TOO_LARGE = -10   /* a size exceeds the 32-bit index range the kernels use */
+};
+
+/* How one call is cut into work: see paged_prefill_plan(). */
+typedef struct {
+  int32_t n_splits;        /* key-axis splits actually used (>= 1) */
+  int32_t split_tokens;    /* keys per split; a multiple of kv_tile and of page_size */
+  int32_t m_tile;          /* query vectors (row, head pairs of one KV head) per workgroup */
+  int32_t kv_tile;         /* keys per inner-loop tile */
+  int32_t tiles_m;         /* m tiles per KV head: ceil(R * Hq/Hkv / m_tile) */
+  int32_t grid;            /* attention workgroups: tiles_m * Hkv * n_splits */
+  int32_t merge_grid;      /* merge workgroups (0 when n_splits == 1) */
+  int32_t reserved;
+  int64_t workspace_bytes; /* split workspace bytes (0 when n_splits == 1) */
+} ppa_plan;
+
+/*
+ * Paged prefill attention for one chunk (or one piece of a chunk).
+ * n_splits: 0 lets the planner choose (fill the 256 CUs, see
+ * paged_prefill_plan); >= 1 requests that many splits, clamped to the number
+ * of kv-tile units of the key axis.  chunk_rows == 0 is a no-op (returns 0,
+ * pointers unused).
+ */
+int paged_prefill_attention(const void* q, const void* k_pages, const void* v_pages,
+                            const int32_t* block_table, int64_t history_len, int32_t chunk_rows,
+                            int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                            int32_t page_size, int32_t n_splits, void* out, int32_t dtype,
+                            ppa_stream_t stream);
+
+/*
+ * The same computation over contiguous K/V [>= ctx][Hkv][d] (the A/B partner
+ * of the issue: same values, no block table).  It runs the same kernels with
+ * identity addressing and the same plan as a paged call with page_size 16,
+ * so its output is bit-identical to the paged one.
+ */
+int contiguous_prefill_attention(const void* q, const void* k, const void* v,
+                                 int64_t history_len, int32_t chunk_rows, int32_t n_q_heads,
+                                 int32_t n_kv_heads, int32_t head_dim, int32_t n_splits, void* out,
+                                 int32_t dtype, ppa_stream_t stream);
+
+/*
+ * A whole chunk in pieces of piece_rows rows (the PR's prefill pieces): call
+ * p covers rows [p*P, min((p+1)*P, R)) of q and out at history
+ * history_len + p*P, against the same block table.  piece_rows == 0 or
+ * >= chunk_rows is one call.  Each piece is planned on its own.
+ */
+int paged_prefill_attention_pieces(const void* q, const void* k_pages, const void* v_pages,
+                                   const int32_t* block_table, int64_t history_len,
+                                   int32_t chunk_rows, int32_t piece_rows, int32_t n_q_heads,
+                                   int32_t n_kv_heads, int32_t head_dim, int32_t page_size,
+                                   int32_t n_splits, void* out, int32_t dtype, ppa_stream_t stream);
+
+/* Contiguous-KV counterpart of paged_prefill_attention_pieces. */
+int contiguous_prefill_attention_pieces(const void* q, const void* k, const void* v,
+                                        int64_t history_len, int32_t chunk_rows,
+                                        int32_t piece_rows, int32_t n_q_heads, int32_t n_kv_heads,
+                                        int32_t head_dim, int32_t n_splits, void* out,
+                                        int32_t dtype, ppa_stream_t stream);
+
+/*
+ * Host-only: the plan a call with these arguments would use on an MI355X
+ * (256 CUs).  n_splits_req as in paged_prefill_attention.  The planner
+ * follows the PR's split rule ("What changed": threadgroups per core times
+ * cores over KV heads, capped at a full chunk's tile slots, divided by the
+ * piece's tiles, clamped) with MI355X's numbers: one resident workgroup per
+ * CU, 256 CUs, the tile slots of a 2048-row chunk as the cap, 64 splits at
+ * most, and no split shorter than one kv-tile unit.
+ */
+int paged_prefill_plan(int64_t history_len, int32_t chunk_rows, int32_t n_q_heads,
+                       int32_t n_kv_heads, int32_t head_dim, int32_t page_size,
+                       int32_t n_splits_req, ppa_plan* plan_out);
+
+/*
+ * Host-only: the PR's split rule with explicit parameters,
+ * clamp(min(slot_cap, max(floor, per_core * gpu_cores / kv_heads)) / tiles,
+ * 1, max_splits) in integer arithmetic.  Returns the split count, or a
+ * negative PPA_ERR_BAD_SHAPE if an argument is < 1.
+ */
+int paged_prefill_split_rule(int32_t gpu_cores, int32_t kv_heads, int32_t tiles,
+                             int32_t per_core, int32_t floor_tg, int32_t slot_cap,
+                             int32_t max_splits);
+
+/*
+ * Host-only: the PR's piece size (explanatory note after "Testing"): halve
+ * chunk_rows until rows * (history + rows) <= budget.  budget <= 0 means 2^25.
+ */
+int32_t paged_prefill_piece_rows(int64_t history_len, int32_t chunk_rows, int64_t budget);
+
+/*
+ * Host-only: check that the first n_entries of a host copy of a block table
+ * lie in [0, n_pool_pages).  Returns 0 or PPA_ERR_BLOCK_TABLE (or
+ * PPA_ERR_NULL_PTR / PPA_ERR_BAD_SHAPE for bad arguments).
+ */
+int paged_prefill_check_block_table(const int32_t* block_table_host, int64_t n_entries,
+                                    int64_t n_pool_pages);
+
+/* Frees every split workspace; call only when no stream still uses one. */
+int paged_prefill_release_workspaces(void);
+
+/* Static text for a status code. */
+const char* paged_prefill_strerror(int code);
+
+/* ABI version: major * 10000 + minor * 100 + patch. */
+int paged_prefill_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_PREFILL_H */

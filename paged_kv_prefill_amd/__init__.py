@@ -1,0 +1,191 @@
+"""Chunked prefill attention over a paged KV cache on MI355X (gfx950).
+
+A thin ctypes binding over ``libpaged_prefill.so`` (C ABI in
+``include/paged_prefill.h``).  It only marshals arguments: torch tensors give
+device pointers, shapes and the current HIP stream; every step of the
+computation runs in the library's HIP kernels.  There is no CPU fallback:
+if the library is missing or fails to load, importing the entry points
+raises.
+"""
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpaged_prefill.so")
+
+PPA_F16 = 0
+PPA_BF16 = 1
+
+
+class PagedPrefillError(RuntimeError):
+    def __init__(self, code, where):
+        self.code = code
+        super().__init__(f"{where}: {strerror(code)} (code {code})")
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [
+        ("n_splits", ctypes.c_int32),
+        ("split_tokens", ctypes.c_int32),
+        ("m_tile", ctypes.c_int32),
+        ("kv_tile", ctypes.c_int32),
+        ("tiles_m", ctypes.c_int32),
+        ("grid", ctypes.c_int32),
+        ("merge_grid", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_int64),
+    ]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+
+
+_lib = None
+
+_VP = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+
+_SIGNATURES = {
+    "paged_prefill_attention": (_I32, [_VP, _VP, _VP, _VP, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _I32, _VP]),
+    "contiguous_prefill_attention": (_I32, [_VP, _VP, _VP, _I64, _I32, _I32, _I32, _I32, _I32, _VP, _I32, _VP]),
+    "paged_prefill_attention_pieces": (_I32, [_VP, _VP, _VP, _VP, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _I32, _VP]),
+    "contiguous_prefill_attention_pieces": (_I32, [_VP, _VP, _VP, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _I32, _VP]),
+    "paged_prefill_plan": (_I32, [_I64, _I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(Plan)]),
+    "paged_prefill_split_rule": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
+    "paged_prefill_piece_rows": (_I32, [_I64, _I32, _I64]),
+    "paged_prefill_check_block_table": (_I32, [_VP, _I64, _I64]),
+    "paged_prefill_release_workspaces": (_I32, []),
+    "paged_prefill_strerror": (ctypes.c_char_p, [_I32]),
+    "paged_prefill_version": (_I32, []),
+}
+
+
+def lib():
+    """The loaded library (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built: run `python -c 'import __graft_entry__ as g; g.build()'`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def strerror(code):
+    return lib().paged_prefill_strerror(int(code)).decode()
+
+
+def _check(code, where):
+    if code != 0:
+        raise PagedPrefillError(code, where)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float16:
+        return PPA_F16
+    if t.dtype == torch.bfloat16:
+        return PPA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream_handle(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need_cuda(*tensors):
+    for t in tensors:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def paged_prefill_attention(q, k_pages, v_pages, block_table, history_len, n_splits=0, out=None,
+                            piece_rows=0, stream=None):
+    """out[R][Hq][d] = causal attention of q[R][Hq][d] (rows at positions
+    history_len .. history_len+R-1) over the paged cache k_pages/v_pages
+    [pool][page_size][Hkv][d] addressed by block_table (int32).  piece_rows
+    > 0 runs the chunk in pieces of that many rows."""
+    _need_cuda(q, k_pages, v_pages, block_table, out)
+    rows, n_q_heads, head_dim = q.shape
+    _, page_size, n_kv_heads, kd = k_pages.shape
+    if kd != head_dim or tuple(v_pages.shape) != tuple(k_pages.shape):
+        raise ValueError("k_pages/v_pages shape mismatch")
+    if out is None:
+        out = q.new_empty(q.shape)
+    common = (int(history_len), int(rows))
+    tail = (int(n_q_heads), int(n_kv_heads), int(head_dim), int(page_size), int(n_splits), _ptr(out),
+            _dtype_code(q), _stream_handle(stream, q.device))
+    if piece_rows:
+        rc = lib().paged_prefill_attention_pieces(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+                                                  *common, int(piece_rows), *tail)
+        _check(rc, "paged_prefill_attention_pieces")
+    else:
+        rc = lib().paged_prefill_attention(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+                                           *common, *tail)
+        _check(rc, "paged_prefill_attention")
+    return out
+
+
+def contiguous_prefill_attention(q, k, v, history_len, n_splits=0, out=None, piece_rows=0, stream=None):
+    """The same over contiguous k/v [>= H+R][Hkv][d]."""
+    _need_cuda(q, k, v, out)
+    rows, n_q_heads, head_dim = q.shape
+    n_kv_heads = k.shape[1]
+    if out is None:
+        out = q.new_empty(q.shape)
+    args = (int(history_len), int(rows))
+    tail = (int(n_q_heads), int(n_kv_heads), int(head_dim), int(n_splits), _ptr(out), _dtype_code(q),
+            _stream_handle(stream, q.device))
+    if piece_rows:
+        rc = lib().contiguous_prefill_attention_pieces(_ptr(q), _ptr(k), _ptr(v), *args, int(piece_rows), *tail)
+        _check(rc, "contiguous_prefill_attention_pieces")
+    else:
+        rc = lib().contiguous_prefill_attention(_ptr(q), _ptr(k), _ptr(v), *args, *tail)
+        _check(rc, "contiguous_prefill_attention")
+    return out
+
+
+def paged_prefill_plan(history_len, chunk_rows, n_q_heads, n_kv_heads, head_dim, page_size=16, n_splits=0):
+    plan = Plan()
+    rc = lib().paged_prefill_plan(int(history_len), int(chunk_rows), int(n_q_heads), int(n_kv_heads),
+                                  int(head_dim), int(page_size), int(n_splits), ctypes.byref(plan))
+    _check(rc, "paged_prefill_plan")
+    return plan.as_dict()
+
+
+def paged_prefill_split_rule(gpu_cores, kv_heads, tiles, per_core=32, floor_tg=32, slot_cap=256, max_splits=32):
+    rc = lib().paged_prefill_split_rule(gpu_cores, kv_heads, tiles, per_core, floor_tg, slot_cap, max_splits)
+    if rc < 0:
+        raise PagedPrefillError(rc, "paged_prefill_split_rule")
+    return rc
+
+
+def paged_prefill_piece_rows(history_len, chunk_rows=2048, budget=0):
+    return lib().paged_prefill_piece_rows(int(history_len), int(chunk_rows), int(budget))
+
+
+def paged_prefill_check_block_table(block_table_host, n_pool_pages):
+    import numpy as np
+    arr = np.ascontiguousarray(block_table_host, dtype=np.int32)
+    rc = lib().paged_prefill_check_block_table(arr.ctypes.data_as(ctypes.c_void_p), int(arr.size),
+                                               int(n_pool_pages))
+    return rc
+
+
+def paged_prefill_release_workspaces():
+    _check(lib().paged_prefill_release_workspaces(), "paged_prefill_release_workspaces")

@@ -1,0 +1,56 @@
+"""Build the HIP library in-tree: libpaged_prefill.so next to this file.
+
+hipcc cross-compiles for gfx950 without a GPU.  Packed fp32 instructions are
+disabled for the device code (they are emitted by the compiler on its own
+from plain float code otherwise).
+"""
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libpaged_prefill.so")
+BUILD_DIR = os.path.join(ROOT, "_build")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}"]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"build step failed ({res.returncode}): {' '.join(cmd)}\n{err}")
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+
+
+def build(verbose=False, resource_usage=False):
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    objs = []
+    kern_obj = os.path.join(BUILD_DIR, "attention.o")
+    extra = ["-Rpass-analysis=kernel-resource-usage"] if resource_usage else []
+    _run([HIPCC, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, *extra, "-c",
+          os.path.join(CSRC, "attention.hip"), "-o", kern_obj], verbose or resource_usage)
+    objs.append(kern_obj)
+    for src in ("api.cpp", "plan.cpp"):
+        obj = os.path.join(BUILD_DIR, src.replace(".cpp", ".o"))
+        _run([HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True, resource_usage="--usage" in sys.argv)

@@ -1,0 +1,221 @@
+// C ABI entry points: argument checks, planning, the split workspace and the
+// kernel launches.  Every step of the computation runs in the HIP kernels of
+// attention.hip; this file only validates, plans and enqueues.
+#include <hip/hip_runtime.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <cmath>
+#include <map>
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "kernels.h"
+#include "paged_prefill.h"
+#include "plan.h"
+
+namespace ppa {
+namespace {
+
+struct Workspace {
+  void* ptr = nullptr;
+  int64_t bytes = 0;
+};
+
+std::mutex g_ws_mutex;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+// Grow-only workspace per (device, stream).  The first use of a size blocks
+// in hipMalloc; later calls of the same or smaller size reuse it.
+int get_workspace(hipStream_t stream, int64_t bytes, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PPA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  Workspace& ws = g_ws[{dev, stream}];
+  if (ws.bytes < bytes) {
+    if (ws.ptr) {
+      // The old buffer may still be in use by work queued on this stream.
+      if (hipStreamSynchronize(stream) != hipSuccess) return PPA_ERR_HIP;
+      (void)hipFree(ws.ptr);
+      ws.ptr = nullptr;
+      ws.bytes = 0;
+    }
+    if (hipMalloc(&ws.ptr, size_t(bytes)) != hipSuccess) {
+      (void)hipGetLastError();
+      ws.ptr = nullptr;
+      return PPA_ERR_WORKSPACE;
+    }
+    ws.bytes = bytes;
+  }
+  *out = ws.ptr;
+  return PPA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool env_validate() {
+  const char* e = getenv("PPA_VALIDATE");
+  return e && e[0] == '1';
+}
+
+// Host check of the device block table (PPA_VALIDATE=1): the pool size is
+// not an argument, so only negative entries can be rejected here.
+int validate_block_table(const int32_t* bt_dev, int64_t n_entries, hipStream_t stream) {
+  std::vector<int32_t> host(size_t(n_entries > 0 ? n_entries : 0));
+  if (n_entries > 0) {
+    if (hipMemcpyAsync(host.data(), bt_dev, size_t(n_entries) * 4, hipMemcpyDeviceToHost, stream) !=
+        hipSuccess)
+      return PPA_ERR_HIP;
+    if (hipStreamSynchronize(stream) != hipSuccess) return PPA_ERR_HIP;
+  }
+  for (int32_t v : host)
+    if (v < 0) return PPA_ERR_BLOCK_TABLE;
+  return PPA_OK;
+}
+
+int run(const void* q, const void* k, const void* v, const int32_t* bt, bool paged,
+        int64_t history, int32_t rows, int32_t hq, int32_t hkv, int32_t d, int32_t ps,
+        int32_t n_splits, void* out, int32_t dtype, hipStream_t stream) {
+  Shape shape{history, rows, hq, hkv, d, ps, dtype};
+  int rc = check_shape(shape);
+  if (rc != PPA_OK) return rc;
+  if (n_splits < 0) return PPA_ERR_BAD_SHAPE;
+  if (rows == 0) return PPA_OK;
+  if (!q || !k || !v || !out || (paged && !bt)) return PPA_ERR_NULL_PTR;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return PPA_ERR_ALIGNMENT;
+  const int64_t qbytes = int64_t(rows) * hq * d * 2;
+  const char* qb = static_cast<const char*>(q);
+  const char* ob = static_cast<const char*>(out);
+  if (ob < qb + qbytes && qb < ob + qbytes) return PPA_ERR_ALIAS;
+
+  ppa_plan plan;
+  rc = make_plan(shape, n_splits, max_workspace_bytes(), &plan);
+  if (rc != PPA_OK) return rc;
+  if (plan.workspace_bytes > max_workspace_bytes()) return PPA_ERR_WORKSPACE;
+
+  if (paged && env_validate()) {
+    rc = validate_block_table(bt, (history + rows + ps - 1) / ps, stream);
+    if (rc != PPA_OK) return rc;
+  }
+
+  void* ws = nullptr;
+  if (plan.n_splits > 1) {
+    rc = get_workspace(stream, plan.workspace_bytes, &ws);
+    if (rc != PPA_OK) return rc;
+  }
+  const int64_t pairs = int64_t(rows) * hq;
+  const int64_t o_bytes = (int64_t(plan.n_splits) * pairs * d * 4 + 255) / 256 * 256;
+
+  AttnArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.bt = bt;
+  a.out = static_cast<uint16_t*>(out);
+  a.ws_o = static_cast<float*>(ws);
+  a.ws_lse = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + o_bytes) : nullptr;
+  a.history = history;
+  a.rows = rows;
+  a.n_q_heads = hq;
+  a.n_kv_heads = hkv;
+  a.group = hq / hkv;
+  a.log2_ps = paged ? log2_exact(ps) : 0;
+  a.ctx = int32_t(history + rows);
+  a.split_tokens = plan.split_tokens;
+  a.n_splits = plan.n_splits;
+  a.tiles_m = plan.tiles_m;
+  a.xcd_remap = (plan.grid % 8 == 0) ? 1 : 0;
+  a.scale_log2 = float(1.4426950408889634 / std::sqrt(double(d)));
+
+  if (launch_attention(a, d, dtype, paged, plan.grid, stream) != hipSuccess) return PPA_ERR_HIP;
+  if (plan.n_splits > 1) {
+    MergeArgs m;
+    m.ws_o = a.ws_o;
+    m.ws_lse = a.ws_lse;
+    m.out = a.out;
+    m.history = history;
+    m.rows = rows;
+    m.n_q_heads = hq;
+    m.split_tokens = plan.split_tokens;
+    m.n_splits = plan.n_splits;
+    if (launch_merge(m, d, dtype, plan.merge_grid, stream) != hipSuccess) return PPA_ERR_HIP;
+  }
+  return PPA_OK;
+}
+
+int run_pieces(const void* q, const void* k, const void* v, const int32_t* bt, bool paged,
+               int64_t history, int32_t rows, int32_t piece_rows, int32_t hq, int32_t hkv,
+               int32_t d, int32_t ps, int32_t n_splits, void* out, int32_t dtype,
+               hipStream_t stream) {
+  if (piece_rows < 0) return PPA_ERR_BAD_SHAPE;
+  Shape shape{history, rows, hq, hkv, d, ps, dtype};
+  int rc = check_shape(shape);
+  if (rc != PPA_OK) return rc;
+  if (piece_rows == 0 || piece_rows >= rows)
+    return run(q, k, v, bt, paged, history, rows, hq, hkv, d, ps, n_splits, out, dtype, stream);
+  const int64_t row_bytes = int64_t(hq) * d * 2;
+  for (int32_t r0 = 0; r0 < rows; r0 += piece_rows) {
+    const int32_t n = rows - r0 < piece_rows ? rows - r0 : piece_rows;
+    rc = run(static_cast<const char*>(q) + r0 * row_bytes, k, v, bt, paged, history + r0, n, hq,
+             hkv, d, ps, n_splits, static_cast<char*>(out) + r0 * row_bytes, dtype, stream);
+    if (rc != PPA_OK) return rc;
+  }
+  return PPA_OK;
+}
+
+}  // namespace
+}  // namespace ppa
+
+extern "C" {
+
+int paged_prefill_attention(const void* q, const void* k_pages, const void* v_pages,
+                            const int32_t* block_table, int64_t history_len, int32_t chunk_rows,
+                            int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                            int32_t page_size, int32_t n_splits, void* out, int32_t dtype,
+                            ppa_stream_t stream) {
+  return ppa::run(q, k_pages, v_pages, block_table, true, history_len, chunk_rows, n_q_heads,
+                  n_kv_heads, head_dim, page_size, n_splits, out, dtype,
+                  reinterpret_cast<hipStream_t>(stream));
+}
+
+int contiguous_prefill_attention(const void* q, const void* k, const void* v, int64_t history_len,
+                                 int32_t chunk_rows, int32_t n_q_heads, int32_t n_kv_heads,
+                                 int32_t head_dim, int32_t n_splits, void* out, int32_t dtype,
+                                 ppa_stream_t stream) {
+  return ppa::run(q, k, v, nullptr, false, history_len, chunk_rows, n_q_heads, n_kv_heads,
+                  head_dim, 16, n_splits, out, dtype, reinterpret_cast<hipStream_t>(stream));
+}
+
+int paged_prefill_attention_pieces(const void* q, const void* k_pages, const void* v_pages,
+                                   const int32_t* block_table, int64_t history_len,
+                                   int32_t chunk_rows, int32_t piece_rows, int32_t n_q_heads,
+                                   int32_t n_kv_heads, int32_t head_dim, int32_t page_size,
+                                   int32_t n_splits, void* out, int32_t dtype,
+                                   ppa_stream_t stream) {
+  return ppa::run_pieces(q, k_pages, v_pages, block_table, true, history_len, chunk_rows,
+                         piece_rows, n_q_heads, n_kv_heads, head_dim, page_size, n_splits, out,
+                         dtype, reinterpret_cast<hipStream_t>(stream));
+}
+
+int contiguous_prefill_attention_pieces(const void* q, const void* k, const void* v,
+                                        int64_t history_len, int32_t chunk_rows,
+                                        int32_t piece_rows, int32_t n_q_heads, int32_t n_kv_heads,
+                                        int32_t head_dim, int32_t n_splits, void* out,
+                                        int32_t dtype, ppa_stream_t stream) {
+  return ppa::run_pieces(q, k, v, nullptr, false, history_len, chunk_rows, piece_rows, n_q_heads,
+                         n_kv_heads, head_dim, 16, n_splits, out, dtype,
+                         reinterpret_cast<hipStream_t>(stream));
+}
+
+int paged_prefill_release_workspaces(void) {
+  std::lock_guard<std::mutex> lock(ppa::g_ws_mutex);
+  int rc = PPA_OK;
+  for (auto& kv : ppa::g_ws) {
+    if (kv.second.ptr && hipFree(kv.second.ptr) != hipSuccess) rc = PPA_ERR_HIP;
+  }
+  ppa::g_ws.clear();
+  return rc;
+}
+
+}  // extern "C"

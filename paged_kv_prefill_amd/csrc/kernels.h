@@ -1,0 +1,47 @@
+// Device-side argument blocks and launch wrappers shared by the host API and
+// the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ppa {
+
+struct AttnArgs {
+  const uint16_t* q;       // [R][Hq][D]
+  const uint16_t* k;       // paged: [pool][ps][Hkv][D]; contiguous: [ctx][Hkv][D]
+  const uint16_t* v;
+  const int32_t* bt;       // block table (paged only)
+  uint16_t* out;           // [R][Hq][D] (single split)
+  float* ws_o;             // [S][R][Hq][D] normalised split partials
+  float* ws_lse;           // [S][R][Hq] log2-domain log-sum-exp of each partial
+  int64_t history;         // H
+  int32_t rows;            // R
+  int32_t n_q_heads;       // Hq
+  int32_t n_kv_heads;      // Hkv
+  int32_t group;           // Hq / Hkv
+  int32_t log2_ps;         // log2(page_size) (paged)
+  int32_t ctx;             // H + R
+  int32_t split_tokens;    // keys per split
+  int32_t n_splits;        // S
+  int32_t tiles_m;         // m tiles per KV head
+  int32_t xcd_remap;       // 1: spread consecutive logical tiles over one XCD
+  float scale_log2;        // log2(e) / sqrt(D)
+};
+
+struct MergeArgs {
+  const float* ws_o;
+  const float* ws_lse;
+  uint16_t* out;
+  int64_t history;
+  int32_t rows;
+  int32_t n_q_heads;
+  int32_t split_tokens;
+  int32_t n_splits;
+};
+
+// dtype: 0 = fp16, 1 = bf16.  Returns hipSuccess or the launch error.
+hipError_t launch_attention(const AttnArgs& a, int head_dim, int dtype, bool paged, int grid,
+                            hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, int head_dim, int dtype, int grid, hipStream_t stream);
+
+}  // namespace ppa

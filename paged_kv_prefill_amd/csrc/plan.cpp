@@ -1,0 +1,165 @@
+// Split planner, argument checks and the host-only helpers of the C ABI.
+//
+// The split rule follows PR "perf: scale prefill attention splits with GPU
+// cores on Apple7/8" ("What changed"): aim for a number of threadgroups per
+// core, cap the threadgroups per KV head at the tile slots a full 2048-row
+// chunk already uses (so the workspace bound does not grow), divide by the
+// piece's row tiles and clamp.  On MI355X one attention workgroup fills a CU
+// (it holds 128 KB of LDS at head_dim 256), so the target is one workgroup
+// per CU over 256 CUs.
+#include "plan.h"
+
+#include <stdlib.h>
+
+namespace ppa {
+
+int log2_exact(int32_t v) {
+  if (v <= 0 || (v & (v - 1)) != 0) return -1;
+  int r = 0;
+  while ((1 << r) < v) ++r;
+  return r;
+}
+
+int check_shape(const Shape& s) {
+  if (s.dtype != PPA_F16 && s.dtype != PPA_BF16) return PPA_ERR_BAD_DTYPE;
+  if (s.rows < 0 || s.history < 0 || s.n_q_heads < 1 || s.n_kv_heads < 1) return PPA_ERR_BAD_SHAPE;
+  if (s.n_q_heads % s.n_kv_heads != 0) return PPA_ERR_BAD_SHAPE;
+  if (s.head_dim != 64 && s.head_dim != 128 && s.head_dim != 256) return PPA_ERR_UNSUPPORTED;
+  const int lps = log2_exact(s.page_size);
+  if (lps < 0 || lps > 10) return PPA_ERR_UNSUPPORTED;
+  // 32-bit index ranges used on the device: token positions, q/out elements.
+  const int64_t ctx = s.history + s.rows;
+  if (ctx + 2 * kKvTile >= (int64_t(1) << 31)) return PPA_ERR_TOO_LARGE;
+  if (int64_t(s.rows) * s.n_q_heads * s.head_dim >= (int64_t(1) << 31)) return PPA_ERR_TOO_LARGE;
+  return PPA_OK;
+}
+
+int64_t max_workspace_bytes() {
+  const char* env = getenv("PPA_MAX_WORKSPACE_BYTES");
+  if (env && *env) {
+    char* end = nullptr;
+    long long v = strtoll(env, &end, 10);
+    if (end != env && v >= 0) return v;
+  }
+  return int64_t(2) << 30;
+}
+
+static int split_rule(int32_t cores, int32_t kv_heads, int32_t tiles, int32_t per_core,
+                      int32_t floor_tg, int32_t slot_cap, int32_t max_splits) {
+  const int64_t want = int64_t(per_core) * cores / kv_heads;
+  int64_t per_head = want > floor_tg ? want : floor_tg;
+  if (per_head > slot_cap) per_head = slot_cap;
+  int64_t splits = per_head / tiles;
+  if (splits < 1) splits = 1;
+  if (splits > max_splits) splits = max_splits;
+  return int(splits);
+}
+
+int make_plan(const Shape& s, int32_t n_splits_req, int64_t max_ws_bytes, ppa_plan* out) {
+  const int32_t group = s.n_q_heads / s.n_kv_heads;
+  const int64_t ctx = s.history + s.rows;
+  const int32_t unit = s.page_size > kKvTile ? s.page_size : kKvTile;
+  const int64_t n_units = (ctx + unit - 1) / unit;
+  const int64_t tiles_m = (int64_t(s.rows) * group + kMTile - 1) / kMTile;
+  int64_t splits;
+  if (n_splits_req <= 0) {
+    const int32_t cap = int32_t((int64_t(kChunkRowsForCap) * group + kMTile - 1) / kMTile);
+    splits = split_rule(kNumCUs, s.n_kv_heads, int32_t(tiles_m > 0 ? tiles_m : 1), kWgPerCu, 1,
+                        cap, kMaxSplits);
+  } else {
+    splits = n_splits_req;
+  }
+  if (splits > n_units) splits = n_units;
+  if (splits < 1) splits = 1;
+  const int64_t units_per_split = (n_units + splits - 1) / splits;
+  const int64_t split_tokens = units_per_split * unit;
+  int64_t n_eff = split_tokens > 0 ? (ctx + split_tokens - 1) / split_tokens : 1;
+  if (n_eff < 1) n_eff = 1;
+  if (split_tokens >= (int64_t(1) << 31)) return PPA_ERR_TOO_LARGE;
+  out->n_splits = int32_t(n_eff);
+  out->split_tokens = int32_t(split_tokens);
+  out->m_tile = kMTile;
+  out->kv_tile = kKvTile;
+  out->tiles_m = int32_t(tiles_m);
+  const int64_t grid = tiles_m * s.n_kv_heads * n_eff;
+  if (grid >= (int64_t(1) << 31)) return PPA_ERR_TOO_LARGE;
+  out->grid = int32_t(grid);
+  out->reserved = 0;
+  if (n_eff > 1) {
+    const int64_t pairs = int64_t(s.rows) * s.n_q_heads;
+    const int64_t o_elems = n_eff * pairs * s.head_dim;
+    if (o_elems >= (int64_t(1) << 31)) return PPA_ERR_TOO_LARGE;
+    const int64_t o_bytes = (o_elems * 4 + 255) / 256 * 256;
+    const int64_t lse_bytes = (n_eff * pairs * 4 + 255) / 256 * 256;
+    out->workspace_bytes = o_bytes + lse_bytes;
+    const int threads_per_pair = s.head_dim / 4;
+    const int pairs_per_block = kThreads / threads_per_pair;
+    out->merge_grid = int32_t((pairs + pairs_per_block - 1) / pairs_per_block);
+    if (n_splits_req > 0 && out->workspace_bytes > max_ws_bytes) return PPA_ERR_WORKSPACE;
+  } else {
+    out->workspace_bytes = 0;
+    out->merge_grid = 0;
+  }
+  return PPA_OK;
+}
+
+}  // namespace ppa
+
+extern "C" {
+
+int paged_prefill_plan(int64_t history_len, int32_t chunk_rows, int32_t n_q_heads,
+                       int32_t n_kv_heads, int32_t head_dim, int32_t page_size,
+                       int32_t n_splits_req, ppa_plan* plan_out) {
+  if (!plan_out) return PPA_ERR_NULL_PTR;
+  ppa::Shape s{history_len, chunk_rows, n_q_heads, n_kv_heads, head_dim, page_size, PPA_F16};
+  int rc = ppa::check_shape(s);
+  if (rc != PPA_OK) return rc;
+  if (n_splits_req < 0) return PPA_ERR_BAD_SHAPE;
+  return ppa::make_plan(s, n_splits_req, ppa::max_workspace_bytes(), plan_out);
+}
+
+int paged_prefill_split_rule(int32_t gpu_cores, int32_t kv_heads, int32_t tiles, int32_t per_core,
+                             int32_t floor_tg, int32_t slot_cap, int32_t max_splits) {
+  if (gpu_cores < 1 || kv_heads < 1 || tiles < 1 || per_core < 1 || floor_tg < 1 ||
+      slot_cap < 1 || max_splits < 1)
+    return PPA_ERR_BAD_SHAPE;
+  return ppa::split_rule(gpu_cores, kv_heads, tiles, per_core, floor_tg, slot_cap, max_splits);
+}
+
+int32_t paged_prefill_piece_rows(int64_t history_len, int32_t chunk_rows, int64_t budget) {
+  if (budget <= 0) budget = int64_t(1) << 25;
+  if (chunk_rows < 1 || history_len < 0) return chunk_rows < 0 ? 0 : chunk_rows;
+  int64_t rows = chunk_rows;
+  while (rows > 1 && rows * (history_len + rows) > budget) rows /= 2;
+  return int32_t(rows);
+}
+
+int paged_prefill_check_block_table(const int32_t* bt, int64_t n_entries, int64_t n_pool_pages) {
+  if (n_entries < 0 || n_pool_pages < 0) return PPA_ERR_BAD_SHAPE;
+  if (n_entries == 0) return PPA_OK;
+  if (!bt) return PPA_ERR_NULL_PTR;
+  for (int64_t i = 0; i < n_entries; ++i)
+    if (bt[i] < 0 || bt[i] >= n_pool_pages) return PPA_ERR_BLOCK_TABLE;
+  return PPA_OK;
+}
+
+const char* paged_prefill_strerror(int code) {
+  switch (code) {
+    case PPA_OK: return "ok";
+    case PPA_ERR_NULL_PTR: return "a required pointer is NULL";
+    case PPA_ERR_BAD_SHAPE: return "bad shape (negative size, heads < 1 or Hq not a multiple of Hkv)";
+    case PPA_ERR_UNSUPPORTED: return "unsupported head_dim (64/128/256) or page_size (power of two, 1..1024)";
+    case PPA_ERR_BAD_DTYPE: return "dtype must be PPA_F16 or PPA_BF16";
+    case PPA_ERR_WORKSPACE: return "split workspace too large or its allocation failed";
+    case PPA_ERR_HIP: return "HIP runtime error";
+    case PPA_ERR_BLOCK_TABLE: return "block-table entry outside the page pool";
+    case PPA_ERR_ALIGNMENT: return "tensor pointer not 16-byte aligned";
+    case PPA_ERR_ALIAS: return "out overlaps q";
+    case PPA_ERR_TOO_LARGE: return "size beyond the kernels' 32-bit index range";
+    default: return "unknown status";
+  }
+}
+
+int paged_prefill_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+
+}  // extern "C"

@@ -1,0 +1,36 @@
+// Host-side planning and argument checks.  HIP-free: builds with g++ alone so
+// the planner is testable without a GPU.
+#pragma once
+#include <stdint.h>
+
+#include "paged_prefill.h"
+
+namespace ppa {
+
+// Work decomposition of the attention kernel (fixed by the kernel design).
+constexpr int kMTile = 128;      // query vectors per workgroup (4 waves x 32)
+constexpr int kKvTile = 64;      // keys per inner-loop tile
+constexpr int kThreads = 256;    // threads per workgroup
+constexpr int kNumCUs = 256;     // MI355X compute units
+constexpr int kWgPerCu = 1;      // resident attention workgroups per CU (LDS/VGPR bound)
+constexpr int kMaxSplits = 64;
+constexpr int kChunkRowsForCap = 2048;  // the cap: tile slots of a full 2048-row chunk
+
+struct Shape {
+  int64_t history;
+  int32_t rows, n_q_heads, n_kv_heads, head_dim, page_size, dtype;
+};
+
+// Shape checks shared by every entry point (no pointers).
+int check_shape(const Shape& s);
+
+// The plan for a call; assumes check_shape passed.  max_ws_bytes bounds an
+// explicitly requested split count.
+int make_plan(const Shape& s, int32_t n_splits_req, int64_t max_ws_bytes, ppa_plan* out);
+
+// Split workspace cap: PPA_MAX_WORKSPACE_BYTES or 2 GiB.
+int64_t max_workspace_bytes();
+
+int log2_exact(int32_t v);  // log2 of a power of two, -1 otherwise
+
+}  // namespace ppa

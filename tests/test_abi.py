@@ -1,0 +1,126 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function
+include/paged_prefill.h declares, and its host-only helpers (planner, split
+rule, piece rule, block-table check, argument checks) behave as documented.
+No call here reaches a GPU."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import _pins
+import paged_kv_prefill_amd as pkg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n.startswith(("paged_", "contiguous_"))))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = pkg.lib()
+    names = declared_functions()
+    assert len(names) == 11, names
+    for name in names:
+        assert hasattr(lib, name), name
+    assert lib.paged_prefill_version() == 10000
+
+
+def test_binding_covers_every_declared_symbol():
+    for name in declared_functions():
+        assert name in pkg._SIGNATURES, name
+
+
+def test_split_rule_reproduces_the_pr_table():
+    for cores, kv_heads, piece_rows, tiles, splits in _pins.load_golden("page_split_table.txt"):
+        assert pkg.paged_prefill_split_rule(cores, kv_heads, tiles) == splits
+
+
+def test_piece_rows_reproduce_the_pr_sizes():
+    for history, piece in _pins.load_golden("page_piece_rows.txt"):
+        assert pkg.paged_prefill_piece_rows(history) == piece
+
+
+def test_plan_matches_the_workloads():
+    # 2048-row chunk, 16/2 heads, d 256: 128 m-tiles x 2 KV heads fill 256 CUs with one split
+    p = pkg.paged_prefill_plan(32768, 2048, 16, 2, 256)
+    assert p["n_splits"] == 1 and p["grid"] == 256 and p["workspace_bytes"] == 0
+    # 256-row piece, 32/4 heads, d 128: 16 m-tiles x 4 heads -> 4 splits
+    p = pkg.paged_prefill_plan(65536, 256, 32, 4, 128)
+    assert p["n_splits"] == 4 and p["grid"] == 256
+    # 128-row piece, 16/2 heads, d 256 at 128K: 8 x 2 -> 16 splits, the PR's count at 128K
+    p = pkg.paged_prefill_plan(131072, 128, 16, 2, 256)
+    assert p["n_splits"] == 16 and p["grid"] == 256
+    assert p["workspace_bytes"] <= 2048 * 16 * 257 * 4 + 512
+
+
+@pytest.mark.parametrize("history,rows,hq,hkv,d,ps,req", [
+    (0, 1, 1, 1, 64, 16, 0), (5, 3, 4, 1, 64, 1, 0), (512, 64, 4, 1, 64, 16, 4), (1000, 77, 6, 2, 128, 8, 0),
+    (131072, 128, 16, 2, 256, 16, 0), (100, 2048, 32, 4, 128, 256, 0), (37, 5, 16, 2, 256, 16, 64),
+    (8192, 512, 16, 2, 256, 16, 0), (65536, 2048, 32, 8, 128, 16, 0), (3, 1, 2, 2, 64, 1024, 5),
+])
+def test_plan_invariants(history, rows, hq, hkv, d, ps, req):
+    p = pkg.paged_prefill_plan(history, rows, hq, hkv, d, ps, req)
+    ctx = history + rows
+    unit = max(64, ps)
+    assert p["split_tokens"] % 64 == 0 and p["split_tokens"] % ps == 0
+    assert 1 <= p["n_splits"] <= 64
+    # the splits cover [0, ctx) and none is empty
+    assert (p["n_splits"] - 1) * p["split_tokens"] < ctx <= p["n_splits"] * p["split_tokens"]
+    assert p["tiles_m"] == -(-rows * (hq // hkv) // 128)
+    assert p["grid"] == p["tiles_m"] * hkv * p["n_splits"]
+    if req:
+        assert p["n_splits"] <= max(1, min(req, -(-ctx // unit)))
+    if p["n_splits"] > 1:
+        assert p["workspace_bytes"] >= p["n_splits"] * rows * hq * (d + 1) * 4
+        assert p["merge_grid"] * (256 // (d // 4)) >= rows * hq
+    else:
+        assert p["workspace_bytes"] == 0 and p["merge_grid"] == 0
+
+
+def test_planner_never_exceeds_a_full_chunk_workspace():
+    for history in (1024, 8192, 32768, 65536, 131072, 262144):
+        for rows in (1, 16, 128, 256, 512, 1024, 2048):
+            for hq, hkv, d in ((16, 2, 256), (32, 4, 128), (4, 1, 64), (32, 8, 128)):
+                p = pkg.paged_prefill_plan(history, rows, hq, hkv, d)
+                assert p["n_splits"] * rows <= max(2048, rows) * 1 + 2048, (history, rows)
+                assert p["workspace_bytes"] <= 2048 * hq * (d + 1) * 4 * 2 + 1024
+
+
+def test_check_block_table():
+    assert pkg.paged_prefill_check_block_table(np.array([0, 5, 3]), 6) == 0
+    assert pkg.paged_prefill_check_block_table(np.array([0, 6, 3]), 6) == -7
+    assert pkg.paged_prefill_check_block_table(np.array([-1]), 6) == -7
+    assert pkg.paged_prefill_check_block_table(np.array([], dtype=np.int32), 6) == 0
+
+
+def _call_paged(**kw):
+    a = dict(q=16, kp=16, vp=16, bt=16, H=10, R=4, hq=4, hkv=2, d=64, ps=16, S=0, out=4096, dt=0)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return pkg.lib().paged_prefill_attention(vp(a["q"]), vp(a["kp"]), vp(a["vp"]), vp(a["bt"]), a["H"], a["R"],
+                                             a["hq"], a["hkv"], a["d"], a["ps"], a["S"], vp(a["out"]), a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=2), -4), (dict(R=-1), -2), (dict(H=-5), -2), (dict(hq=5, hkv=2), -2), (dict(hkv=0), -2),
+    (dict(d=96), -3), (dict(d=512), -3), (dict(ps=12), -3), (dict(ps=2048), -3), (dict(ps=0), -3),
+    (dict(S=-1), -2), (dict(q=0), -1), (dict(bt=0), -1), (dict(out=0), -1), (dict(q=24), -8),
+    (dict(out=16 + 64), -9), (dict(H=2 ** 31), -10),
+])
+def test_argument_errors_return_before_any_device_work(kw, code):
+    assert _call_paged(**kw) == code
+    assert pkg.strerror(code) not in ("unknown status", "ok")
+
+
+def test_empty_chunk_is_a_no_op():
+    assert _call_paged(R=0, q=0, kp=0, vp=0, bt=0, out=0) == 0
