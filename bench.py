@@ -1,0 +1,242 @@
+"""Benchmark: paged prefill attention, TFLOP/s and ms per 2048-row chunk at
+32K-128K history, on one MI355X.
+
+One step is one 2048-row chunk at each of three histories, paged KV with the
+pages in random order (the workloads of the PR's attention sweep and the
+issue's long prefill):
+  * 32K history, 16 Q / 2 KV heads, d 256, fp16, the chunk in one call;
+  * 64K history, 32 Q / 4 KV heads, d 128, bf16, eight 256-row pieces;
+  * 128K history, 16 Q / 2 KV heads, d 256, bf16, sixteen 128-row pieces,
+    pages scattered over a 65,536-page pool.
+Inputs are resident in HBM before the timed region.  The contiguous-KV path
+runs on the same values right after each paged chunk (A/B), outside the
+step's value.  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--copy-calibration]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}   # MI355X dense fp16/bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+CHUNKS = ("sweep_32768", "piece_64k", "long_128k")
+ROOFLINE_CHUNK = "sweep_32768"   # one attention launch per call (one split, no merge)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-ab", action="store_true", help="skip the contiguous-KV A/B")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device copy (known bytes) for counter scaling")
+    ap.add_argument("--chunks", default=",".join(CHUNKS))
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("attention.hip", "kernels.h"):
+        with open(os.path.join(ROOT, "paged_kv_prefill_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_hash):
+    """HBM bytes per launch of the roofline kernel from the committed counter
+    summary, or None if the kernel changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "attn_d256_f16_paged_32k_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case):
+    """The oracle (numpy float64) on a bounded sample of the 32K chunk's rows,
+    timed on this host's cores; reported in TFLOP/s of exact causal FLOPs."""
+    import numpy as np
+    import oracle
+    from paged_kv_prefill_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    dec = oracle.decode_f16 if case.dtype == "f16" else oracle.decode_bf16
+    q, k, v = dec(case.q), dec(case.k_contig), dec(case.v_contig)
+
+    def flops(rows):
+        return sum(4 * case.head_dim * case.n_q_heads * (case.history + int(r) + 1) for r in rows)
+
+    probe = np.arange(0, case.rows, case.rows // 16)
+    t0 = time.perf_counter()
+    oracle.causal_attention_rows(q, k, v, case.history, probe)
+    per_row = (time.perf_counter() - t0) / len(probe)
+    n = int(min(case.rows, max(32, 15.0 / max(per_row, 1e-6))))
+    rows = np.unique(np.linspace(0, case.rows - 1, n).astype(np.int64))
+    t0 = time.perf_counter()
+    oracle.causal_attention_rows(q, k, v, case.history, rows)
+    dt = time.perf_counter() - t0
+    return {"value": flops(rows) / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(rows)} of {case.rows} rows (evenly spaced) of the 32K-history chunk, "
+                      f"{dt:.1f} s, numpy float64 with BLAS on {threads} threads",
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the design note on sharding covers how it would split)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_prefill_amd as pkg
+    from paged_kv_prefill_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    names = [c for c in args.chunks.split(",") if c]
+
+    def to_dev(a, dt):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(dt).to(dev)
+
+    chunks = []
+    for name in names:
+        case = synth.config_case(name)
+        dt = torch.float16 if case.dtype == "f16" else torch.bfloat16
+        c = {"name": name, "case": case, "q": to_dev(case.q, dt), "kp": to_dev(case.k_pages, dt),
+             "vp": to_dev(case.v_pages, dt), "bt": torch.from_numpy(case.block_table).to(dev),
+             "k": to_dev(case.k_contig, dt), "v": to_dev(case.v_contig, dt),
+             "flops": synth.exact_flops(case.history, case.rows, case.n_q_heads, case.head_dim)}
+        c["out"] = torch.empty_like(c["q"])
+        c["out_c"] = torch.empty_like(c["q"])
+        chunks.append(c)
+        print(f"# {name}: H={case.history} R={case.rows} Hq={case.n_q_heads} Hkv={case.n_kv_heads} "
+              f"d={case.head_dim} {case.dtype} pieces={case.piece_rows or case.rows} "
+              f"GFLOP={c['flops'] / 1e9:.1f}", file=sys.stderr, flush=True)
+
+    def paged(c):
+        return pkg.paged_prefill_attention(c["q"], c["kp"], c["vp"], c["bt"], c["case"].history,
+                                           out=c["out"], piece_rows=c["case"].piece_rows, stream=stream)
+
+    def contig(c):
+        return pkg.contiguous_prefill_attention(c["q"], c["k"], c["v"], c["case"].history, out=c["out_c"],
+                                                piece_rows=c["case"].piece_rows, stream=stream)
+
+    for _ in range(args.warmup):
+        for c in chunks:
+            paged(c)
+            if not args.no_ab:
+                contig(c)
+    torch.cuda.synchronize()
+
+    n = args.steps
+    ev = {c["name"]: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+          for c in chunks}
+    ev_c = {c["name"]: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+            for c in chunks}
+    paged_ms_total = 0.0
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(n):
+        for c in chunks:
+            a, b = ev[c["name"]][i]
+            a.record(stream)
+            paged(c)
+            b.record(stream)
+            if not args.no_ab:
+                a2, b2 = ev_c[c["name"]][i]
+                a2.record(stream)
+                contig(c)
+                b2.record(stream)
+        print(f"# step {i + 1}/{n} enqueued", file=sys.stderr, flush=True) if (i + 1) % 10 == 0 else None
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    per_chunk = {}
+    for c in chunks:
+        ms = np.array([a.elapsed_time(b) for a, b in ev[c["name"]]])
+        paged_ms_total += ms.sum()
+        rec = {"ms_median": float(np.median(ms)), "ms_p10": float(np.percentile(ms, 10)),
+               "ms_p90": float(np.percentile(ms, 90)),
+               "tflops": c["flops"] / (np.median(ms) * 1e-3) / 1e12,
+               "history": c["case"].history, "piece_rows": c["case"].piece_rows or c["case"].rows,
+               "heads": f"{c['case'].n_q_heads}/{c['case'].n_kv_heads}", "head_dim": c["case"].head_dim,
+               "dtype": c["case"].dtype,
+               "plan_splits": pkg.paged_prefill_plan(c["case"].history, c["case"].piece_rows or c["case"].rows,
+                                                     c["case"].n_q_heads, c["case"].n_kv_heads,
+                                                     c["case"].head_dim)["n_splits"]}
+        if not args.no_ab:
+            msc = np.array([a.elapsed_time(b) for a, b in ev_c[c["name"]]])
+            rec["contiguous_ms_median"] = float(np.median(msc))
+            rec["paged_over_contiguous"] = float(np.median(ms) / np.median(msc))
+            rec["bitwise_equal_to_contiguous"] = bool(torch.equal(c["out"].view(torch.int16),
+                                                                  c["out_c"].view(torch.int16)))
+        per_chunk[c["name"]] = rec
+
+    total_flops = sum(c["flops"] for c in chunks)
+    step_ms = paged_ms_total / n
+    value = total_flops / (step_ms * 1e-3) / 1e12
+
+    roofline = None
+    rc = next((c for c in chunks if c["name"] == ROOFLINE_CHUNK), None)
+    if rc is not None:
+        plan = pkg.paged_prefill_plan(rc["case"].history, rc["case"].rows, rc["case"].n_q_heads,
+                                      rc["case"].n_kv_heads, rc["case"].head_dim)
+        assert plan["n_splits"] == 1  # one kernel launch per call: the events bracket exactly it
+        ms = np.array([a.elapsed_time(b) for a, b in ev[ROOFLINE_CHUNK]])
+        achieved = rc["flops"] / (ms.mean() * 1e-3) / 1e12
+        khash = kernel_source_hash()
+        traffic = load_traffic(khash)
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["f16"], "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_TFLOPS["f16"], 4), "traffic": traffic,
+                    "kernel": "attn_partial_kernel<256, F16, paged> (32K-history 2048-row chunk, one launch)",
+                    "launch_ms_mean": round(float(ms.mean()), 4), "kernel_source_hash": khash}
+
+    line = {
+        "metric": "paged prefill-attn TFLOP/s + ms per 2048-row chunk at 32K-128K history",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": n, "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16+bf16 (fp32 accumulate)", "data": "synthetic",
+        "config": {"workload": "one 2048-row chunk each at 32K (16/2 heads, d256, fp16, one call), "
+                               "64K (32/4, d128, bf16, 8x256-row pieces) and 128K history (16/2, d256, "
+                               "bf16, 16x128-row pieces, pages scattered in a 65536-page pool); paged KV, "
+                               "16-token pages in random order",
+                   "chunks": per_chunk, "wall_s": round(wall, 3)},
+        "roofline": roofline,
+    }
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        line["copy_calibration_bytes"] = 2 * src.numel()
+
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(next(c["case"] for c in chunks if c["name"] == ROOFLINE_CHUNK)
+                                            if rc is not None else chunks[0]["case"])
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
