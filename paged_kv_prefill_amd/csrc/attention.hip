@@ -33,6 +33,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace ppa {
@@ -89,23 +91,20 @@ template <int D>
 struct Geom {
   static constexpr int CH = D / 8;                 // 16-byte chunks per K/V row
   static constexpr int TILE_BYTES = kTK * D * 2;   // one K (or V) tile
-  static constexpr int LPW = TILE_BYTES / 1024 / kWaves;  // 1 KB direct loads per wave per tile
-  static constexpr int RPI = 64 / CH;              // rows covered by one 1 KB load
+  static constexpr int BLOCKS = TILE_BYTES / 1024; // 1 KB blocks per tile
+  static constexpr int LPW = BLOCKS / kWaves;      // blocks one wave loads per tile
 };
 
-// Chunk swizzles: LDS chunk position of (row, chunk c) is c ^ swz(row).
-// K: the 32 rows one QK operand read touches land on distinct 16-byte bank
-// groups.  V: the 8 rows x 4 chunks one transposing read touches cover each
-// bank group exactly twice.
-template <int CH>
-__device__ __forceinline__ int swz_k(int row) {
-  if constexpr (CH >= 16) return row & 15;
-  else return (row >> 1) & 7;
-}
-template <int CH>
-__device__ __forceinline__ int swz_v(int row) {
-  if constexpr (CH >= 16) return (row & 3) << 2;
-  else return ((row >> 1) & 1) << 2;
+// LDS layout of a 64-key K or V tile: 1 KB blocks of 8 rows x 8 chunks
+// (16 bytes each), chunk-major inside the block.  Block (row / 8, c / 8)
+// sits at ((c / 8) * 8 + row / 8) KB.  One direct-to-LDS load fills one
+// block: its 64 lanes read 8 rows x 128 contiguous bytes (8 whole cache
+// lines), and with pages of 8 tokens or more the 8 rows lie in one page.
+// Both MFMA operand reads below (K: 32 rows x one chunk; V transposed:
+// 8 rows x 4 chunks) touch every 16-byte bank group the minimum number of
+// times, and their addresses are a per-lane base plus compile-time offsets.
+__device__ __forceinline__ constexpr int lds_off(int row, int c) {
+  return (c >> 3) * 8192 + (row >> 3) * 1024 + (c & 7) * 128 + (row & 7) * 16;
 }
 
 __device__ __forceinline__ float max_with_partner(float x) {
@@ -118,50 +117,34 @@ __device__ __forceinline__ float sum_with_partner(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);  // same order on both lanes
 }
 
-// Issue the direct-to-LDS loads of one 64-key tile of K and V.  `page` is the
-// pool page of key t0 + lane (paged), keys at or past `kend` are not read and
-// their V rows are zeroed (K rows there are masked by the softmax).
-template <int D, bool PAGED>
-__device__ __forceinline__ void issue_tile(const AttnArgs& a, int g, int t0, int kend, int wave,
-                                           int lane, int page, uint8_t* kbuf, uint8_t* vbuf) {
-  using Gm = Geom<D>;
-  const int ps_mask = (1 << a.log2_ps) - 1;
-#pragma unroll
-  for (int i = 0; i < Gm::LPW; ++i) {
-    const int instr = wave * Gm::LPW + i;
-    const int slot = instr * 64 + lane;
-    const int row = slot / Gm::CH;
-    const int pos = slot % Gm::CH;
-    const int t = t0 + row;
-    int64_t tok;
-    if constexpr (PAGED) {
-      const int pg = __shfl(page, row, 64);
-      tok = ((int64_t)pg << a.log2_ps) + (t & ps_mask);
-    } else {
-      tok = t;
-    }
-    const int64_t base = (tok * a.n_kv_heads + g) * D;
-    const int ck = pos ^ swz_k<Gm::CH>(row);
-    const int cv = pos ^ swz_v<Gm::CH>(row);
-    uint8_t* kd = kbuf + instr * 1024;
-    uint8_t* vd = vbuf + instr * 1024;
-    if (t < kend) {
-      __builtin_amdgcn_global_load_lds((const void*)(a.k + base + ck * 8), LDS_PTR(void, kd), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(a.v + base + cv * 8), LDS_PTR(void, vd), 16, 0, 0);
-    } else {
-      *LDS_PTR(u32x4, vd + lane * 16) = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-}
+// How K/V rows are addressed.  Contig: [ctx][Hkv][d].  PageWave: pages of
+// 16 tokens or more; the 16 rows one wave loads per tile then lie in one page,
+// so the page is wave-uniform and an address is a scalar base plus a per-lane
+// offset that does not change from tile to tile.  PageLane: smaller pages;
+// every row looks up its own page.
+enum class Addr { Contig, PageWave, PageLane };
 
-template <int D, class E, bool PAGED>
+// Softmax reference max is only raised when a tile's max exceeds it by more
+// than 2^8 (log2 domain): the weights exp2(s c - m) then stay below 256, well
+// inside fp16 and bf16 range, and the O/l rescale (128 multiplies per lane at
+// head_dim 256) runs a handful of times per row instead of on every tile.
+// The result is the same softmax; only rounding differs.
+constexpr float kRescaleLog2 = 8.0f;
+
+template <int D, class E, Addr AM>
 __global__ __launch_bounds__(256, 1) void attn_partial_kernel(AttnArgs a) {
   using Gm = Geom<D>;
   using vec8 = typename E::vec8;
   constexpr int CH = Gm::CH;
+  constexpr int LPW = Gm::LPW;
   constexpr int KS = D / 16;   // 16-wide d steps of QK
   constexpr int DB = D / 32;   // 32-wide d blocks of O
+  constexpr bool PAGED = AM != Addr::Contig;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * Gm::TILE_BYTES];
+  uint8_t* const kbuf0 = smem;
+  uint8_t* const kbuf1 = smem + Gm::TILE_BYTES;
+  uint8_t* const vbuf0 = smem + 2 * Gm::TILE_BYTES;
+  uint8_t* const vbuf1 = smem + 3 * Gm::TILE_BYTES;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -193,7 +176,9 @@ __global__ __launch_bounds__(256, 1) void attn_partial_kernel(AttnArgs a) {
   const int kend = min(k1, (int)(a.history + r_last + 1));
   const int n_tiles = kend > k0 ? (kend - k0 + kTK - 1) / kTK : 0;
   const int lim = (int)a.history + row;             // last key this query vector sees
-  const int mask_from = (int)a.history + r_first;   // tiles ending past this need the mask
+  // Tiles ending at or before the first row's last key need no mask.
+  const int mask_x = (int)a.history + r_first - k0 - (kTK - 1);
+  const int n_plain = min(n_tiles, mask_x < 0 ? 0 : mask_x / kTK + 1);
 
   // Q fragments (B operand of QK): lane holds Q[f][16 ks + 8 h .. +7].
   vec8 qf[KS];
@@ -209,119 +194,195 @@ __global__ __launch_bounds__(256, 1) void attn_partial_kernel(AttnArgs a) {
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
-  float m = kNegInf;  // running max of raw scores
-  float l = 0.f;      // this lane's share of the running sum
+  float m_ref = kNegInf;  // reference max, scaled log2 domain
+  float l = 0.f;          // this lane's share of the softmax sum
   const float c = a.scale_log2;
 
-  // Block-table prefetch: lane k holds the page of key (tile start + k).
-  int page_next = 0;
-  if constexpr (PAGED) {
-    if (n_tiles > 0 && k0 + lane < kend) page_next = a.bt[(k0 + lane) >> a.log2_ps];
-  }
-  if (n_tiles > 0) {
-    issue_tile<D, PAGED>(a, g, k0, kend, wave, lane, page_next, smem, smem + Gm::TILE_BYTES);
-    if constexpr (PAGED) {
-      const int tn = k0 + kTK + lane;
-      page_next = (n_tiles > 1 && tn < kend) ? a.bt[tn >> a.log2_ps] : 0;
+  // ---- loader -------------------------------------------------------------
+  // Block b = wave * LPW + i of a tile holds rows 8 (b % 8) .. +7 and chunks
+  // 8 (b / 8) .. +7; lane L loads row 8 (b % 8) + L % 8, chunk 8 (b / 8) + L / 8.
+  const int hkvd2 = a.n_kv_heads * D * 2;  // bytes per token (all KV heads)
+  const int ps_mask = (1 << a.log2_ps) - 1;
+  const int cg = (wave * LPW) >> 3;        // the wave's chunk group (same for all its blocks)
+  const uint32_t lane_off = (lane & 7) * hkvd2 + ((cg * 8 + (lane >> 3)) << 4);
+  const char* kg = (const char*)a.k + g * D * 2;
+  const char* vg = (const char*)a.v + g * D * 2;
+
+  auto pages = [&](int j) -> int {
+    if constexpr (!PAGED) return 0;
+    const int key = k0 + j * kTK + lane;
+    return (j < n_tiles && key < kend) ? a.bt[key >> a.log2_ps] : 0;
+  };
+
+  // Direct-to-LDS loads of tile j of K or V.  Keys at or past `kend` are read
+  // from key kend-1 instead: they are masked for every query of the workgroup
+  // (weight exactly 0) and a finite row keeps 0 * V finite, so there is no
+  // zero fill.  `page` holds the pool page of key (tile start + lane).
+  auto issue = [&](int j, int page, bool is_v, uint8_t* dst) {
+    const int t0 = k0 + j * kTK;
+    const int last = kend - 1 - t0;
+    const char* src = is_v ? vg : kg;
+    if (AM != Addr::PageLane && last >= kTK - 1) {
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int b = wave * LPW + i;
+        const int r0 = 8 * (b & 7);   // first row of the block
+        const char* base;
+        if constexpr (AM == Addr::Contig) {
+          base = src + (int64_t)(t0 + r0) * hkvd2;
+        } else {
+          const int pg = __builtin_amdgcn_readlane(page, r0);
+          base = src + (((int64_t)pg << a.log2_ps) + ((t0 + r0) & ps_mask)) * hkvd2;
+        }
+        __builtin_amdgcn_global_load_lds((const void*)(base + lane_off), LDS_PTR(void, dst + b * 1024), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int b = wave * LPW + i;
+        const int rr = min(8 * (b & 7) + (lane & 7), last);
+        int64_t tok;
+        if constexpr (AM == Addr::Contig) {
+          tok = t0 + rr;
+        } else {
+          const int pg = __shfl(page, rr, 64);
+          tok = ((int64_t)pg << a.log2_ps) + ((t0 + rr) & ps_mask);
+        }
+        __builtin_amdgcn_global_load_lds((const void*)(src + tok * hkvd2 + ((cg * 8 + (lane >> 3)) << 4)),
+                                         LDS_PTR(void, dst + b * 1024), 16, 0, 0);
+      }
     }
+  };
+
+  // ---- MFMA phases --------------------------------------------------------
+  // S^T[key][qv] = K Q^T for the 64 keys of a tile: lane holds qv = lane & 31
+  // and keys 32 kb + 8 (r / 4) + 4 h + r % 4.
+  f32x16 sc[2];
+  auto qk = [&](const uint8_t* kt) {
+    sc[0] = f32x16{};
+    sc[1] = f32x16{};
+    const uint8_t* kl = kt + lds_off(lane & 31, h);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      i16x8 r0 = *LDS_PTR(const i16x8, kl + lds_off(0, 2 * ks));
+      i16x8 r1 = *LDS_PTR(const i16x8, kl + lds_off(32, 2 * ks));
+      sc[0] = E::mfma(__builtin_bit_cast(vec8, r0), qf[ks], sc[0]);
+      sc[1] = E::mfma(__builtin_bit_cast(vec8, r1), qf[ks], sc[1]);
+    }
+  };
+
+  // O^T[d][qv] += V^T[d][key] P^T[key][qv], 16 keys per MFMA.  V^T comes from
+  // row-major V by two transposing reads per operand: the 16 lanes of a
+  // group read rows 16 kstep + 4 h + (lane % 16) / 4 (and + 8) at columns
+  // 32 db + 16 ((lane / 16) % 2) + 4 (lane % 4), and each lane receives one
+  // column over 4 rows.
+  vec8 pb[4];
+  auto pv = [&](const uint8_t* vt) {
+    const int col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // column within a 32-wide block
+    const uint8_t* vl = vt + lds_off(4 * h + ((lane & 15) >> 2), col >> 3) + (col & 7) * 2;
+#pragma unroll
+    for (int kstep = 0; kstep < 4; ++kstep) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vl + lds_off(16 * kstep, 4 * db)));
+        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vl + lds_off(16 * kstep + 8, 4 * db)));
+        i16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[db] = E::mfma(__builtin_bit_cast(vec8, av), pb[kstep], o[db]);
+      }
+    }
+  };
+
+  // Weights of the current S into pb (the B operand of PV), and their sum.
+  auto softmax = [&](float alpha) {
+    const float base = m_ref == kNegInf ? 0.f : m_ref;
+    float rs = 0.f;
+#pragma unroll
+    for (int kstep = 0; kstep < 4; ++kstep) {
+      float p8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[kstep >> 1][8 * (kstep & 1) + e], c, -base));
+        p8[e] = p;
+        rs += p;
+      }
+      pb[kstep] = E::from_f32(p8);
+    }
+    l = l * alpha + rs;
+  };
+
+  // ---- pipeline -----------------------------------------------------------
+  // Iteration it: QK of tile it, then the softmax of tile it interleaved with
+  // the PV of tile it-1 (independent of each other).  Loads run one tile
+  // ahead: K(it+1) and V(it) are issued at the start of iteration it.  The
+  // V buffer of "tile -1" is zeroed and pb starts at 0, so iteration 0 runs
+  // the same code (its PV adds exact zeros).
+#pragma unroll
+  for (int kstep = 0; kstep < 4; ++kstep) pb[kstep] = vec8{};
+  for (int i = tid; i < Gm::TILE_BYTES / 16; i += 256) *LDS_PTR(u32x4, vbuf1 + i * 16) = u32x4{0u, 0u, 0u, 0u};
+  int pg0 = 0, pg1 = 0;  // pages of tiles it and it+1
+  if (n_tiles > 0) {
+    pg0 = pages(0);
+    issue(0, pg0, false, kbuf0);
+    pg1 = pages(1);
   }
 
-  for (int it = 0; it < n_tiles; ++it) {
+  bool pend = false;       // O waits for a rescale by pend_alpha
+  float pend_alpha = 1.f;
+  auto body = [&](int it, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
     const int t0 = k0 + it * kTK;
-    uint8_t* kt = smem + (it & 1) * 2 * Gm::TILE_BYTES;
-    uint8_t* vt = kt + Gm::TILE_BYTES;
-    // This tile's loads (and the page prefetch) have landed in every wave,
-    // and every wave is done reading the other buffer.
+    // K(it) and V(it-1) have landed in every wave; K(it-1), V(it-2) are free.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (it + 1 < n_tiles) {
-      uint8_t* kn = smem + ((it + 1) & 1) * 2 * Gm::TILE_BYTES;
-      issue_tile<D, PAGED>(a, g, t0 + kTK, kend, wave, lane, page_next, kn, kn + Gm::TILE_BYTES);
-      if constexpr (PAGED) {
-        const int tn = t0 + 2 * kTK + lane;
-        page_next = (it + 2 < n_tiles && tn < kend) ? a.bt[tn >> a.log2_ps] : 0;
-      }
-    }
-
-    // S^T[key][qv] for keys 32 kb + (lane's C rows), qv = lane & 31.
-    f32x16 sc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sc[kb] = f32x16{};
-      const int krow = 32 * kb + (lane & 31);
-      const uint8_t* kr = kt + krow * CH * 16;
-      const int sw = swz_k<CH>(krow);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int pos = (2 * ks + h) ^ sw;
-        i16x8 raw = *LDS_PTR(const i16x8, kr + pos * 16);
-        sc[kb] = E::mfma(__builtin_bit_cast(vec8, raw), qf[ks], sc[kb]);
-      }
-    }
-
-    if (t0 + kTK - 1 > mask_from) {
+    if (it + 1 < n_tiles) issue(it + 1, pg1, false, (it & 1) ? kbuf0 : kbuf1);
+    issue(it, pg0, true, (it & 1) ? vbuf1 : vbuf0);
+    pg0 = pg1;
+    pg1 = pages(it + 2);
+    qk((it & 1) ? kbuf1 : kbuf0);
+    if constexpr (MASKED) {
+      const int rel = lim - t0;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = t0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-          sc[kb][r] = key > lim ? kNegInf : sc[kb][r];
+          const int key = 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+          sc[kb][r] = key > rel ? kNegInf : sc[kb][r];
         }
     }
-
     float mx = sc[0][0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[0][r]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[1][r]);
-    mx = max_with_partner(mx);
-    const float m_new = fmaxf(m, mx);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f((m - m_use) * c);
-    const float mc = m_use * c;
-    float rs = 0.f;
+    const float mxs = max_with_partner(mx) * c;
+    // A raise of the reference max decided on the previous tile moves O to
+    // the new reference now, after PV(it-2) and before PV(it-1) (rare).
+    if (__ballot(pend)) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], c, -mc));
-        sc[kb][r] = p;
-        rs += p;
-      }
-    l = l * alpha + rs;
-    m = m_new;
-    if (__ballot(alpha != 1.f)) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      for (int db = 0; db < DB; ++db) o[db] *= pend_alpha;
     }
+    // Raise the reference max where this tile exceeds it by more than 2^8.
+    pend = mxs > m_ref + kRescaleLog2;
+    const float m_new = pend ? mxs : m_ref;
+    pend_alpha = __builtin_amdgcn_exp2f(m_ref - m_new);  // 1 where unchanged
+    m_ref = m_new;
+    // PV(it-1) reads the previous pb before softmax(it) rewrites it; the two
+    // are independent and form one block, so MFMA and VALU work interleave.
+    pv((it & 1) ? vbuf0 : vbuf1);
+    softmax(pend_alpha);
+  };
 
-    // O^T[d][qv] += V^T[d][key] P^T[key][qv], 16 keys per MFMA.
-    const int grp = (lane >> 4) & 1;
-    const int sub = (lane & 15) >> 2;
+  int it = 0;
+  for (; it < n_plain; ++it) body(it, std::false_type{});
+  for (; it < n_tiles; ++it) body(it, std::true_type{});
+  if (n_tiles > 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (__ballot(pend)) {
 #pragma unroll
-    for (int kstep = 0; kstep < 4; ++kstep) {
-      const int kb = kstep >> 1;
-      const int tt = kstep & 1;
-      float pv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pv[e] = sc[kb][8 * tt + e];
-      const vec8 pb = E::from_f32(pv);
-      const int row1 = 16 * kstep + 4 * h + sub;
-      const int row2 = row1 + 8;
-      const int sw1 = swz_v<CH>(row1), sw2 = swz_v<CH>(row2);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int col = 32 * db + 16 * grp + 4 * (lane & 3);
-        const int cc = col >> 3;
-        const int within = (col & 7) * 2;
-        const uint8_t* p1 = vt + (row1 * CH + (cc ^ sw1)) * 16 + within;
-        const uint8_t* p2 = vt + (row2 * CH + (cc ^ sw2)) * 16 + within;
-        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p1));
-        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p2));
-        i16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[db] = E::mfma(__builtin_bit_cast(vec8, av), pb, o[db]);
-      }
+      for (int db = 0; db < DB; ++db) o[db] *= pend_alpha;
     }
+    pv(((n_tiles - 1) & 1) ? vbuf1 : vbuf0);
   }
 
   // Epilogue: combine the two lanes' sums; lane holds d = 32 db + 8 q + 4 h + 0..3.
@@ -350,7 +411,7 @@ __global__ __launch_bounds__(256, 1) void attn_partial_kernel(AttnArgs a) {
                     o[db][4 * q4 + 3] * inv};
         *(f32x4*)(wp + 32 * db + 8 * q4) = v4;
       }
-    if (h == 0) a.ws_lse[(int64_t)s * pairs + pair] = l_tot > 0.f ? m * c + __log2f(l_tot) : kNegInf;
+    if (h == 0) a.ws_lse[(int64_t)s * pairs + pair] = l_tot > 0.f ? m_ref + log2f(l_tot) : kNegInf;
   }
 }
 
@@ -384,15 +445,17 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   *(u32x2*)(a.out + (int64_t)pair * D + dl) = u32x2{lo, hi};
 }
 
-template <int D, class E, bool PAGED>
+template <int D, class E, Addr AM>
 hipError_t launch_attn_t(const AttnArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_partial_kernel<D, E, PAGED>), dim3(grid), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((attn_partial_kernel<D, E, AM>), dim3(grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 template <int D, class E>
 hipError_t launch_attn_p(const AttnArgs& a, bool paged, int grid, hipStream_t stream) {
-  return paged ? launch_attn_t<D, E, true>(a, grid, stream) : launch_attn_t<D, E, false>(a, grid, stream);
+  if (!paged) return launch_attn_t<D, E, Addr::Contig>(a, grid, stream);
+  if (a.log2_ps >= 3) return launch_attn_t<D, E, Addr::PageWave>(a, grid, stream);
+  return launch_attn_t<D, E, Addr::PageLane>(a, grid, stream);
 }
 
 template <class E>
