@@ -18,10 +18,9 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                # MFMA accumulators in VGPRs: the rare softmax rescale of O is then a plain
-                # multiply instead of AGPR round trips the register allocator hoists.
-                "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+if os.environ.get("PPA_MFMA_VGPR_FORM"):
+    DEVICE_FLAGS += ["-mllvm", "-amdgpu-mfma-vgpr-form=" + os.environ["PPA_MFMA_VGPR_FORM"]]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 

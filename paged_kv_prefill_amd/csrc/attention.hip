@@ -96,15 +96,20 @@ struct Geom {
 };
 
 // LDS layout of a 64-key K or V tile: 1 KB blocks of 8 rows x 8 chunks
-// (16 bytes each), chunk-major inside the block.  Block (row / 8, c / 8)
-// sits at ((c / 8) * 8 + row / 8) KB.  One direct-to-LDS load fills one
-// block: its 64 lanes read 8 rows x 128 contiguous bytes (8 whole cache
-// lines), and with pages of 8 tokens or more the 8 rows lie in one page.
-// Both MFMA operand reads below (K: 32 rows x one chunk; V transposed:
-// 8 rows x 4 chunks) touch every 16-byte bank group the minimum number of
-// times, and their addresses are a per-lane base plus compile-time offsets.
+// (16 bytes each).  Block (row / 8, c / 8) sits at ((c / 8) * 8 + row / 8) KB.
+// Inside a block, chunk c and row r occupy 16-byte unit
+//   ((c % 8) ^ (row / 8 % 2)) * 8 + ((row % 8) ^ 4 (c / 2 % 2)).
+// One direct-to-LDS load fills one block: its 64 lanes read 8 rows x 128
+// contiguous bytes (8 whole cache lines), and with pages of 8 tokens or more
+// the 8 rows lie in one page.  LDS has 64 four-byte banks; a 16-byte read is
+// served 16 lanes at a time and an 8-byte read 32 lanes at a time.  The two
+// XOR terms make every such group of the two MFMA operand reads below
+// (K: 16 rows x one chunk; V transposed: 4 rows x 4 chunks) cover all 64
+// banks once, and keep their addresses a per-lane base plus compile-time
+// offsets.
 __device__ __forceinline__ constexpr int lds_off(int row, int c) {
-  return (c >> 3) * 8192 + (row >> 3) * 1024 + (c & 7) * 128 + (row & 7) * 16;
+  return (c >> 3) * 8192 + (row >> 3) * 1024 +
+         ((((c & 7) ^ ((row >> 3) & 1)) << 3) + ((row & 7) ^ (((c >> 1) & 1) << 2))) * 16;
 }
 
 __device__ __forceinline__ float max_with_partner(float x) {
@@ -124,15 +129,18 @@ __device__ __forceinline__ float sum_with_partner(float x) {
 // every row looks up its own page.
 enum class Addr { Contig, PageWave, PageLane };
 
-// Softmax reference max is only raised when a tile's max exceeds it by more
-// than 2^8 (log2 domain): the weights exp2(s c - m) then stay below 256, well
-// inside fp16 and bf16 range, and the O/l rescale (128 multiplies per lane at
-// head_dim 256) runs a handful of times per row instead of on every tile.
-// The result is the same softmax; only rounding differs.
-constexpr float kRescaleLog2 = 8.0f;
+// The softmax weights are exp2(s c - m_ref) with a fixed reference m_ref per
+// query vector instead of a running max, so the output accumulators are never
+// rescaled inside the key loop.  The reference is the max of the first tile
+// that has a visible key; later weights may exceed 1 by up to 2^15, which
+// fp16 (and bf16) P and fp32 O and l hold.  If any query vector of the
+// workgroup sees a larger score (its running max passes m_ref + 15 in the
+// log2 domain), the split is computed again with the exact max as reference.
+// Either way the result is the same softmax; only rounding differs.
+constexpr float kRefMarginLog2 = 15.0f;
 
 template <int D, class E, Addr AM>
-__global__ __launch_bounds__(256, 1) void attn_partial_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_partial_kernel(AttnArgs a) {
   using Gm = Geom<D>;
   using vec8 = typename E::vec8;
   constexpr int CH = Gm::CH;
@@ -140,11 +148,13 @@ __global__ __launch_bounds__(256, 1) void attn_partial_kernel(AttnArgs a) {
   constexpr int KS = D / 16;   // 16-wide d steps of QK
   constexpr int DB = D / 32;   // 32-wide d blocks of O
   constexpr bool PAGED = AM != Addr::Contig;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * Gm::TILE_BYTES];
-  uint8_t* const kbuf0 = smem;
-  uint8_t* const kbuf1 = smem + Gm::TILE_BYTES;
-  uint8_t* const vbuf0 = smem + 2 * Gm::TILE_BYTES;
-  uint8_t* const vbuf1 = smem + 3 * Gm::TILE_BYTES;
+  // Four separate arrays, each picked statically: the compiler can then see
+  // that a read of one buffer does not alias a direct-to-LDS load into another
+  // and does not make it wait for those loads (they complete a tile later).
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[Gm::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[Gm::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf0[Gm::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf1[Gm::TILE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -192,9 +202,8 @@ __global__ __launch_bounds__(256, 1) void attn_partial_kernel(AttnArgs a) {
   }
 
   f32x16 o[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
-  float m_ref = kNegInf;  // reference max, scaled log2 domain
+  float m_ref = kNegInf;  // softmax reference, scaled log2 domain
+  float m_true = kNegInf; // running max of the scaled scores
   float l = 0.f;          // this lane's share of the softmax sum
   const float c = a.scale_log2;
 
@@ -204,110 +213,185 @@ __global__ __launch_bounds__(256, 1) void attn_partial_kernel(AttnArgs a) {
   const int hkvd2 = a.n_kv_heads * D * 2;  // bytes per token (all KV heads)
   const int ps_mask = (1 << a.log2_ps) - 1;
   const int cg = (wave * LPW) >> 3;        // the wave's chunk group (same for all its blocks)
-  const uint32_t lane_off = (lane & 7) * hkvd2 + ((cg * 8 + (lane >> 3)) << 4);
+  // Lane L fills unit L of a block: row 8 rg + ((L % 8) ^ 4 (L / 16 % 2)),
+  // chunk 8 cg + ((L / 8) ^ (rg % 2)), rg = the block's row group.
+  const int lrow = (lane & 7) ^ (((lane >> 4) & 1) << 2);
   const char* kg = (const char*)a.k + g * D * 2;
   const char* vg = (const char*)a.v + g * D * 2;
 
-  auto pages = [&](int j) -> int {
+  // Pool page of key (tile j start + lane).  The key is clamped to kend-1, so
+  // the block-table read is always in range (lanes and tiles past the end read
+  // an entry nobody uses) and the load needs no branch.
+  auto pages = [&](int j) __attribute__((always_inline)) -> int {
     if constexpr (!PAGED) return 0;
-    const int key = k0 + j * kTK + lane;
-    return (j < n_tiles && key < kend) ? a.bt[key >> a.log2_ps] : 0;
+    const int key = min(k0 + j * kTK + lane, kend - 1);
+    return a.bt[key >> a.log2_ps];
   };
 
-  // Direct-to-LDS loads of tile j of K or V.  Keys at or past `kend` are read
-  // from key kend-1 instead: they are masked for every query of the workgroup
-  // (weight exactly 0) and a finite row keeps 0 * V finite, so there is no
-  // zero fill.  `page` holds the pool page of key (tile start + lane).
-  auto issue = [&](int j, int page, bool is_v, uint8_t* dst) {
+  // Direct-to-LDS load i (of LPW) of tile j of K or V.  Keys at or past `kend`
+  // are read from key kend-1 instead: they are masked for every query of the
+  // workgroup (weight exactly 0) and a finite row keeps 0 * V finite, so there
+  // is no zero fill.  With r0c = min(8 rg, (kend-1-t0) & ~7) and
+  // lrow_c = min(lrow, kend-1-t0-r0c), whole tiles read their own rows and the
+  // last tile's rows past kend-1 read row kend-1 (same 8-row group, so the
+  // same page).  `page` holds the pool page of key (tile start + lane).
+  auto issue_one = [&](int j, int page, bool is_v, uint8_t* dst, int i) __attribute__((always_inline)) {
     const int t0 = k0 + j * kTK;
     const int last = kend - 1 - t0;
     const char* src = is_v ? vg : kg;
-    if (AM != Addr::PageLane && last >= kTK - 1) {
-#pragma unroll
-      for (int i = 0; i < LPW; ++i) {
-        const int b = wave * LPW + i;
-        const int r0 = 8 * (b & 7);   // first row of the block
-        const char* base;
-        if constexpr (AM == Addr::Contig) {
-          base = src + (int64_t)(t0 + r0) * hkvd2;
-        } else {
-          const int pg = __builtin_amdgcn_readlane(page, r0);
-          base = src + (((int64_t)pg << a.log2_ps) + ((t0 + r0) & ps_mask)) * hkvd2;
-        }
-        __builtin_amdgcn_global_load_lds((const void*)(base + lane_off), LDS_PTR(void, dst + b * 1024), 16, 0, 0);
-      }
+    const int b = wave * LPW + i;
+    const int cpart = (cg * 8 + ((lane >> 3) ^ (b & 1))) << 4;
+    if constexpr (AM == Addr::PageLane) {
+      const int rr = min(8 * (b & 7) + lrow, last);
+      const int pg = __shfl(page, rr, 64);
+      const int64_t tok = ((int64_t)pg << a.log2_ps) + ((t0 + rr) & ps_mask);
+      __builtin_amdgcn_global_load_lds((const void*)(src + tok * hkvd2 + cpart), LDS_PTR(void, dst + b * 1024), 16, 0, 0);
     } else {
-#pragma unroll
-      for (int i = 0; i < LPW; ++i) {
-        const int b = wave * LPW + i;
-        const int rr = min(8 * (b & 7) + (lane & 7), last);
-        int64_t tok;
-        if constexpr (AM == Addr::Contig) {
-          tok = t0 + rr;
-        } else {
-          const int pg = __shfl(page, rr, 64);
-          tok = ((int64_t)pg << a.log2_ps) + ((t0 + rr) & ps_mask);
-        }
-        __builtin_amdgcn_global_load_lds((const void*)(src + tok * hkvd2 + ((cg * 8 + (lane >> 3)) << 4)),
-                                         LDS_PTR(void, dst + b * 1024), 16, 0, 0);
+      const int r0c = __builtin_amdgcn_readfirstlane(min(8 * (b & 7), last & ~7));
+      const int lrow_c = min(lrow, last - r0c);
+      const char* base;
+      if constexpr (AM == Addr::Contig) {
+        base = src + (int64_t)(t0 + r0c) * hkvd2;
+      } else {
+        const int pg = __builtin_amdgcn_readlane(page, r0c);
+        base = src + (((int64_t)pg << a.log2_ps) + ((t0 + r0c) & ps_mask)) * hkvd2;
       }
+      __builtin_amdgcn_global_load_lds((const void*)(base + (uint32_t)(lrow_c * hkvd2 + cpart)),
+                                       LDS_PTR(void, dst + b * 1024), 16, 0, 0);
     }
+  };
+  auto issue = [&](int j, int page, bool is_v, uint8_t* dst) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) issue_one(j, page, is_v, dst, i);
   };
 
   // ---- MFMA phases --------------------------------------------------------
   // S^T[key][qv] = K Q^T for the 64 keys of a tile: lane holds qv = lane & 31
   // and keys 32 kb + 8 (r / 4) + 4 h + r % 4.
   f32x16 sc[2];
-  auto qk = [&](const uint8_t* kt) {
+  // The operand reads run QPF steps ahead of their MFMAs; sched_barrier pins
+  // that order (the compiler otherwise waits on each read right before its
+  // MFMA).
+  auto qk = [&](const uint8_t* kt, auto&& step_hook) __attribute__((always_inline)) {
+    constexpr int QPF = 3;
     sc[0] = f32x16{};
     sc[1] = f32x16{};
-    const uint8_t* kl = kt + lds_off(lane & 31, h);
+    const int kr = lane & 31;
+    const int kbase = (kr >> 3) * 1024 + ((h ^ ((kr >> 3) & 1)) << 7);
+    const uint8_t* kl0 = kt + kbase + (kr & 7) * 16;
+    const uint8_t* kl1 = kt + kbase + ((kr & 7) ^ 4) * 16;
+    i16x8 k0r[KS], k1r[KS];
+    auto load = [&](int ks) __attribute__((always_inline)) {
+      // lds_off(row, 2 ks + h) = base[ks % 2] + (ks / 4) 8192 + (ks % 4) 256, row = lane % 32
+      const uint8_t* kl = (ks & 1) ? kl1 : kl0;
+      const int imm = (ks >> 2) * 8192 + (ks & 3) * 256;
+      k0r[ks] = *LDS_PTR(const i16x8, kl + imm);
+      k1r[ks] = *LDS_PTR(const i16x8, kl + imm + 4096);
+    };
+#pragma unroll
+    for (int ks = 0; ks < QPF && ks < KS; ++ks) load(ks);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      i16x8 r0 = *LDS_PTR(const i16x8, kl + lds_off(0, 2 * ks));
-      i16x8 r1 = *LDS_PTR(const i16x8, kl + lds_off(32, 2 * ks));
-      sc[0] = E::mfma(__builtin_bit_cast(vec8, r0), qf[ks], sc[0]);
-      sc[1] = E::mfma(__builtin_bit_cast(vec8, r1), qf[ks], sc[1]);
+      if (ks + QPF < KS) load(ks + QPF);
+      sc[0] = E::mfma(__builtin_bit_cast(vec8, k0r[ks]), qf[ks], sc[0]);
+      sc[1] = E::mfma(__builtin_bit_cast(vec8, k1r[ks]), qf[ks], sc[1]);
+      step_hook(ks);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // O^T[d][qv] += V^T[d][key] P^T[key][qv], 16 keys per MFMA.  V^T comes from
-  // row-major V by two transposing reads per operand: the 16 lanes of a
-  // group read rows 16 kstep + 4 h + (lane % 16) / 4 (and + 8) at columns
-  // 32 db + 16 ((lane / 16) % 2) + 4 (lane % 4), and each lane receives one
-  // column over 4 rows.
-  vec8 pb[4];
-  auto pv = [&](const uint8_t* vt) {
-    const int col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // column within a 32-wide block
-    const uint8_t* vl = vt + lds_off(4 * h + ((lane & 15) >> 2), col >> 3) + (col & 7) * 2;
+  // PV of the previous tile fused with the row max and softmax of this one:
+  // O^T[d][qv] += V^T[d][key] P^T[key][qv] (16 keys per MFMA, V^T read from
+  // row-major V by two transposing reads per operand: the 16 lanes of a group
+  // read rows 16 kstep + 4 h + (lane % 16) / 4 (and + 8) at columns
+  // 32 db + 16 ((lane / 16) % 2) + 4 (lane % 4), each lane receiving one column
+  // over 4 rows), while the VALU computes the max, the weights exp2(s c - m)
+  // of this tile into pb_new and their sum.  Step i issues the V reads of
+  // step i + VPF, one MFMA and a slice of the VALU work; sched_barrier pins
+  // the interleave.  The two halves are independent: PV reads pb, softmax
+  // writes pb_new.
+  vec8 pb[4], pb_new[4];
+  // lds_off(16 kstep + r (+ 8), 4 db + cc) + within = base1 (base2) + (db / 2) 8192 + (db % 2) 512
+  // + kstep 2048 (+ 1024), r = 4 h + (lane % 16) / 4, cc = 2 grp + (lane % 4) / 2
+  const int v_grp = (lane >> 4) & 1;
+  const int v_cc = 2 * v_grp + ((lane & 3) >> 1);
+  const int v_row = (4 * h + ((lane & 15) >> 2)) ^ (v_grp << 2);
+  const int v_off1 = (v_cc << 7) + v_row * 16 + (lane & 1) * 8;
+  const int v_off2 = 1024 + ((v_cc ^ 1) << 7) + v_row * 16 + (lane & 1) * 8;
+  auto pv_softmax = [&](const uint8_t* vt, auto&& step_hook) __attribute__((always_inline)) {
+    constexpr int NPV = 4 * DB;
+    constexpr int VPF = 3;
+    constexpr int MAX_STEPS = NPV >= 16 ? 4 : 2;  // steps that carry the max reduction
+    const uint8_t* vl1 = vt + v_off1;
+    const uint8_t* vl2 = vt + v_off2;
+    i16x4 vlo[NPV], vhi[NPV];
+    auto load = [&](int i) __attribute__((always_inline)) {
+      const int kstep = i / DB, db = i % DB;
+      const int imm = (db >> 1) * 8192 + (db & 1) * 512 + kstep * 2048;
+      vlo[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vl1 + imm));
+      vhi[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vl2 + imm));
+    };
+    // VALU work: max over the 32 scores (MAX_STEPS steps), then 32 weights.
+    float part[MAX_STEPS];
+    float base = 0.f, rs = 0.f, p32[32];
+    auto valu = [&](int i) __attribute__((always_inline)) {
+      if (i < MAX_STEPS) {
+        constexpr int PER = 32 / MAX_STEPS;
+        float mx = sc[(i * PER) >> 4][(i * PER) & 15];
 #pragma unroll
-    for (int kstep = 0; kstep < 4; ++kstep) {
+        for (int e = 1; e < PER; ++e) mx = fmaxf(mx, sc[(i * PER + e) >> 4][(i * PER + e) & 15]);
+        part[i] = mx;
+        if (i == MAX_STEPS - 1) {
+          float m = part[0];
+#pragma unroll
+          for (int j = 1; j < MAX_STEPS; ++j) m = fmaxf(m, part[j]);
+          const float mxs = max_with_partner(m) * c;
+          m_true = fmaxf(m_true, mxs);
+          if (m_ref == kNegInf) m_ref = mxs;  // first tile with a visible key (O and l are still 0)
+          base = m_ref == kNegInf ? 0.f : m_ref;
+        }
+        return;
+      }
+      // weights of elements [e0, e1) of the 32 (kstep-major, 8 per pb entry)
+      const int n = NPV - MAX_STEPS;
+      const int e0 = ((i - MAX_STEPS) * 32) / n, e1 = ((i - MAX_STEPS + 1) * 32) / n;
+#pragma unroll
+      for (int e = e0; e < e1; ++e) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[e >> 4][e & 15], c, -base));
+        p32[e] = p;
+        rs += p;
+        if ((e & 7) == 7) pb_new[e >> 3] = E::from_f32(p32 + (e & ~7));
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < VPF && i < NPV; ++i) load(i);
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      if (i + VPF < NPV) load(i + VPF);
+      const int kstep = i / DB, db = i % DB;
+      i16x8 av = __builtin_shufflevector(vlo[i], vhi[i], 0, 1, 2, 3, 4, 5, 6, 7);
+      o[db] = E::mfma(__builtin_bit_cast(vec8, av), pb[kstep], o[db]);
+      valu(i);
+      step_hook(i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l += rs;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) pb[k] = pb_new[k];
+  };
+
+  // PV of the last tile (no softmax left to overlap).
+  auto pv_last = [&](const uint8_t* vt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kstep = 0; kstep < 4; ++kstep)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vl + lds_off(16 * kstep, 4 * db)));
-        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vl + lds_off(16 * kstep + 8, 4 * db)));
+        const int imm = (db >> 1) * 8192 + (db & 1) * 512 + kstep * 2048;
+        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vt + v_off1 + imm));
+        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vt + v_off2 + imm));
         i16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         o[db] = E::mfma(__builtin_bit_cast(vec8, av), pb[kstep], o[db]);
       }
-    }
-  };
-
-  // Weights of the current S into pb (the B operand of PV), and their sum.
-  auto softmax = [&](float alpha) {
-    const float base = m_ref == kNegInf ? 0.f : m_ref;
-    float rs = 0.f;
-#pragma unroll
-    for (int kstep = 0; kstep < 4; ++kstep) {
-      float p8[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sc[kstep >> 1][8 * (kstep & 1) + e], c, -base));
-        p8[e] = p;
-        rs += p;
-      }
-      pb[kstep] = E::from_f32(p8);
-    }
-    l = l * alpha + rs;
   };
 
   // ---- pipeline -----------------------------------------------------------
@@ -316,29 +400,29 @@ __global__ __launch_bounds__(256, 1) void attn_partial_kernel(AttnArgs a) {
   // ahead: K(it+1) and V(it) are issued at the start of iteration it.  The
   // V buffer of "tile -1" is zeroed and pb starts at 0, so iteration 0 runs
   // the same code (its PV adds exact zeros).
-#pragma unroll
-  for (int kstep = 0; kstep < 4; ++kstep) pb[kstep] = vec8{};
-  for (int i = tid; i < Gm::TILE_BYTES / 16; i += 256) *LDS_PTR(u32x4, vbuf1 + i * 16) = u32x4{0u, 0u, 0u, 0u};
   int pg0 = 0, pg1 = 0;  // pages of tiles it and it+1
-  if (n_tiles > 0) {
-    pg0 = pages(0);
-    issue(0, pg0, false, kbuf0);
-    pg1 = pages(1);
-  }
-
-  bool pend = false;       // O waits for a rescale by pend_alpha
-  float pend_alpha = 1.f;
-  auto body = [&](int it, auto masked) {
+  // vmcnt(0) with the other counters left alone (gfx9 s_waitcnt encoding).
+  constexpr int kWaitVmcnt0 = 0x0F70;
+  auto body = [&](int it, auto masked, auto parity) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
+    constexpr bool ODD = decltype(parity)::value;  // it is odd
     const int t0 = k0 + it * kTK;
     // K(it) and V(it-1) have landed in every wave; K(it-1), V(it-2) are free.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    if (it + 1 < n_tiles) issue(it + 1, pg1, false, (it & 1) ? kbuf0 : kbuf1);
-    issue(it, pg0, true, (it & 1) ? vbuf1 : vbuf0);
+    // The loads of K(it+1) and V(it) are spread over the MFMA steps (one per
+    // few MFMAs) rather than issued in a burst, which would stall the waves on
+    // a full address queue before any math starts.
+    // On the last tile the K load of "tile n_tiles" reads row kend-1 (the
+    // clamp above) into a buffer nothing reads again; keeping it unconditional
+    // keeps this a straight-line block.
+    const int pk = pg1, pv = pg0;
     pg0 = pg1;
     pg1 = pages(it + 2);
-    qk((it & 1) ? kbuf1 : kbuf0);
+    qk(ODD ? kbuf1 : kbuf0, [&](int ks) {
+      constexpr int EVERY = KS / LPW;
+      if (ks % EVERY == 0) issue_one(it + 1, pk, false, ODD ? kbuf0 : kbuf1, ks / EVERY);
+    });
     if constexpr (MASKED) {
       const int rel = lim - t0;
 #pragma unroll
@@ -349,40 +433,60 @@ __global__ __launch_bounds__(256, 1) void attn_partial_kernel(AttnArgs a) {
           sc[kb][r] = key > rel ? kNegInf : sc[kb][r];
         }
     }
-    float mx = sc[0][0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[0][r]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[1][r]);
-    const float mxs = max_with_partner(mx) * c;
-    // A raise of the reference max decided on the previous tile moves O to
-    // the new reference now, after PV(it-2) and before PV(it-1) (rare).
-    if (__ballot(pend)) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= pend_alpha;
+    // PV(it-1) with the previous weights, fused with this tile's softmax.
+    pv_softmax(ODD ? vbuf0 : vbuf1, [&](int i) {
+      constexpr int EVERY = 4 * DB / LPW;
+      if (i % EVERY == 0) issue_one(it, pv, true, ODD ? vbuf1 : vbuf0, i / EVERY);
+    });
+  };
+  // Tiles in even/odd pairs so that each body has its buffers fixed at compile
+  // time and the output accumulators flow through one chain of code.
+  auto run = [&](int& it, int end, auto masked) __attribute__((always_inline)) {
+    if (it < end && (it & 1)) {
+      body(it, masked, std::true_type{});
+      ++it;
     }
-    // Raise the reference max where this tile exceeds it by more than 2^8.
-    pend = mxs > m_ref + kRescaleLog2;
-    const float m_new = pend ? mxs : m_ref;
-    pend_alpha = __builtin_amdgcn_exp2f(m_ref - m_new);  // 1 where unchanged
-    m_ref = m_new;
-    // PV(it-1) reads the previous pb before softmax(it) rewrites it; the two
-    // are independent and form one block, so MFMA and VALU work interleave.
-    pv((it & 1) ? vbuf0 : vbuf1);
-    softmax(pend_alpha);
+    for (; it + 1 < end; it += 2) {
+      body(it, masked, std::false_type{});
+      body(it + 1, masked, std::true_type{});
+    }
+    if (it < end) {
+      body(it, masked, std::false_type{});
+      ++it;
+    }
   };
 
-  int it = 0;
-  for (; it < n_plain; ++it) body(it, std::false_type{});
-  for (; it < n_tiles; ++it) body(it, std::true_type{});
-  if (n_tiles > 0) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (__ballot(pend)) {
+  __shared__ int wg_redo[kWaves];
+  for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= pend_alpha;
+    for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+#pragma unroll
+    for (int kstep = 0; kstep < 4; ++kstep) pb[kstep] = vec8{};
+    l = 0.f;
+    for (int i = tid; i < Gm::TILE_BYTES / 16; i += 256) *LDS_PTR(u32x4, vbuf1 + i * 16) = u32x4{0u, 0u, 0u, 0u};
+    if (n_tiles > 0) {
+      pg0 = pages(0);
+      issue(0, pg0, false, kbuf0);
+      pg1 = pages(1);
     }
-    pv(((n_tiles - 1) & 1) ? vbuf1 : vbuf0);
+    int it = 0;
+    run(it, n_plain, std::false_type{});
+    run(it, n_tiles, std::true_type{});
+    if (n_tiles > 0) {
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+      if ((n_tiles - 1) & 1) pv_last(vbuf1);
+      else pv_last(vbuf0);
+    }
+    if (pass == 1) break;
+    // Did any query vector of the workgroup outgrow its reference?
+    const bool redo = __ballot(m_true > m_ref + kRefMarginLog2) != 0;
+    if (lane == 0) wg_redo[wave] = redo;
+    __syncthreads();
+    const bool any = wg_redo[0] | wg_redo[1] | wg_redo[2] | wg_redo[3];
+    __syncthreads();
+    if (!any) break;
+    m_ref = m_true;  // the exact max: every weight is at most 1 now
   }
 
   // Epilogue: combine the two lanes' sums; lane holds d = 32 db + 8 q + 4 h + 0..3.
