@@ -159,3 +159,45 @@ def test_full_size_workloads_sampled(name):
     _gpu.assert_close(got[rows].astype(np.float64), ref, f"{name} on {len(rows)} sampled rows")
     del d, out, out_c
     torch.cuda.empty_cache()
+
+
+def _plant_outlier(case, key, value):
+    """Shift component 0 of every query by +2 and set K[key, :, 0] = value, so
+    key `key` scores about 2 value / sqrt(d) for every row."""
+    from paged_kv_prefill_amd.synth import ENCODERS
+    import oracle
+    dec = oracle.decode_f16 if case.dtype == "f16" else oracle.decode_bf16
+    enc = ENCODERS[case.dtype]
+    q = dec(case.q).astype(np.float32)
+    q[:, :, 0] += 2.0
+    case.q = enc(q)
+    k = dec(case.k_contig).astype(np.float32)
+    k[key, :, 0] = value
+    case.k_contig = enc(k)
+    ps = case.page_size
+    case.k_pages[case.block_table[key // ps], key % ps] = case.k_contig[key]
+    return case
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("where", ["late", "first_tile"])
+def test_score_outlier_reference(dtype, where):
+    """A key whose score exceeds the first tile's max by more than 2^15 (log2)
+    sends the workgroup through the second, exact-max pass; an outlier in the
+    first tile only raises the reference.  Either way the output matches the
+    oracle, and rows that see the outlier take (almost) its value."""
+    import torch
+    case = synth.make_case("outlier", 3000, 64, 8, 2, 128, 16, dtype, seed=21)
+    key = 2900 if where == "late" else 5
+    case = _plant_outlier(case, key, 80.0)
+    print(f"case outlier {where} {dtype}: key {key} K[.,0]=80, q[.,0]+=2", flush=True)
+    d = _gpu.dev_case(case)
+    ref = _gpu.oracle_out(case)
+    for s in (1, 3):
+        out = run_paged(d, case, n_splits=s)
+        torch.cuda.synchronize()
+        got = _gpu.host_out(out)
+        if dtype == "f16":
+            _gpu.assert_close(got, ref, f"{where} S={s}")
+        else:
+            _gpu.assert_close_bf16_bound(got, ref, _gpu.oracle_abs_weighted(case), f"{where} S={s}")
