@@ -97,19 +97,33 @@ struct Geom {
 
 // LDS layout of a 64-key K or V tile: 1 KB blocks of 8 rows x 8 chunks
 // (16 bytes each).  Block (row / 8, c / 8) sits at ((c / 8) * 8 + row / 8) KB.
-// Inside a block, chunk c and row r occupy 16-byte unit
-//   ((c % 8) ^ (row / 8 % 2)) * 8 + ((row % 8) ^ 4 (c / 2 % 2)).
-// One direct-to-LDS load fills one block: its 64 lanes read 8 rows x 128
-// contiguous bytes (8 whole cache lines), and with pages of 8 tokens or more
-// the 8 rows lie in one page.  LDS has 64 four-byte banks; a 16-byte read is
-// served 16 lanes at a time and an 8-byte read 32 lanes at a time.  The two
-// XOR terms make every such group of the two MFMA operand reads below
-// (K: 16 rows x one chunk; V transposed: 4 rows x 4 chunks) cover all 64
-// banks once, and keep their addresses a per-lane base plus compile-time
-// offsets.
+// Inside a block, row r and chunk c occupy 16-byte unit
+//   (r % 8) * 8 + ((c % 8) ^ g(r)),   g(r) = ((r & 2) << 1) | ((r >> 2) & 3).
+// One direct-to-LDS load fills one block; lane L writes unit L, so each group
+// of 8 consecutive lanes reads 128 contiguous bytes of one row (in a permuted
+// order), which the address unit coalesces (a lane order that spreads
+// consecutive lanes over rows streams three times slower).  With pages of 8
+// tokens or more the 8 rows of a block lie in one page.  LDS has 64 four-byte
+// banks; a 16-byte read is served 16 lanes at a time and an 8-byte read 32
+// lanes at a time.  g() makes every such group of the two MFMA operand reads
+// below (K: 16 rows x one chunk; V transposed: 4 rows x 4 chunks) cover all 64
+// banks once.
+__device__ __forceinline__ constexpr int lds_g(int r) { return ((r & 2) << 1) | ((r >> 2) & 3); }
 __device__ __forceinline__ constexpr int lds_off(int row, int c) {
-  return (c >> 3) * 8192 + (row >> 3) * 1024 +
-         ((((c & 7) ^ ((row >> 3) & 1)) << 3) + ((row & 7) ^ (((c >> 1) & 1) << 2))) * 16;
+  return (c >> 3) * 8192 + (row >> 3) * 1024 + ((row & 7) * 8 + ((c & 7) ^ lds_g(row & 15))) * 16;
+}
+
+// Barrier for the tile loop, which keeps direct-to-LDS loads in flight across
+// it.  A workgroup-scope release (as in __syncthreads) must wait for every
+// LDS write in flight, those loads included (vmcnt(0)); instead the caller
+// waits for exactly the loads and LDS operations the next phase needs
+// (s_waitcnt vmcnt(n) lgkmcnt(0)), and the wavefront-scope fences only keep
+// the compiler from moving LDS accesses across the barrier.  LDS is one
+// memory per CU, so a write that has completed is seen by every wave.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
 __device__ __forceinline__ float max_with_partner(float x) {
@@ -200,6 +214,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
       qf[ks] = __builtin_bit_cast(vec8, raw);
     }
   }
+  // Wait for Q here, on every path: otherwise the compiler's wait before the
+  // first use of Q inside the tile loop covers every load in flight, on every
+  // iteration.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   f32x16 o[DB];
   float m_ref = kNegInf;  // softmax reference, scaled log2 domain
@@ -209,13 +227,15 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
   // ---- loader -------------------------------------------------------------
   // Block b = wave * LPW + i of a tile holds rows 8 (b % 8) .. +7 and chunks
-  // 8 (b / 8) .. +7; lane L loads row 8 (b % 8) + L % 8, chunk 8 (b / 8) + L / 8.
+  // 8 (b / 8) .. +7 (lds_off).
   const int hkvd2 = a.n_kv_heads * D * 2;  // bytes per token (all KV heads)
   const int ps_mask = (1 << a.log2_ps) - 1;
   const int cg = (wave * LPW) >> 3;        // the wave's chunk group (same for all its blocks)
-  // Lane L fills unit L of a block: row 8 rg + ((L % 8) ^ 4 (L / 16 % 2)),
-  // chunk 8 cg + ((L / 8) ^ (rg % 2)), rg = the block's row group.
-  const int lrow = (lane & 7) ^ (((lane >> 4) & 1) << 2);
+  // Lane L fills unit L of a block: row 8 rg + L / 8, chunk 8 cg + ((L % 8) ^ g(row)),
+  // rg = the block's row group; g depends on rg only through its parity.
+  const int lrow = lane >> 3;
+  const int cpart_even = (cg * 8 + ((lane & 7) ^ lds_g(lrow))) << 4;
+  const int cpart_odd = (cg * 8 + ((lane & 7) ^ lds_g(8 + lrow))) << 4;
   const char* kg = (const char*)a.k + g * D * 2;
   const char* vg = (const char*)a.v + g * D * 2;
 
@@ -240,7 +260,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const int last = kend - 1 - t0;
     const char* src = is_v ? vg : kg;
     const int b = wave * LPW + i;
-    const int cpart = (cg * 8 + ((lane >> 3) ^ (b & 1))) << 4;
+    const int cpart = (b & 1) ? cpart_odd : cpart_even;
     if constexpr (AM == Addr::PageLane) {
       const int rr = min(8 * (b & 7) + lrow, last);
       const int pg = __shfl(page, rr, 64);
@@ -269,6 +289,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   // S^T[key][qv] = K Q^T for the 64 keys of a tile: lane holds qv = lane & 31
   // and keys 32 kb + 8 (r / 4) + 4 h + r % 4.
   f32x16 sc[2];
+  // lds_off(lane % 32 + 32 kb, 2 ks + h) = (kofs ^ (ks % 4) 32) + (ks / 4) 8192 + kb 4096
+  const int kofs = ((lane >> 3) & 3) * 1024 + (lane & 7) * 128 + ((h ^ lds_g(lane & 15)) << 4);
   // The operand reads run QPF steps ahead of their MFMAs; sched_barrier pins
   // that order (the compiler otherwise waits on each read right before its
   // MFMA).
@@ -276,15 +298,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     constexpr int QPF = 3;
     sc[0] = f32x16{};
     sc[1] = f32x16{};
-    const int kr = lane & 31;
-    const int kbase = (kr >> 3) * 1024 + ((h ^ ((kr >> 3) & 1)) << 7);
-    const uint8_t* kl0 = kt + kbase + (kr & 7) * 16;
-    const uint8_t* kl1 = kt + kbase + ((kr & 7) ^ 4) * 16;
     i16x8 k0r[KS], k1r[KS];
     auto load = [&](int ks) __attribute__((always_inline)) {
-      // lds_off(row, 2 ks + h) = base[ks % 2] + (ks / 4) 8192 + (ks % 4) 256, row = lane % 32
-      const uint8_t* kl = (ks & 1) ? kl1 : kl0;
-      const int imm = (ks >> 2) * 8192 + (ks & 3) * 256;
+      const uint8_t* kl = kt + (kofs ^ ((ks & 3) << 5));
+      const int imm = (ks >> 2) * 8192;
       k0r[ks] = *LDS_PTR(const i16x8, kl + imm);
       k1r[ks] = *LDS_PTR(const i16x8, kl + imm + 4096);
     };
@@ -311,25 +328,22 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   // the interleave.  The two halves are independent: PV reads pb, softmax
   // writes pb_new.
   vec8 pb[4], pb_new[4];
-  // lds_off(16 kstep + r (+ 8), 4 db + cc) + within = base1 (base2) + (db / 2) 8192 + (db % 2) 512
-  // + kstep 2048 (+ 1024), r = 4 h + (lane % 16) / 4, cc = 2 grp + (lane % 4) / 2
-  const int v_grp = (lane >> 4) & 1;
-  const int v_cc = 2 * v_grp + ((lane & 3) >> 1);
-  const int v_row = (4 * h + ((lane & 15) >> 2)) ^ (v_grp << 2);
-  const int v_off1 = (v_cc << 7) + v_row * 16 + (lane & 1) * 8;
-  const int v_off2 = 1024 + ((v_cc ^ 1) << 7) + v_row * 16 + (lane & 1) * 8;
+  // lds_off(16 kstep + vr (+ 8), 4 db + cc) + within = (vofs1 (vofs2) ^ (db % 2) 64)
+  // + (db / 2) 8192 + kstep 2048, vr = 4 h + (lane % 16) / 4, cc = 2 ((lane / 16) % 2) + (lane % 4) / 2
+  const int v_r = 4 * h + ((lane & 15) >> 2);
+  const int v_cc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int vofs1 = v_r * 128 + ((v_cc ^ lds_g(v_r)) << 4) + (lane & 1) * 8;
+  const int vofs2 = 1024 + v_r * 128 + ((v_cc ^ lds_g(v_r + 8)) << 4) + (lane & 1) * 8;
   auto pv_softmax = [&](const uint8_t* vt, auto&& step_hook) __attribute__((always_inline)) {
     constexpr int NPV = 4 * DB;
     constexpr int VPF = 3;
     constexpr int MAX_STEPS = NPV >= 16 ? 4 : 2;  // steps that carry the max reduction
-    const uint8_t* vl1 = vt + v_off1;
-    const uint8_t* vl2 = vt + v_off2;
     i16x4 vlo[NPV], vhi[NPV];
     auto load = [&](int i) __attribute__((always_inline)) {
       const int kstep = i / DB, db = i % DB;
-      const int imm = (db >> 1) * 8192 + (db & 1) * 512 + kstep * 2048;
-      vlo[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vl1 + imm));
-      vhi[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vl2 + imm));
+      const int imm = (db >> 1) * 8192 + kstep * 2048;
+      vlo[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vt + (vofs1 ^ ((db & 1) << 6)) + imm));
+      vhi[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vt + (vofs2 ^ ((db & 1) << 6)) + imm));
     };
     // VALU work: max over the 32 scores (MAX_STEPS steps), then 32 weights.
     float part[MAX_STEPS];
@@ -386,9 +400,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     for (int kstep = 0; kstep < 4; ++kstep)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const int imm = (db >> 1) * 8192 + (db & 1) * 512 + kstep * 2048;
-        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vt + v_off1 + imm));
-        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vt + v_off2 + imm));
+        const int imm = (db >> 1) * 8192 + kstep * 2048;
+        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vt + (vofs1 ^ ((db & 1) << 6)) + imm));
+        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vt + (vofs2 ^ ((db & 1) << 6)) + imm));
         i16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         o[db] = E::mfma(__builtin_bit_cast(vec8, av), pb[kstep], o[db]);
       }
@@ -401,15 +415,22 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   // V buffer of "tile -1" is zeroed and pb starts at 0, so iteration 0 runs
   // the same code (its PV adds exact zeros).
   int pg0 = 0, pg1 = 0;  // pages of tiles it and it+1
-  // vmcnt(0) with the other counters left alone (gfx9 s_waitcnt encoding).
+  // vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding:
+  // vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
   constexpr int kWaitVmcnt0 = 0x0F70;
+  // vmcnt(LPW) lgkmcnt(0): before the tile loop's barriers.
+  constexpr int kWaitVmcntLPW = 0x0070 | (LPW & 15) | ((LPW >> 4) << 14);
+  static_assert(LPW < 64, "vmcnt holds 6 bits");
   auto body = [&](int it, auto masked, auto parity) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
     constexpr bool ODD = decltype(parity)::value;  // it is odd
     const int t0 = k0 + it * kTK;
-    // K(it) and V(it-1) have landed in every wave; K(it-1), V(it-2) are free.
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
+    // This wave's loads in flight, oldest first: K(it) (issued during the QK
+    // of it-1), V(it-1) (during the PV phase of it-1), LPW each.  Wait for
+    // K(it) only; after the barrier K(it) is in LDS and the buffers of K(it-1)
+    // and V(it-2) are free (every wave is done with body it-1).
+    __builtin_amdgcn_s_waitcnt(kWaitVmcntLPW);
+    lds_barrier();
     // The loads of K(it+1) and V(it) are spread over the MFMA steps (one per
     // few MFMAs) rather than issued in a burst, which would stall the waves on
     // a full address queue before any math starts.
@@ -433,6 +454,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
           sc[kb][r] = key > rel ? kNegInf : sc[kb][r];
         }
     }
+    // Now in flight: V(it-1), then K(it+1).  Wait for V(it-1), which the PV
+    // below reads, so that its load latency hides behind the QK phase.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcntLPW);
+    lds_barrier();
     // PV(it-1) with the previous weights, fused with this tile's softmax.
     pv_softmax(ODD ? vbuf0 : vbuf1, [&](int i) {
       constexpr int EVERY = 4 * DB / LPW;
@@ -468,6 +493,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
       pg0 = pages(0);
       issue(0, pg0, false, kbuf0);
       pg1 = pages(1);
+      // K(0) is the only load in flight: the first body's vmcnt(LPW) would not wait for it.
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     }
     int it = 0;
     run(it, n_plain, std::false_type{});
