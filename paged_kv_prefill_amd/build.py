@@ -3,6 +3,13 @@
 hipcc cross-compiles for gfx950 without a GPU.  Packed fp32 instructions are
 disabled for the device code (they are emitted by the compiler on its own
 from plain float code otherwise).
+
+MFMA instructions are selected in their VGPR form (accumulator and result in
+the unified register file, moved to AGPRs only where the register allocator
+wants).  In the default AGPR form every score tile the softmax reads is
+copied out of AGPRs, and the allocator parks output accumulators in VGPRs
+around the score tiles, which costs some 60-130 extra moves per key tile.
+PPA_MFMA_VGPR_FORM=0 selects the AGPR form for comparison.
 """
 
 import os
@@ -18,9 +25,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-if os.environ.get("PPA_MFMA_VGPR_FORM"):
-    DEVICE_FLAGS += ["-mllvm", "-amdgpu-mfma-vgpr-form=" + os.environ["PPA_MFMA_VGPR_FORM"]]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-mfma-vgpr-form=" + os.environ.get("PPA_MFMA_VGPR_FORM", "1")]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 

@@ -12,21 +12,23 @@
 // one (row, head) pair of the head group, flattened row-major, so the G heads
 // of a row share a causal limit and every K/V byte staged in LDS serves
 // 128 queries.  Per 64-key tile:
-//   * K and V rows stream from HBM straight into LDS with 16-byte
-//     global_load_lds (no VGPR staging), double-buffered so the next tile's
-//     loads overlap this tile's math.  Paged addressing reads one block-table
-//     entry per key, prefetched one tile ahead and shared across the wave by
-//     a lane shuffle; contiguous addressing is the identity.  Chunks are
-//     XOR-swizzled per row so the MFMA operand reads below do not collide in
-//     LDS banks.
+//   * K and V rows stream from memory straight into LDS with 16-byte
+//     buffer_load ... lds (no VGPR staging), double-buffered: K of the next
+//     tile and V of this one load while this tile's QK and the previous
+//     tile's PV run.  Paged addressing reads the block-table entries of a
+//     tile once (one per lane), turns them into per-lane page addresses with
+//     one 64-bit multiply-add, and each load takes its page base from one
+//     lane; contiguous addressing is a per-tile base.  Rows are stored
+//     row-major in 8x8-chunk blocks with an XOR swizzle so the MFMA operand
+//     reads below do not collide in LDS banks.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_{f16,bf16}: K is the A operand
-//     (ds_read_b128), Q stays in VGPRs as the B operand for the whole kernel.
-//     Each lane then owns one query vector and 32 of the tile's 64 keys, so
-//     row max and row sum need only one cross-lane exchange
+//     (ds_read_b128), Q stays in registers as the B operand for the whole
+//     kernel.  Each lane then owns one query vector and 32 of the tile's 64
+//     keys, so a row max needs only one cross-lane exchange
 //     (v_permlane32_swap) with the lane holding the other 32 keys.
-//   * fp32 online softmax in the log2 domain (scale * log2 e folded into one
-//     FMA before v_exp_f32); the O rescale is skipped when no lane's max
-//     moved, which is exact (the factor would be 1.0).
+//   * Softmax weights exp2(s c - m_ref) in fp32 (scale * log2 e folded into
+//     one FMA before v_exp_f32) against a fixed per-row reference, so the
+//     output accumulators are never rescaled (see kRefMarginLog2 below).
 //   * O^T += V^T P^T on the same MFMA: V^T is read with ds_read_b64_tr_b16,
 //     which transposes 16-bit elements across lanes, so V stays row-major in
 //     LDS; P's registers are already the B operand's layout.
@@ -65,6 +67,13 @@ struct F16 {
   static __device__ __forceinline__ uint16_t bits(float x) {
     return __builtin_bit_cast(uint16_t, (_Float16)x);
   }
+  // acc + the sum of the 8 elements (v_dot2c_f32_f16 against (1, 1), fp32 accumulation)
+  static __device__ __forceinline__ float sum8(vec8 v, float acc) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) acc = __builtin_amdgcn_fdot2(f16x2{v[e], v[e + 1]}, f16x2{1, 1}, acc, false);
+    return acc;
+  }
 };
 
 struct BF16 {
@@ -80,6 +89,13 @@ struct BF16 {
   }
   static __device__ __forceinline__ uint16_t bits(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
+  }
+  static __device__ __forceinline__ float sum8(vec8 v, float acc) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int e = 0; e < 8; e += 2)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[e], v[e + 1]}, bf16x2{1, 1}, acc, false);
+    return acc;
   }
 };
 
@@ -126,6 +142,29 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
+// A wave-uniform pointer pinned to scalar registers (a buffer descriptor
+// must be uniform; this keeps the compiler from treating it as per-lane).
+__device__ __forceinline__ const char* scalar_ptr(const char* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char*)(((uint64_t)hi << 32) | lo);
+}
+
+// 16-byte direct-to-LDS load of lane bytes [base + voff, +16) into lds + 16 lane
+// (lds is wave-uniform), as buffer_load_dwordx4 ... lds.  The buffer
+// (MUBUF) form rather than global_load_lds: the compiler counts a global
+// (FLAT-encoded) load that writes LDS against both vmcnt and lgkmcnt, and
+// then waits for lgkmcnt(0) at the next use of any LDS read result, which
+// would drain the operand-read prefetch after every K/V load.  Descriptor:
+// base = the scalar base, stride 0, no practical range limit (offsets stay
+// below 2^31), 32-bit data format (word 3 = 0x20000).
+// soff is a wave-uniform byte offset added to every lane's address.
+__device__ __forceinline__ void load_lds16(const char* base, uint32_t voff, int soff, void* lds) {
+  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)scalar_ptr(base), (short)0, 0x7fffffff, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(void, lds), 16, (int)voff, __builtin_amdgcn_readfirstlane(soff), 0, 0);
+}
+
 __device__ __forceinline__ float max_with_partner(float x) {
   // v_permlane32_swap pairs lane l with lane l^32; both results hold the pair.
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -136,12 +175,14 @@ __device__ __forceinline__ float sum_with_partner(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);  // same order on both lanes
 }
 
-// How K/V rows are addressed.  Contig: [ctx][Hkv][d].  PageWave: pages of
-// 16 tokens or more; the 16 rows one wave loads per tile then lie in one page,
-// so the page is wave-uniform and an address is a scalar base plus a per-lane
-// offset that does not change from tile to tile.  PageLane: smaller pages;
-// every row looks up its own page.
-enum class Addr { Contig, PageWave, PageLane };
+// How K/V rows are addressed.  Contig: [ctx][Hkv][d].  Paged: pages of
+// `page_size` tokens, each [page_size][Hkv][d].  Page16: pages of 16 tokens or
+// more, so the 16 rows of two neighbouring 8-row groups share a page; Page8:
+// pages of 8 tokens, one page per 8-row group.  Either way the 8 rows one
+// direct-to-LDS load covers lie in one page, the page is wave-uniform, and an
+// address is a scalar base plus a per-lane offset that does not change from
+// tile to tile.  PageLane: smaller pages; every row looks up its own page.
+enum class Addr { Contig, Page16, Page8, PageLane };
 
 // The softmax weights are exp2(s c - m_ref) with a fixed reference m_ref per
 // query vector instead of a running max, so the output accumulators are never
@@ -200,9 +241,13 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   const int kend = min(k1, (int)(a.history + r_last + 1));
   const int n_tiles = kend > k0 ? (kend - k0 + kTK - 1) / kTK : 0;
   const int lim = (int)a.history + row;             // last key this query vector sees
-  // Tiles ending at or before the first row's last key need no mask.
+  // Tiles ending at or before the first row's last key need no mask, and they
+  // are whole (split bounds are multiples of the tile).  A body works on tile
+  // it and loads tile it+1, so the fast body (no mask, no load clamp) runs
+  // while both are such tiles: it < n_fast.
   const int mask_x = (int)a.history + r_first - k0 - (kTK - 1);
   const int n_plain = min(n_tiles, mask_x < 0 ? 0 : mask_x / kTK + 1);
+  const int n_fast = n_plain > 0 ? n_plain - 1 : 0;
 
   // Q fragments (B operand of QK): lane holds Q[f][16 ks + 8 h .. +7].
   vec8 qf[KS];
@@ -236,8 +281,26 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   const int lrow = lane >> 3;
   const int cpart_even = (cg * 8 + ((lane & 7) ^ lds_g(lrow))) << 4;
   const int cpart_odd = (cg * 8 + ((lane & 7) ^ lds_g(8 + lrow))) << 4;
+  // Lane byte offsets within an 8-row group for whole tiles (tile to tile only
+  // the group's scalar base changes).
+  const uint32_t voff_even = lrow * hkvd2 + cpart_even;
+  const uint32_t voff_odd = lrow * hkvd2 + cpart_odd;
+  // Row group rg_i = (wave LPW + i) % 8 of load i starts soff[i] bytes into
+  // its page (paged, plus the tile's own offset in the page when pages are
+  // longer than a tile) or into the tile (contiguous).
+  int soff[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int rg = (wave * LPW + i) & 7;
+    soff[i] = (PAGED ? ((8 * rg) & ps_mask) : 8 * rg) * hkvd2;
+  }
   const char* kg = (const char*)a.k + g * D * 2;
   const char* vg = (const char*)a.v + g * D * 2;
+  const uint32_t page_bytes = (uint32_t)hkvd2 << a.log2_ps;
+  // Per lane: address of pool page `page` (of K or V).
+  auto page_addr = [&](int page, bool is_v) __attribute__((always_inline)) -> uint64_t {
+    return (uint64_t)(is_v ? vg : kg) + (uint64_t)(uint32_t)page * page_bytes;
+  };
 
   // Pool page of key (tile j start + lane).  The key is clamped to kend-1, so
   // the block-table read is always in range (lanes and tiles past the end read
@@ -255,13 +318,33 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   // lrow_c = min(lrow, kend-1-t0-r0c), whole tiles read their own rows and the
   // last tile's rows past kend-1 read row kend-1 (same 8-row group, so the
   // same page).  `page` holds the pool page of key (tile start + lane).
-  auto issue_one = [&](int j, int page, bool is_v, uint8_t* dst, int i) __attribute__((always_inline)) {
+  // WHOLE: the caller knows tile j lies below kend, so the clamp is skipped:
+  // the address is a scalar base (one lane read for the page) plus a
+  // loop-invariant lane offset.
+  // `paddr` = page_addr(page, is_v), used by the WHOLE paged form: the lane
+  // holding key t0 + 8 rg holds the page of row group rg (with Page16 so does
+  // the lane of key t0 + 16 (rg / 2), which lets two loads share one lookup).
+  auto issue_one = [&](int j, int page, uint64_t paddr, bool is_v, uint8_t* dst, int i, auto whole)
+                       __attribute__((always_inline)) {
+    constexpr bool WHOLE = decltype(whole)::value;
     const int t0 = k0 + j * kTK;
     const int last = kend - 1 - t0;
     const char* src = is_v ? vg : kg;
     const int b = wave * LPW + i;
     const int cpart = (b & 1) ? cpart_odd : cpart_even;
-    if constexpr (AM == Addr::PageLane) {
+    if constexpr (WHOLE && AM != Addr::PageLane) {
+      const uint32_t voff = (b & 1) ? voff_odd : voff_even;
+      if constexpr (AM == Addr::Contig) {
+        load_lds16(src + (int64_t)t0 * hkvd2, voff, soff[i], dst + b * 1024);
+      } else {
+        const int rg = b & 7;
+        const int ln = AM == Addr::Page16 ? 16 * (rg >> 1) : 8 * rg;
+        const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)paddr, ln);
+        const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(paddr >> 32), ln);
+        load_lds16((const char*)(((uint64_t)hi << 32) | lo), voff, (t0 & ps_mask) * hkvd2 + soff[i],
+                   dst + b * 1024);
+      }
+    } else if constexpr (AM == Addr::PageLane) {
       const int rr = min(8 * (b & 7) + lrow, last);
       const int pg = __shfl(page, rr, 64);
       const int64_t tok = ((int64_t)pg << a.log2_ps) + ((t0 + rr) & ps_mask);
@@ -276,13 +359,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         const int pg = __builtin_amdgcn_readlane(page, r0c);
         base = src + (((int64_t)pg << a.log2_ps) + ((t0 + r0c) & ps_mask)) * hkvd2;
       }
-      __builtin_amdgcn_global_load_lds((const void*)(base + (uint32_t)(lrow_c * hkvd2 + cpart)),
-                                       LDS_PTR(void, dst + b * 1024), 16, 0, 0);
+      load_lds16(base, (uint32_t)(lrow_c * hkvd2 + cpart), 0, dst + b * 1024);
     }
   };
   auto issue = [&](int j, int page, bool is_v, uint8_t* dst) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) issue_one(j, page, is_v, dst, i);
+    for (int i = 0; i < LPW; ++i) issue_one(j, page, 0, is_v, dst, i, std::false_type{});
   };
 
   // ---- MFMA phases --------------------------------------------------------
@@ -371,10 +453,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
       const int e0 = ((i - MAX_STEPS) * 32) / n, e1 = ((i - MAX_STEPS + 1) * 32) / n;
 #pragma unroll
       for (int e = e0; e < e1; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sc[e >> 4][e & 15], c, -base));
-        p32[e] = p;
-        rs += p;
-        if ((e & 7) == 7) pb_new[e >> 3] = E::from_f32(p32 + (e & ~7));
+        p32[e] = __builtin_amdgcn_exp2f(fmaf(sc[e >> 4][e & 15], c, -base));
+        if ((e & 7) == 7) {
+          // The sum takes the rounded weights, the ones the PV product uses.
+          pb_new[e >> 3] = E::from_f32(p32 + (e & ~7));
+          rs = E::sum8(pb_new[e >> 3], rs);
+        }
       }
     };
 #pragma unroll
@@ -440,9 +524,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const int pk = pg1, pv = pg0;
     pg0 = pg1;
     pg1 = pages(it + 2);
+    const uint64_t pka = PAGED && !MASKED ? page_addr(pk, false) : 0;
+    const uint64_t pva = PAGED && !MASKED ? page_addr(pv, true) : 0;
     qk(ODD ? kbuf1 : kbuf0, [&](int ks) {
       constexpr int EVERY = KS / LPW;
-      if (ks % EVERY == 0) issue_one(it + 1, pk, false, ODD ? kbuf0 : kbuf1, ks / EVERY);
+      if (ks % EVERY == 0)
+        issue_one(it + 1, pk, pka, false, ODD ? kbuf0 : kbuf1, ks / EVERY, std::bool_constant<!MASKED>{});
     });
     if constexpr (MASKED) {
       const int rel = lim - t0;
@@ -461,7 +548,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // PV(it-1) with the previous weights, fused with this tile's softmax.
     pv_softmax(ODD ? vbuf0 : vbuf1, [&](int i) {
       constexpr int EVERY = 4 * DB / LPW;
-      if (i % EVERY == 0) issue_one(it, pv, true, ODD ? vbuf1 : vbuf0, i / EVERY);
+      if (i % EVERY == 0)
+        issue_one(it, pv, pva, true, ODD ? vbuf1 : vbuf0, i / EVERY, std::bool_constant<!MASKED>{});
     });
   };
   // Tiles in even/odd pairs so that each body has its buffers fixed at compile
@@ -497,7 +585,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     }
     int it = 0;
-    run(it, n_plain, std::false_type{});
+    run(it, n_fast, std::false_type{});
     run(it, n_tiles, std::true_type{});
     if (n_tiles > 0) {
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -585,7 +673,8 @@ hipError_t launch_attn_t(const AttnArgs& a, int grid, hipStream_t stream) {
 template <int D, class E>
 hipError_t launch_attn_p(const AttnArgs& a, bool paged, int grid, hipStream_t stream) {
   if (!paged) return launch_attn_t<D, E, Addr::Contig>(a, grid, stream);
-  if (a.log2_ps >= 3) return launch_attn_t<D, E, Addr::PageWave>(a, grid, stream);
+  if (a.log2_ps >= 4) return launch_attn_t<D, E, Addr::Page16>(a, grid, stream);
+  if (a.log2_ps == 3) return launch_attn_t<D, E, Addr::Page8>(a, grid, stream);
   return launch_attn_t<D, E, Addr::PageLane>(a, grid, stream);
 }
 
