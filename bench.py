@@ -16,7 +16,6 @@ step's value.  Prints one JSON line.
 """
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -45,11 +44,8 @@ def parse():
 
 
 def kernel_source_hash():
-    h = hashlib.sha256()
-    for f in ("attention.hip", "kernels.h"):
-        with open(os.path.join(ROOT, "paged_kv_prefill_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+    from paged_kv_prefill_amd.profsum import kernel_source_hash as h
+    return h()
 
 
 def load_traffic(kernel_hash):

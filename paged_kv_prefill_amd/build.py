@@ -6,10 +6,11 @@ from plain float code otherwise).
 
 MFMA instructions are selected in their VGPR form (accumulator and result in
 the unified register file, moved to AGPRs only where the register allocator
-wants).  In the default AGPR form every score tile the softmax reads is
+wants): in the default AGPR form every score tile the softmax reads is
 copied out of AGPRs, and the allocator parks output accumulators in VGPRs
-around the score tiles, which costs some 60-130 extra moves per key tile.
-PPA_MFMA_VGPR_FORM=0 selects the AGPR form for comparison.
+around the score tiles, some 60-130 extra moves per key tile.  Each head
+dimension has its own translation unit so the choice can differ per head
+dimension; PPA_MFMA_VGPR_FORM=0 selects the AGPR form for comparison.
 """
 
 import os
@@ -25,8 +26,13 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                "-mllvm", "-amdgpu-mfma-vgpr-form=" + os.environ.get("PPA_MFMA_VGPR_FORM", "1")]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# device sources and their MFMA register form
+KERNEL_SOURCES = (
+    ("attention.hip", "0"),
+    ("attention_d64_d128.hip", os.environ.get("PPA_MFMA_VGPR_FORM", "1")),
+    ("attention_d256.hip", os.environ.get("PPA_MFMA_VGPR_FORM", "1")),
+)
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
@@ -45,11 +51,12 @@ def _run(cmd, verbose):
 def build(verbose=False, resource_usage=False):
     os.makedirs(BUILD_DIR, exist_ok=True)
     objs = []
-    kern_obj = os.path.join(BUILD_DIR, "attention.o")
     extra = ["-Rpass-analysis=kernel-resource-usage"] if resource_usage else []
-    _run([HIPCC, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, *extra, "-c",
-          os.path.join(CSRC, "attention.hip"), "-o", kern_obj], verbose or resource_usage)
-    objs.append(kern_obj)
+    for src, vgpr_form in KERNEL_SOURCES:
+        kern_obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
+        _run([HIPCC, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, "-mllvm", "-amdgpu-mfma-vgpr-form=" + vgpr_form,
+              *extra, "-c", os.path.join(CSRC, src), "-o", kern_obj], verbose or resource_usage)
+        objs.append(kern_obj)
     for src in ("api.cpp", "plan.cpp"):
         obj = os.path.join(BUILD_DIR, src.replace(".cpp", ".o"))
         _run([HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj], verbose)

@@ -1,0 +1,662 @@
+// Device code of the split-partial attention kernel, included by the
+// translation units that instantiate it for each head dimension (they are
+// compiled with their own register-allocation options).
+//
+// Chunked prefill attention over a paged KV cache: the split-partial kernel
+// and the log-sum-exp merge kernel, written for gfx950 (CDNA4, wave64).
+//
+// What is computed (issue "Metal: paged-KV prefill is 4.43x slower than
+// contiguous KV at 32K"; PR "perf: scale prefill attention splits with GPU
+// cores on Apple7/8", "What changed" and "Testing"): chunk row i at position
+// H+i attends to keys 0..H+i; query head h reads KV head h / G; the key axis
+// is cut into splits whose partials (output normalised by its own softmax
+// sum, plus its log-sum-exp) are merged by a second kernel.
+//
+// Workgroup = 4 waves = 128 query vectors of one KV head.  A query vector is
+// one (row, head) pair of the head group, flattened row-major, so the G heads
+// of a row share a causal limit and every K/V byte staged in LDS serves
+// 128 queries.  Per 64-key tile:
+//   * K and V rows stream from memory straight into LDS with 16-byte
+//     buffer_load ... lds (no VGPR staging), double-buffered: K of the next
+//     tile and V of this one load while this tile's QK and the previous
+//     tile's PV run.  Paged addressing reads the block-table entries of a
+//     tile once (one per lane), turns them into per-lane page addresses with
+//     one 64-bit multiply-add, and each load takes its page base from one
+//     lane; contiguous addressing is a per-tile base.  Rows are stored
+//     row-major in 8x8-chunk blocks with an XOR swizzle so the MFMA operand
+//     reads below do not collide in LDS banks.
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_{f16,bf16}: K is the A operand
+//     (ds_read_b128), Q stays in registers as the B operand for the whole
+//     kernel.  Each lane then owns one query vector and 32 of the tile's 64
+//     keys, so a row max needs only one cross-lane exchange
+//     (v_permlane32_swap) with the lane holding the other 32 keys.
+//   * Softmax weights exp2(s c - m_ref) in fp32 (scale * log2 e folded into
+//     one FMA before v_exp_f32) against a fixed per-row reference, so the
+//     output accumulators are never rescaled (see kRefMarginLog2 below).
+//   * O^T += V^T P^T on the same MFMA: V^T is read with ds_read_b64_tr_b16,
+//     which transposes 16-bit elements across lanes, so V stays row-major in
+//     LDS; P's registers are already the B operand's layout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "kernels.h"
+
+namespace ppa {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+struct F16 {
+  using vec8 = f16x8;
+  static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ vec8 from_f32(const float* x) {
+    vec8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (_Float16)x[e];
+    return r;
+  }
+  static __device__ __forceinline__ uint16_t bits(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+  }
+  // acc + the sum of the 8 elements (v_dot2c_f32_f16 against (1, 1), fp32 accumulation)
+  static __device__ __forceinline__ float sum8(vec8 v, float acc) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) acc = __builtin_amdgcn_fdot2(f16x2{v[e], v[e + 1]}, f16x2{1, 1}, acc, false);
+    return acc;
+  }
+};
+
+struct BF16 {
+  using vec8 = bf16x8;
+  static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ vec8 from_f32(const float* x) {
+    vec8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (__bf16)x[e];
+    return r;
+  }
+  static __device__ __forceinline__ uint16_t bits(float x) {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+  }
+  static __device__ __forceinline__ float sum8(vec8 v, float acc) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int e = 0; e < 8; e += 2)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[e], v[e + 1]}, bf16x2{1, 1}, acc, false);
+    return acc;
+  }
+};
+
+constexpr int kTK = 64;        // keys per tile
+constexpr int kWaves = 4;
+constexpr float kNegInf = -__builtin_inff();
+
+template <int D>
+struct Geom {
+  static constexpr int CH = D / 8;                 // 16-byte chunks per K/V row
+  static constexpr int TILE_BYTES = kTK * D * 2;   // one K (or V) tile
+  static constexpr int BLOCKS = TILE_BYTES / 1024; // 1 KB blocks per tile
+  static constexpr int LPW = BLOCKS / kWaves;      // blocks one wave loads per tile
+};
+
+// LDS layout of a 64-key K or V tile: 1 KB blocks of 8 rows x 8 chunks
+// (16 bytes each).  Block (row / 8, c / 8) sits at ((c / 8) * 8 + row / 8) KB.
+// Inside a block, row r and chunk c occupy 16-byte unit
+//   (r % 8) * 8 + ((c % 8) ^ g(r)),   g(r) = ((r & 2) << 1) | ((r >> 2) & 3).
+// One direct-to-LDS load fills one block; lane L writes unit L, so each group
+// of 8 consecutive lanes reads 128 contiguous bytes of one row (in a permuted
+// order), which the address unit coalesces (a lane order that spreads
+// consecutive lanes over rows streams three times slower).  With pages of 8
+// tokens or more the 8 rows of a block lie in one page.  LDS has 64 four-byte
+// banks; a 16-byte read is served 16 lanes at a time and an 8-byte read 32
+// lanes at a time.  g() makes every such group of the two MFMA operand reads
+// below (K: 16 rows x one chunk; V transposed: 4 rows x 4 chunks) cover all 64
+// banks once.
+__device__ __forceinline__ constexpr int lds_g(int r) { return ((r & 2) << 1) | ((r >> 2) & 3); }
+__device__ __forceinline__ constexpr int lds_off(int row, int c) {
+  return (c >> 3) * 8192 + (row >> 3) * 1024 + ((row & 7) * 8 + ((c & 7) ^ lds_g(row & 15))) * 16;
+}
+
+// Barrier for the tile loop, which keeps direct-to-LDS loads in flight across
+// it.  A workgroup-scope release (as in __syncthreads) must wait for every
+// LDS write in flight, those loads included (vmcnt(0)); instead the caller
+// waits for exactly the loads and LDS operations the next phase needs
+// (s_waitcnt vmcnt(n) lgkmcnt(0)), and the wavefront-scope fences only keep
+// the compiler from moving LDS accesses across the barrier.  LDS is one
+// memory per CU, so a write that has completed is seen by every wave.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+// A wave-uniform pointer pinned to scalar registers (a buffer descriptor
+// must be uniform; this keeps the compiler from treating it as per-lane).
+__device__ __forceinline__ const char* scalar_ptr(const char* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char*)(((uint64_t)hi << 32) | lo);
+}
+
+// 16-byte direct-to-LDS load of lane bytes [base + voff, +16) into lds + 16 lane
+// (lds is wave-uniform), as buffer_load_dwordx4 ... lds.  The buffer
+// (MUBUF) form rather than global_load_lds: the compiler counts a global
+// (FLAT-encoded) load that writes LDS against both vmcnt and lgkmcnt, and
+// then waits for lgkmcnt(0) at the next use of any LDS read result, which
+// would drain the operand-read prefetch after every K/V load.  Descriptor:
+// base = the scalar base, stride 0, no practical range limit (offsets stay
+// below 2^31), 32-bit data format (word 3 = 0x20000).
+// soff is a wave-uniform byte offset added to every lane's address.
+__device__ __forceinline__ void load_lds16(const char* base, uint32_t voff, int soff, void* lds) {
+  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)scalar_ptr(base), (short)0, 0x7fffffff, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(void, lds), 16, (int)voff, __builtin_amdgcn_readfirstlane(soff), 0, 0);
+}
+
+__device__ __forceinline__ float max_with_partner(float x) {
+  // v_permlane32_swap pairs lane l with lane l^32; both results hold the pair.
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_with_partner(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);  // same order on both lanes
+}
+
+// How K/V rows are addressed.  Contig: [ctx][Hkv][d].  Paged: pages of
+// `page_size` tokens, each [page_size][Hkv][d].  Page16: pages of 16 tokens or
+// more, so the 16 rows of two neighbouring 8-row groups share a page; Page8:
+// pages of 8 tokens, one page per 8-row group.  Either way the 8 rows one
+// direct-to-LDS load covers lie in one page, the page is wave-uniform, and an
+// address is a scalar base plus a per-lane offset that does not change from
+// tile to tile.  PageLane: smaller pages; every row looks up its own page.
+enum class Addr { Contig, Page16, Page8, PageLane };
+
+// The softmax weights are exp2(s c - m_ref) with a fixed reference m_ref per
+// query vector instead of a running max, so the output accumulators are never
+// rescaled inside the key loop.  The reference is the max of the first tile
+// that has a visible key; later weights may exceed 1 by up to 2^15, which
+// fp16 (and bf16) P and fp32 O and l hold.  If any query vector of the
+// workgroup sees a larger score (its running max passes m_ref + 15 in the
+// log2 domain), the split is computed again with the exact max as reference.
+// Either way the result is the same softmax; only rounding differs.
+constexpr float kRefMarginLog2 = 15.0f;
+
+template <int D, class E, Addr AM>
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_partial_kernel(AttnArgs a) {
+  using Gm = Geom<D>;
+  using vec8 = typename E::vec8;
+  constexpr int CH = Gm::CH;
+  constexpr int LPW = Gm::LPW;
+  constexpr int KS = D / 16;   // 16-wide d steps of QK
+  constexpr int DB = D / 32;   // 32-wide d blocks of O
+  constexpr bool PAGED = AM != Addr::Contig;
+  // Four separate arrays, each picked statically: the compiler can then see
+  // that a read of one buffer does not alias a direct-to-LDS load into another
+  // and does not make it wait for those loads (they complete a tile later).
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[Gm::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[Gm::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf0[Gm::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf1[Gm::TILE_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;
+
+  // Workgroup -> (split, KV head, m tile).  Consecutive workgroup ids go to
+  // different XCDs; remap so the workgroups one XCD holds are consecutive
+  // logical tiles, which share a KV head and split and so share L2.
+  int b = blockIdx.x;
+  if (a.xcd_remap) b = (b & 7) * (gridDim.x >> 3) + (b >> 3);
+  const int mt = b % a.tiles_m;
+  const int rest = b / a.tiles_m;
+  const int g = rest % a.n_kv_heads;
+  const int s = rest / a.n_kv_heads;
+
+  const int G = a.group;
+  const int nqv = a.rows * G;
+  const int f = mt * 128 + wave * 32 + (lane & 31);
+  const bool qv_valid = f < nqv;
+  const int row = qv_valid ? f / G : a.rows - 1;
+  const int head = g * G + (qv_valid ? f % G : 0);
+  const int f_last = min(mt * 128 + 127, nqv - 1);
+  const int r_first = (mt * 128) / G;
+  const int r_last = f_last / G;
+
+  const int k0 = s * a.split_tokens;
+  const int k1 = min(k0 + a.split_tokens, a.ctx);
+  const int kend = min(k1, (int)(a.history + r_last + 1));
+  const int n_tiles = kend > k0 ? (kend - k0 + kTK - 1) / kTK : 0;
+  const int lim = (int)a.history + row;             // last key this query vector sees
+  // Tiles ending at or before the first row's last key need no mask, and they
+  // are whole (split bounds are multiples of the tile).  A body works on tile
+  // it and loads tile it+1, so the fast body (no mask, no load clamp) runs
+  // while both are such tiles: it < n_fast.
+  const int mask_x = (int)a.history + r_first - k0 - (kTK - 1);
+  const int n_plain = min(n_tiles, mask_x < 0 ? 0 : mask_x / kTK + 1);
+  const int n_fast = n_plain > 0 ? n_plain - 1 : 0;
+
+  // Q fragments (B operand of QK): lane holds Q[f][16 ks + 8 h .. +7].
+  vec8 qf[KS];
+  {
+    const uint16_t* qp = a.q + ((int64_t)row * a.n_q_heads + head) * D + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 raw = qv_valid ? *(const u32x4*)(qp + 16 * ks) : u32x4{0u, 0u, 0u, 0u};
+      qf[ks] = __builtin_bit_cast(vec8, raw);
+    }
+  }
+  // Wait for Q here, on every path: otherwise the compiler's wait before the
+  // first use of Q inside the tile loop covers every load in flight, on every
+  // iteration.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  f32x16 o[DB];
+  float m_ref = kNegInf;  // softmax reference, scaled log2 domain
+  float m_true = kNegInf; // running max of the scaled scores
+  float l = 0.f;          // this lane's share of the softmax sum
+  const float c = a.scale_log2;
+
+  // ---- loader -------------------------------------------------------------
+  // Block b = wave * LPW + i of a tile holds rows 8 (b % 8) .. +7 and chunks
+  // 8 (b / 8) .. +7 (lds_off).
+  const int hkvd2 = a.n_kv_heads * D * 2;  // bytes per token (all KV heads)
+  const int ps_mask = (1 << a.log2_ps) - 1;
+  const int cg = (wave * LPW) >> 3;        // the wave's chunk group (same for all its blocks)
+  // Lane L fills unit L of a block: row 8 rg + L / 8, chunk 8 cg + ((L % 8) ^ g(row)),
+  // rg = the block's row group; g depends on rg only through its parity.
+  const int lrow = lane >> 3;
+  const int cpart_even = (cg * 8 + ((lane & 7) ^ lds_g(lrow))) << 4;
+  const int cpart_odd = (cg * 8 + ((lane & 7) ^ lds_g(8 + lrow))) << 4;
+  // Lane byte offsets within an 8-row group for whole tiles (tile to tile only
+  // the group's scalar base changes).
+  const uint32_t voff_even = lrow * hkvd2 + cpart_even;
+  const uint32_t voff_odd = lrow * hkvd2 + cpart_odd;
+  // Row group rg_i = (wave LPW + i) % 8 of load i starts soff[i] bytes into
+  // its page (paged, plus the tile's own offset in the page when pages are
+  // longer than a tile) or into the tile (contiguous).
+  int soff[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int rg = (wave * LPW + i) & 7;
+    soff[i] = (PAGED ? ((8 * rg) & ps_mask) : 8 * rg) * hkvd2;
+  }
+  const char* kg = (const char*)a.k + g * D * 2;
+  const char* vg = (const char*)a.v + g * D * 2;
+  const uint32_t page_bytes = (uint32_t)hkvd2 << a.log2_ps;
+  // Per lane: address of pool page `page` (of K or V).
+  auto page_addr = [&](int page, bool is_v) __attribute__((always_inline)) -> uint64_t {
+    return (uint64_t)(is_v ? vg : kg) + (uint64_t)(uint32_t)page * page_bytes;
+  };
+
+  // Pool page of key (tile j start + lane).  The key is clamped to kend-1, so
+  // the block-table read is always in range (lanes and tiles past the end read
+  // an entry nobody uses) and the load needs no branch.
+  auto pages = [&](int j) __attribute__((always_inline)) -> int {
+    if constexpr (!PAGED) return 0;
+    const int key = min(k0 + j * kTK + lane, kend - 1);
+    return a.bt[key >> a.log2_ps];
+  };
+
+  // Direct-to-LDS load i (of LPW) of tile j of K or V.  Keys at or past `kend`
+  // are read from key kend-1 instead: they are masked for every query of the
+  // workgroup (weight exactly 0) and a finite row keeps 0 * V finite, so there
+  // is no zero fill.  With r0c = min(8 rg, (kend-1-t0) & ~7) and
+  // lrow_c = min(lrow, kend-1-t0-r0c), whole tiles read their own rows and the
+  // last tile's rows past kend-1 read row kend-1 (same 8-row group, so the
+  // same page).  `page` holds the pool page of key (tile start + lane).
+  // WHOLE: the caller knows tile j lies below kend, so the clamp is skipped:
+  // the address is a scalar base (one lane read for the page) plus a
+  // loop-invariant lane offset.
+  // `paddr` = page_addr(page, is_v), used by the WHOLE paged form: the lane
+  // holding key t0 + 8 rg holds the page of row group rg (with Page16 so does
+  // the lane of key t0 + 16 (rg / 2), which lets two loads share one lookup).
+  auto issue_one = [&](int j, int page, uint64_t paddr, bool is_v, uint8_t* dst, int i, auto whole)
+                       __attribute__((always_inline)) {
+    constexpr bool WHOLE = decltype(whole)::value;
+    const int t0 = k0 + j * kTK;
+    const int last = kend - 1 - t0;
+    const char* src = is_v ? vg : kg;
+    const int b = wave * LPW + i;
+    const int cpart = (b & 1) ? cpart_odd : cpart_even;
+    if constexpr (WHOLE && AM != Addr::PageLane) {
+      const uint32_t voff = (b & 1) ? voff_odd : voff_even;
+      if constexpr (AM == Addr::Contig) {
+        load_lds16(src + (int64_t)t0 * hkvd2, voff, soff[i], dst + b * 1024);
+      } else {
+        const int rg = b & 7;
+        const int ln = AM == Addr::Page16 ? 16 * (rg >> 1) : 8 * rg;
+        const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)paddr, ln);
+        const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(paddr >> 32), ln);
+        load_lds16((const char*)(((uint64_t)hi << 32) | lo), voff, (t0 & ps_mask) * hkvd2 + soff[i],
+                   dst + b * 1024);
+      }
+    } else if constexpr (AM == Addr::PageLane) {
+      const int rr = min(8 * (b & 7) + lrow, last);
+      const int pg = __shfl(page, rr, 64);
+      const int64_t tok = ((int64_t)pg << a.log2_ps) + ((t0 + rr) & ps_mask);
+      __builtin_amdgcn_global_load_lds((const void*)(src + tok * hkvd2 + cpart), LDS_PTR(void, dst + b * 1024), 16, 0, 0);
+    } else {
+      const int r0c = __builtin_amdgcn_readfirstlane(min(8 * (b & 7), last & ~7));
+      const int lrow_c = min(lrow, last - r0c);
+      const char* base;
+      if constexpr (AM == Addr::Contig) {
+        base = src + (int64_t)(t0 + r0c) * hkvd2;
+      } else {
+        const int pg = __builtin_amdgcn_readlane(page, r0c);
+        base = src + (((int64_t)pg << a.log2_ps) + ((t0 + r0c) & ps_mask)) * hkvd2;
+      }
+      load_lds16(base, (uint32_t)(lrow_c * hkvd2 + cpart), 0, dst + b * 1024);
+    }
+  };
+  auto issue = [&](int j, int page, bool is_v, uint8_t* dst) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) issue_one(j, page, 0, is_v, dst, i, std::false_type{});
+  };
+
+  // ---- MFMA phases --------------------------------------------------------
+  // S^T[key][qv] = K Q^T for the 64 keys of a tile: lane holds qv = lane & 31
+  // and keys 32 kb + 8 (r / 4) + 4 h + r % 4.
+  f32x16 sc[2];
+  // lds_off(lane % 32 + 32 kb, 2 ks + h) = (kofs ^ (ks % 4) 32) + (ks / 4) 8192 + kb 4096
+  const int kofs = ((lane >> 3) & 3) * 1024 + (lane & 7) * 128 + ((h ^ lds_g(lane & 15)) << 4);
+  // The operand reads run QPF steps ahead of their MFMAs; sched_barrier pins
+  // that order (the compiler otherwise waits on each read right before its
+  // MFMA).
+  auto qk = [&](const uint8_t* kt, auto&& step_hook) __attribute__((always_inline)) {
+    constexpr int QPF = 3;
+    sc[0] = f32x16{};
+    sc[1] = f32x16{};
+    i16x8 k0r[KS], k1r[KS];
+    auto load = [&](int ks) __attribute__((always_inline)) {
+      const uint8_t* kl = kt + (kofs ^ ((ks & 3) << 5));
+      const int imm = (ks >> 2) * 8192;
+      k0r[ks] = *LDS_PTR(const i16x8, kl + imm);
+      k1r[ks] = *LDS_PTR(const i16x8, kl + imm + 4096);
+    };
+#pragma unroll
+    for (int ks = 0; ks < QPF && ks < KS; ++ks) load(ks);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + QPF < KS) load(ks + QPF);
+      sc[0] = E::mfma(__builtin_bit_cast(vec8, k0r[ks]), qf[ks], sc[0]);
+      sc[1] = E::mfma(__builtin_bit_cast(vec8, k1r[ks]), qf[ks], sc[1]);
+      step_hook(ks);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // PV of the previous tile fused with the row max and softmax of this one:
+  // O^T[d][qv] += V^T[d][key] P^T[key][qv] (16 keys per MFMA, V^T read from
+  // row-major V by two transposing reads per operand: the 16 lanes of a group
+  // read rows 16 kstep + 4 h + (lane % 16) / 4 (and + 8) at columns
+  // 32 db + 16 ((lane / 16) % 2) + 4 (lane % 4), each lane receiving one column
+  // over 4 rows), while the VALU computes the max, the weights exp2(s c - m)
+  // of this tile into pb_new and their sum.  Step i issues the V reads of
+  // step i + VPF, one MFMA and a slice of the VALU work; sched_barrier pins
+  // the interleave.  The two halves are independent: PV reads pb, softmax
+  // writes pb_new.
+  vec8 pb[4], pb_new[4];
+  // lds_off(16 kstep + vr (+ 8), 4 db + cc) + within = (vofs1 (vofs2) ^ (db % 2) 64)
+  // + (db / 2) 8192 + kstep 2048, vr = 4 h + (lane % 16) / 4, cc = 2 ((lane / 16) % 2) + (lane % 4) / 2
+  const int v_r = 4 * h + ((lane & 15) >> 2);
+  const int v_cc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int vofs1 = v_r * 128 + ((v_cc ^ lds_g(v_r)) << 4) + (lane & 1) * 8;
+  const int vofs2 = 1024 + v_r * 128 + ((v_cc ^ lds_g(v_r + 8)) << 4) + (lane & 1) * 8;
+  auto pv_softmax = [&](const uint8_t* vt, auto&& step_hook) __attribute__((always_inline)) {
+    constexpr int NPV = 4 * DB;
+    constexpr int VPF = 3;
+    constexpr int MAX_STEPS = NPV >= 16 ? 4 : 2;  // steps that carry the max reduction
+    i16x4 vlo[NPV], vhi[NPV];
+    auto load = [&](int i) __attribute__((always_inline)) {
+      const int kstep = i / DB, db = i % DB;
+      const int imm = (db >> 1) * 8192 + kstep * 2048;
+      vlo[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vt + (vofs1 ^ ((db & 1) << 6)) + imm));
+      vhi[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vt + (vofs2 ^ ((db & 1) << 6)) + imm));
+    };
+    // VALU work: max over the 32 scores (MAX_STEPS steps), then 32 weights.
+    float part[MAX_STEPS];
+    float base = 0.f, rs = 0.f, p32[32];
+    auto valu = [&](int i) __attribute__((always_inline)) {
+      if (i < MAX_STEPS) {
+        constexpr int PER = 32 / MAX_STEPS;
+        float mx = sc[(i * PER) >> 4][(i * PER) & 15];
+#pragma unroll
+        for (int e = 1; e < PER; ++e) mx = fmaxf(mx, sc[(i * PER + e) >> 4][(i * PER + e) & 15]);
+        part[i] = mx;
+        if (i == MAX_STEPS - 1) {
+          float m = part[0];
+#pragma unroll
+          for (int j = 1; j < MAX_STEPS; ++j) m = fmaxf(m, part[j]);
+          const float mxs = max_with_partner(m) * c;
+          m_true = fmaxf(m_true, mxs);
+          if (m_ref == kNegInf) m_ref = mxs;  // first tile with a visible key (O and l are still 0)
+          base = m_ref == kNegInf ? 0.f : m_ref;
+        }
+        return;
+      }
+      // weights of elements [e0, e1) of the 32 (kstep-major, 8 per pb entry)
+      const int n = NPV - MAX_STEPS;
+      const int e0 = ((i - MAX_STEPS) * 32) / n, e1 = ((i - MAX_STEPS + 1) * 32) / n;
+#pragma unroll
+      for (int e = e0; e < e1; ++e) {
+        p32[e] = __builtin_amdgcn_exp2f(fmaf(sc[e >> 4][e & 15], c, -base));
+        if ((e & 7) == 7) {
+          // The sum takes the rounded weights, the ones the PV product uses.
+          pb_new[e >> 3] = E::from_f32(p32 + (e & ~7));
+          rs = E::sum8(pb_new[e >> 3], rs);
+        }
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < VPF && i < NPV; ++i) load(i);
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      if (i + VPF < NPV) load(i + VPF);
+      const int kstep = i / DB, db = i % DB;
+      i16x8 av = __builtin_shufflevector(vlo[i], vhi[i], 0, 1, 2, 3, 4, 5, 6, 7);
+      o[db] = E::mfma(__builtin_bit_cast(vec8, av), pb[kstep], o[db]);
+      valu(i);
+      step_hook(i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l += rs;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) pb[k] = pb_new[k];
+  };
+
+  // PV of the last tile (no softmax left to overlap).
+  auto pv_last = [&](const uint8_t* vt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kstep = 0; kstep < 4; ++kstep)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int imm = (db >> 1) * 8192 + kstep * 2048;
+        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vt + (vofs1 ^ ((db & 1) << 6)) + imm));
+        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vt + (vofs2 ^ ((db & 1) << 6)) + imm));
+        i16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[db] = E::mfma(__builtin_bit_cast(vec8, av), pb[kstep], o[db]);
+      }
+  };
+
+  // ---- pipeline -----------------------------------------------------------
+  // Iteration it: QK of tile it, then the softmax of tile it interleaved with
+  // the PV of tile it-1 (independent of each other).  Loads run one tile
+  // ahead: K(it+1) and V(it) are issued at the start of iteration it.  The
+  // V buffer of "tile -1" is zeroed and pb starts at 0, so iteration 0 runs
+  // the same code (its PV adds exact zeros).
+  int pg0 = 0, pg1 = 0;  // pages of tiles it and it+1
+  // vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding:
+  // vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+  constexpr int kWaitVmcnt0 = 0x0F70;
+  // vmcnt(LPW) lgkmcnt(0): before the tile loop's barriers.
+  constexpr int kWaitVmcntLPW = 0x0070 | (LPW & 15) | ((LPW >> 4) << 14);
+  static_assert(LPW < 64, "vmcnt holds 6 bits");
+  auto body = [&](int it, auto masked, auto parity) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
+    constexpr bool ODD = decltype(parity)::value;  // it is odd
+    const int t0 = k0 + it * kTK;
+    // This wave's loads in flight, oldest first: K(it) (issued during the QK
+    // of it-1), V(it-1) (during the PV phase of it-1), LPW each.  Wait for
+    // K(it) only; after the barrier K(it) is in LDS and the buffers of K(it-1)
+    // and V(it-2) are free (every wave is done with body it-1).
+    __builtin_amdgcn_s_waitcnt(kWaitVmcntLPW);
+    lds_barrier();
+    // The loads of K(it+1) and V(it) are spread over the MFMA steps (one per
+    // few MFMAs) rather than issued in a burst, which would stall the waves on
+    // a full address queue before any math starts.
+    // On the last tile the K load of "tile n_tiles" reads row kend-1 (the
+    // clamp above) into a buffer nothing reads again; keeping it unconditional
+    // keeps this a straight-line block.
+    const int pk = pg1, pv = pg0;
+    pg0 = pg1;
+    pg1 = pages(it + 2);
+    const uint64_t pka = PAGED && !MASKED ? page_addr(pk, false) : 0;
+    const uint64_t pva = PAGED && !MASKED ? page_addr(pv, true) : 0;
+    qk(ODD ? kbuf1 : kbuf0, [&](int ks) {
+      constexpr int EVERY = KS / LPW;
+      if (ks % EVERY == 0)
+        issue_one(it + 1, pk, pka, false, ODD ? kbuf0 : kbuf1, ks / EVERY, std::bool_constant<!MASKED>{});
+    });
+    if constexpr (MASKED) {
+      const int rel = lim - t0;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+          sc[kb][r] = key > rel ? kNegInf : sc[kb][r];
+        }
+    }
+    // Now in flight: V(it-1), then K(it+1).  Wait for V(it-1), which the PV
+    // below reads, so that its load latency hides behind the QK phase.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcntLPW);
+    lds_barrier();
+    // PV(it-1) with the previous weights, fused with this tile's softmax.
+    pv_softmax(ODD ? vbuf0 : vbuf1, [&](int i) {
+      constexpr int EVERY = 4 * DB / LPW;
+      if (i % EVERY == 0)
+        issue_one(it, pv, pva, true, ODD ? vbuf1 : vbuf0, i / EVERY, std::bool_constant<!MASKED>{});
+    });
+  };
+  // Tiles in even/odd pairs so that each body has its buffers fixed at compile
+  // time and the output accumulators flow through one chain of code.
+  auto run = [&](int& it, int end, auto masked) __attribute__((always_inline)) {
+    if (it < end && (it & 1)) {
+      body(it, masked, std::true_type{});
+      ++it;
+    }
+    for (; it + 1 < end; it += 2) {
+      body(it, masked, std::false_type{});
+      body(it + 1, masked, std::true_type{});
+    }
+    if (it < end) {
+      body(it, masked, std::false_type{});
+      ++it;
+    }
+  };
+
+  __shared__ int wg_redo[kWaves];
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+#pragma unroll
+    for (int kstep = 0; kstep < 4; ++kstep) pb[kstep] = vec8{};
+    l = 0.f;
+    for (int i = tid; i < Gm::TILE_BYTES / 16; i += 256) *LDS_PTR(u32x4, vbuf1 + i * 16) = u32x4{0u, 0u, 0u, 0u};
+    if (n_tiles > 0) {
+      pg0 = pages(0);
+      issue(0, pg0, false, kbuf0);
+      pg1 = pages(1);
+      // K(0) is the only load in flight: the first body's vmcnt(LPW) would not wait for it.
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    }
+    int it = 0;
+    run(it, n_fast, std::false_type{});
+    run(it, n_tiles, std::true_type{});
+    if (n_tiles > 0) {
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+      if ((n_tiles - 1) & 1) pv_last(vbuf1);
+      else pv_last(vbuf0);
+    }
+    if (pass == 1) break;
+    // Did any query vector of the workgroup outgrow its reference?
+    const bool redo = __ballot(m_true > m_ref + kRefMarginLog2) != 0;
+    if (lane == 0) wg_redo[wave] = redo;
+    __syncthreads();
+    const bool any = wg_redo[0] | wg_redo[1] | wg_redo[2] | wg_redo[3];
+    __syncthreads();
+    if (!any) break;
+    m_ref = m_true;  // the exact max: every weight is at most 1 now
+  }
+
+  // Epilogue: combine the two lanes' sums; lane holds d = 32 db + 8 q + 4 h + 0..3.
+  const float l_tot = sum_with_partner(l);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (!qv_valid) return;
+  const int64_t pair = (int64_t)row * a.n_q_heads + head;
+  if (a.n_splits == 1) {
+    uint16_t* op = a.out + pair * D + 4 * h;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const uint32_t lo = E::bits(o[db][4 * q4 + 0] * inv) | ((uint32_t)E::bits(o[db][4 * q4 + 1] * inv) << 16);
+        const uint32_t hi = E::bits(o[db][4 * q4 + 2] * inv) | ((uint32_t)E::bits(o[db][4 * q4 + 3] * inv) << 16);
+        *(u32x2*)(op + 32 * db + 8 * q4) = u32x2{lo, hi};
+      }
+  } else {
+    const int64_t pairs = (int64_t)a.rows * a.n_q_heads;
+    float* wp = a.ws_o + ((int64_t)s * pairs + pair) * D + 4 * h;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        f32x4 v4 = {o[db][4 * q4 + 0] * inv, o[db][4 * q4 + 1] * inv, o[db][4 * q4 + 2] * inv,
+                    o[db][4 * q4 + 3] * inv};
+        *(f32x4*)(wp + 32 * db + 8 * q4) = v4;
+      }
+    if (h == 0) a.ws_lse[(int64_t)s * pairs + pair] = l_tot > 0.f ? m_ref + log2f(l_tot) : kNegInf;
+  }
+}
+
+// Log-sum-exp merge of split partials, one (row, head) pair per D/4 threads,
+// 4 output elements per thread, splits summed in index order.  Splits that
+// start past a row's last key hold nothing for it and are not read.
+
+template <int D, class E, Addr AM>
+hipError_t launch_attn_t(const AttnArgs& a, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((attn_partial_kernel<D, E, AM>), dim3(grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D, class E>
+hipError_t launch_attn_p(const AttnArgs& a, bool paged, int grid, hipStream_t stream) {
+  if (!paged) return launch_attn_t<D, E, Addr::Contig>(a, grid, stream);
+  if (a.log2_ps >= 4) return launch_attn_t<D, E, Addr::Page16>(a, grid, stream);
+  if (a.log2_ps == 3) return launch_attn_t<D, E, Addr::Page8>(a, grid, stream);
+  return launch_attn_t<D, E, Addr::PageLane>(a, grid, stream);
+}
+
+}  // namespace
+}  // namespace ppa

@@ -43,5 +43,9 @@ struct MergeArgs {
 hipError_t launch_attention(const AttnArgs& a, int head_dim, int dtype, bool paged, int grid,
                             hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int head_dim, int dtype, int grid, hipStream_t stream);
+// The per-head-dimension halves of launch_attention (separate translation units).
+hipError_t launch_attention_d64_d128(const AttnArgs& a, int head_dim, int dtype, bool paged, int grid,
+                                     hipStream_t stream);
+hipError_t launch_attention_d256(const AttnArgs& a, int dtype, bool paged, int grid, hipStream_t stream);
 
 }  // namespace ppa
