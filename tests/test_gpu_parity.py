@@ -59,6 +59,13 @@ ODD = [
     ("group16", 900, 19, 16, 1, 128, 16, 0, "scatter"),
     ("many_splits_short", 60, 70, 4, 4, 64, 16, 64, "permute"),
     ("rows_tail_d256", 2047, 129, 16, 2, 256, 16, 5, "permute"),
+    # one loader per page-size class and head dimension: 8-token pages,
+    # pages below 8 tokens, pages longer than a 64-key tile
+    ("ps8_d256", 1100, 90, 8, 2, 256, 8, 2, "scatter"),
+    ("ps8_d64", 900, 41, 4, 1, 64, 8, 0, "permute"),
+    ("ps4_d256", 700, 33, 8, 1, 256, 4, 0, "permute"),
+    ("ps2_d64", 400, 20, 8, 2, 64, 2, 0, "scatter"),
+    ("ps128_d128_hkv4", 1300, 50, 16, 4, 128, 128, 0, "scatter"),
 ]
 ODD_CASES = [o[:7] + (dt,) + o[7:] for o in ODD for dt in ("f16", "bf16")]
 
