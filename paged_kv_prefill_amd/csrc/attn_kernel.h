@@ -303,9 +303,39 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   const char* kg = (const char*)a.k + g * D * 2;
   const char* vg = (const char*)a.v + g * D * 2;
   const uint32_t page_bytes = (uint32_t)hkvd2 << a.log2_ps;
-  // Per lane: address of pool page `page` (of K or V).
-  auto page_addr = [&](int page, bool is_v) __attribute__((always_inline)) -> uint64_t {
-    return (uint64_t)(is_v ? vg : kg) + (uint64_t)(uint32_t)page * page_bytes;
+  // Scalar bases of one whole tile's loads for this wave: the tile start
+  // (contiguous) or the page of each 8-row group the wave loads (paged; with
+  // Page16 two neighbouring groups share a page, so load i uses base i / 2).
+  // They are read once per tile, right after the tile loop's barrier, from
+  // the per-lane page addresses: the lane holding key t0 + 8 rg holds the
+  // page of row group rg, and the wave's first group is (wave LPW) % 8
+  // (even, so group pairs line up with base pairs).
+  constexpr int NBASE = AM == Addr::Page16 ? (LPW + 1) / 2 : AM == Addr::Page8 ? LPW : 1;
+  struct TileBases {
+    const char* base[NBASE];
+    int within;  // byte offset of the tile in its page (pages longer than a tile)
+  };
+  const int lane_base = 8 * ((wave * LPW) & 7);
+  auto tile_bases = [&](int j, int page, bool is_v) __attribute__((always_inline)) -> TileBases {
+    TileBases tb;
+    const int t0 = k0 + j * kTK;
+    const char* src = is_v ? vg : kg;
+    if constexpr (AM == Addr::Contig) {
+      tb.base[0] = src + (int64_t)t0 * hkvd2;
+      tb.within = 0;
+    } else {
+      // per lane: address of pool page `page`
+      const uint64_t paddr = (uint64_t)src + (uint64_t)(uint32_t)page * page_bytes;
+#pragma unroll
+      for (int q = 0; q < NBASE; ++q) {
+        const int ln = lane_base + (AM == Addr::Page16 ? 16 : 8) * q;
+        const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)paddr, ln);
+        const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(paddr >> 32), ln);
+        tb.base[q] = (const char*)(((uint64_t)hi << 32) | lo);
+      }
+      tb.within = (t0 & ps_mask) * hkvd2;
+    }
+    return tb;
   };
 
   // Pool page of key (tile j start + lane).  The key is clamped to kend-1, so
@@ -327,10 +357,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   // WHOLE: the caller knows tile j lies below kend, so the clamp is skipped:
   // the address is a scalar base (one lane read for the page) plus a
   // loop-invariant lane offset.
-  // `paddr` = page_addr(page, is_v), used by the WHOLE paged form: the lane
-  // holding key t0 + 8 rg holds the page of row group rg (with Page16 so does
-  // the lane of key t0 + 16 (rg / 2), which lets two loads share one lookup).
-  auto issue_one = [&](int j, int page, uint64_t paddr, bool is_v, uint8_t* dst, int i, auto whole)
+  // `tb` = tile_bases(j, page, is_v), used by the WHOLE form.
+  auto issue_one = [&](int j, int page, const TileBases& tb, bool is_v, uint8_t* dst, int i, auto whole)
                        __attribute__((always_inline)) {
     constexpr bool WHOLE = decltype(whole)::value;
     const int t0 = k0 + j * kTK;
@@ -340,16 +368,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const int cpart = (b & 1) ? cpart_odd : cpart_even;
     if constexpr (WHOLE && AM != Addr::PageLane) {
       const uint32_t voff = (b & 1) ? voff_odd : voff_even;
-      if constexpr (AM == Addr::Contig) {
-        load_lds16(src + (int64_t)t0 * hkvd2, voff, soff[i], dst + b * 1024);
-      } else {
-        const int rg = b & 7;
-        const int ln = AM == Addr::Page16 ? 16 * (rg >> 1) : 8 * rg;
-        const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)paddr, ln);
-        const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(paddr >> 32), ln);
-        load_lds16((const char*)(((uint64_t)hi << 32) | lo), voff, (t0 & ps_mask) * hkvd2 + soff[i],
-                   dst + b * 1024);
-      }
+      const int q = AM == Addr::Page16 ? i / 2 : AM == Addr::Page8 ? i : 0;
+      load_lds16(tb.base[q], voff, tb.within + soff[i], dst + b * 1024);
     } else if constexpr (AM == Addr::PageLane) {
       const int rr = min(8 * (b & 7) + lrow, last);
       const int pg = __shfl(page, rr, 64);
@@ -370,7 +390,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   };
   auto issue = [&](int j, int page, bool is_v, uint8_t* dst) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) issue_one(j, page, 0, is_v, dst, i, std::false_type{});
+    for (int i = 0; i < LPW; ++i) issue_one(j, page, TileBases{}, is_v, dst, i, std::false_type{});
   };
 
   // ---- MFMA phases --------------------------------------------------------
@@ -530,12 +550,15 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const int pk = pg1, pv = pg0;
     pg0 = pg1;
     pg1 = pages(it + 2);
-    const uint64_t pka = PAGED && !MASKED ? page_addr(pk, false) : 0;
-    const uint64_t pva = PAGED && !MASKED ? page_addr(pv, true) : 0;
+    TileBases kb{}, vb{};
+    if constexpr (!MASKED) {
+      kb = tile_bases(it + 1, pk, false);
+      vb = tile_bases(it, pv, true);
+    }
     qk(ODD ? kbuf1 : kbuf0, [&](int ks) {
       constexpr int EVERY = KS / LPW;
       if (ks % EVERY == 0)
-        issue_one(it + 1, pk, pka, false, ODD ? kbuf0 : kbuf1, ks / EVERY, std::bool_constant<!MASKED>{});
+        issue_one(it + 1, pk, kb, false, ODD ? kbuf0 : kbuf1, ks / EVERY, std::bool_constant<!MASKED>{});
     });
     if constexpr (MASKED) {
       const int rel = lim - t0;
@@ -555,7 +578,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     pv_softmax(ODD ? vbuf0 : vbuf1, [&](int i) {
       constexpr int EVERY = 4 * DB / LPW;
       if (i % EVERY == 0)
-        issue_one(it, pv, pva, true, ODD ? vbuf1 : vbuf0, i / EVERY, std::bool_constant<!MASKED>{});
+        issue_one(it, pv, vb, true, ODD ? vbuf1 : vbuf0, i / EVERY, std::bool_constant<!MASKED>{});
     });
   };
   // Tiles in even/odd pairs so that each body has its buffers fixed at compile
