@@ -61,7 +61,7 @@ def traffic(fetch_csv, write_csv, out_json, kernel_sub, copy_bytes, fetch_cmd, w
         raise SystemExit("no calibration copy found")
     fetch_scale = copy_kib / (sum(cf) / len(cf))
     write_scale = copy_kib / (sum(cw) / len(cw))
-    names = [n for n in fetch if kernel_sub in n]
+    names = [n for n in fetch if kernel_sub in short(n, 1 << 30)]
     if len(names) != 1:
         raise SystemExit(f"kernel match for {kernel_sub!r}: {names}")
     name = names[0]
