@@ -10,9 +10,13 @@ issue's long prefill):
     pages scattered over a 65,536-page pool.
 Inputs are resident in HBM before the timed region.  The contiguous-KV path
 runs on the same values right after each paged chunk (A/B), outside the
-step's value.  Prints one JSON line.
+step's value.  Also outside it (skip with --no-extra): per-chunk medians with
+a cold cache (a 512 MB scratch write before each call, more than the 256 MB
+Infinity Cache plus the 8 x 4 MB L2), the paged/contiguous ratio of the
+2048-row chunk at 1K-16K history, and a split-count sweep at 32K against the
+planner.  Prints one JSON line.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--copy-calibration]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-ab] [--no-extra] [--copy-calibration]
 """
 
 import argparse
@@ -37,6 +41,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-ab", action="store_true", help="skip the contiguous-KV A/B")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the cold-cache, short-history and split-count measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (known bytes) for counter scaling")
     ap.add_argument("--chunks", default=",".join(CHUNKS))
@@ -91,6 +97,97 @@ def cpu_baseline(case):
             "sample": f"{len(rows)} of {case.rows} rows (evenly spaced) of the 32K-history chunk, "
                       f"{dt:.1f} s, numpy float64 with BLAS on {threads} threads",
             "seconds": dt}
+
+
+def kv_bytes(case):
+    """Algorithmic K+V bytes of one chunk: every key read once."""
+    return (case.history + case.rows) * case.n_kv_heads * case.head_dim * 2 * 2
+
+
+def timed(fn, reps, stream, before=None):
+    """Median, p10, p90 ms of fn() over reps calls, each bracketed by events on
+    `stream`; `before` (if given) runs before each call, outside the events."""
+    import numpy as np
+    import torch
+    evs = []
+    for _ in range(reps):
+        if before is not None:
+            before()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    return float(np.median(ms)), float(np.percentile(ms, 10)), float(np.percentile(ms, 90))
+
+
+def timed_pair(fa, fb, reps, stream):
+    """Medians of fa() and fb() called alternately (so clock drift hits both)."""
+    import numpy as np
+    import torch
+    evs = []
+    for _ in range(reps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record(stream)
+        fa()
+        e[1].record(stream)
+        e[2].record(stream)
+        fb()
+        e[3].record(stream)
+        evs.append(e)
+    torch.cuda.synchronize()
+    return (float(np.median([e[0].elapsed_time(e[1]) for e in evs])),
+            float(np.median([e[2].elapsed_time(e[3]) for e in evs])))
+
+
+def extra_measurements(chunks, paged, contig, pkg, synth, to_dev, stream, reps=10):
+    """Cold-cache medians, the short-history sweep and the split sweep."""
+    import torch
+    out = {}
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=stream.device)   # 512 MB
+
+    def flush():
+        scratch.fill_(1)
+
+    out["cold_cache_ms_median"] = {c["name"]: round(timed(lambda: paged(c), reps, stream, flush)[0], 4)
+                                   for c in chunks}
+    del scratch
+    sweep = {}
+    for h in (1024, 2048, 4096, 8192, 16384):
+        case = synth.config_case(f"sweep_{h}")
+        dt = torch.float16 if case.dtype == "f16" else torch.bfloat16
+        q, kp, vp = to_dev(case.q, dt), to_dev(case.k_pages, dt), to_dev(case.v_pages, dt)
+        bt = torch.from_numpy(case.block_table).to(stream.device)
+        k, v = to_dev(case.k_contig, dt), to_dev(case.v_contig, dt)
+        o, oc = torch.empty_like(q), torch.empty_like(q)
+        fp = lambda: pkg.paged_prefill_attention(q, kp, vp, bt, case.history, out=o, stream=stream)
+        fc = lambda: pkg.contiguous_prefill_attention(q, k, v, case.history, out=oc, stream=stream)
+        for _ in range(3):
+            fp()
+            fc()
+        mp, mc = timed_pair(fp, fc, 2 * reps, stream)
+        fl = synth.exact_flops(case.history, case.rows, case.n_q_heads, case.head_dim)
+        sweep[f"{h // 1024}K"] = {"ms_median": round(mp, 4), "tflops": round(fl / (mp * 1e-3) / 1e12, 1),
+                                  "contiguous_ms_median": round(mc, 4), "paged_over_contiguous": round(mp / mc, 4),
+                                  "bitwise_equal_to_contiguous": bool(torch.equal(o.view(torch.int16),
+                                                                                  oc.view(torch.int16)))}
+        del q, kp, vp, bt, k, v, o, oc
+    out["history_sweep_2048_rows"] = sweep
+    c = next((c for c in chunks if c["name"] == "sweep_32768"), None)
+    if c is not None:
+        cs = c["case"]
+        res = {}
+        for s in (1, 2, 4, 8, 16, 32):
+            f = lambda: pkg.paged_prefill_attention(c["q"], c["kp"], c["vp"], c["bt"], cs.history, n_splits=s,
+                                                    out=c["out"], stream=stream)
+            f()
+            res[str(s)] = round(timed(f, reps, stream)[0], 4)
+        out["split_sweep_32k_ms_median"] = res
+        out["split_sweep_planner_splits"] = pkg.paged_prefill_plan(cs.history, cs.rows, cs.n_q_heads,
+                                                                   cs.n_kv_heads, cs.head_dim)["n_splits"]
+    return out
 
 
 def main():
@@ -174,6 +271,7 @@ def main():
         rec = {"ms_median": float(np.median(ms)), "ms_p10": float(np.percentile(ms, 10)),
                "ms_p90": float(np.percentile(ms, 90)),
                "tflops": c["flops"] / (np.median(ms) * 1e-3) / 1e12,
+               "kv_stream_gbs": kv_bytes(c["case"]) / (np.median(ms) * 1e-3) / 1e9,
                "history": c["case"].history, "piece_rows": c["case"].piece_rows or c["case"].rows,
                "heads": f"{c['case'].n_q_heads}/{c['case'].n_kv_heads}", "head_dim": c["case"].head_dim,
                "dtype": c["case"].dtype,
@@ -219,6 +317,10 @@ def main():
                    "chunks": per_chunk, "wall_s": round(wall, 3)},
         "roofline": roofline,
     }
+
+    if not args.no_extra:
+        print("# extra measurements", file=sys.stderr, flush=True)
+        line["config"]["extra"] = extra_measurements(chunks, paged, contig, pkg, synth, to_dev, stream)
 
     if args.copy_calibration:
         src = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
