@@ -182,13 +182,14 @@ __device__ __forceinline__ float sum_with_partner(float x) {
 }
 
 // How K/V rows are addressed.  Contig: [ctx][Hkv][d].  Paged: pages of
-// `page_size` tokens, each [page_size][Hkv][d].  Page16: pages of 16 tokens or
-// more, so the 16 rows of two neighbouring 8-row groups share a page; Page8:
-// pages of 8 tokens, one page per 8-row group.  Either way the 8 rows one
+// `page_size` tokens, each [page_size][Hkv][d].  PageBig: pages of 64 tokens or
+// more, so a 64-key tile lies in one page.  Page16: pages of 16 or 32 tokens,
+// so the 16 rows of two neighbouring 8-row groups share a page.  Page8: pages
+// of 8 tokens, one page per 8-row group.  In these classes the 8 rows one
 // direct-to-LDS load covers lie in one page, the page is wave-uniform, and an
 // address is a scalar base plus a per-lane offset that does not change from
 // tile to tile.  PageLane: smaller pages; every row looks up its own page.
-enum class Addr { Contig, Page16, Page8, PageLane };
+enum class Addr { Contig, PageBig, Page16, Page8, PageLane };
 
 // The softmax weights are exp2(s c - m_ref) with a fixed reference m_ref per
 // query vector instead of a running max, so the output accumulators are never
@@ -291,29 +292,29 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   // the group's scalar base changes).
   const uint32_t voff_even = lrow * hkvd2 + cpart_even;
   const uint32_t voff_odd = lrow * hkvd2 + cpart_odd;
-  // Row group rg_i = (wave LPW + i) % 8 of load i starts soff[i] bytes into
-  // its page (paged, plus the tile's own offset in the page when pages are
-  // longer than a tile) or into the tile (contiguous).
+  // Row group rg_i = (wave LPW + i) % 8 of load i starts soff[i] bytes past
+  // its base: into the tile (contiguous, PageBig) or into its page.
   int soff[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     const int rg = (wave * LPW + i) & 7;
-    soff[i] = (PAGED ? ((8 * rg) & ps_mask) : 8 * rg) * hkvd2;
+    soff[i] = (AM == Addr::Page16 || AM == Addr::Page8 ? ((8 * rg) & ps_mask) : 8 * rg) * hkvd2;
   }
   const char* kg = (const char*)a.k + g * D * 2;
   const char* vg = (const char*)a.v + g * D * 2;
   const uint32_t page_bytes = (uint32_t)hkvd2 << a.log2_ps;
   // Scalar bases of one whole tile's loads for this wave: the tile start
-  // (contiguous) or the page of each 8-row group the wave loads (paged; with
-  // Page16 two neighbouring groups share a page, so load i uses base i / 2).
-  // They are read once per tile, right after the tile loop's barrier, from
-  // the per-lane page addresses: the lane holding key t0 + 8 rg holds the
-  // page of row group rg, and the wave's first group is (wave LPW) % 8
-  // (even, so group pairs line up with base pairs).
+  // (contiguous; with PageBig the tile's place in its page) or the page of
+  // each 8-row group the wave loads (Page16: two neighbouring groups share a
+  // page, so load i uses base i / 2; Page8: base i).  They are read once per
+  // tile, right after the tile loop's barrier, from the per-lane page
+  // addresses: the lane holding key t0 + 8 rg holds the page of row group rg,
+  // and the wave's first group is (wave LPW) % 8 (even, so group pairs line up
+  // with base pairs).  Load i then adds soff[i]; with pages of at most 32
+  // tokens a tile starts on a page boundary, so soff[i] is the whole offset.
   constexpr int NBASE = AM == Addr::Page16 ? (LPW + 1) / 2 : AM == Addr::Page8 ? LPW : 1;
   struct TileBases {
     const char* base[NBASE];
-    int within;  // byte offset of the tile in its page (pages longer than a tile)
   };
   const int lane_base = 8 * ((wave * LPW) & 7);
   auto tile_bases = [&](int j, int page, bool is_v) __attribute__((always_inline)) -> TileBases {
@@ -322,7 +323,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const char* src = is_v ? vg : kg;
     if constexpr (AM == Addr::Contig) {
       tb.base[0] = src + (int64_t)t0 * hkvd2;
-      tb.within = 0;
+    } else if constexpr (AM == Addr::PageBig) {
+      // lane 0 holds key t0's page, which holds the whole tile
+      const uint64_t paddr = (uint64_t)src + (uint64_t)(uint32_t)page * page_bytes;
+      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)paddr, 0);
+      const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(paddr >> 32), 0);
+      tb.base[0] = (const char*)(((uint64_t)hi << 32) | lo) + (t0 & ps_mask) * hkvd2;
     } else {
       // per lane: address of pool page `page`
       const uint64_t paddr = (uint64_t)src + (uint64_t)(uint32_t)page * page_bytes;
@@ -333,7 +339,6 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(paddr >> 32), ln);
         tb.base[q] = (const char*)(((uint64_t)hi << 32) | lo);
       }
-      tb.within = (t0 & ps_mask) * hkvd2;
     }
     return tb;
   };
@@ -369,7 +374,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     if constexpr (WHOLE && AM != Addr::PageLane) {
       const uint32_t voff = (b & 1) ? voff_odd : voff_even;
       const int q = AM == Addr::Page16 ? i / 2 : AM == Addr::Page8 ? i : 0;
-      load_lds16(tb.base[q], voff, tb.within + soff[i], dst + b * 1024);
+      load_lds16(tb.base[q], voff, soff[i], dst + b * 1024);
     } else if constexpr (AM == Addr::PageLane) {
       const int rr = min(8 * (b & 7) + lrow, last);
       const int pg = __shfl(page, rr, 64);
@@ -444,7 +449,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   const int vofs2 = 1024 + v_r * 128 + ((v_cc ^ lds_g(v_r + 8)) << 4) + (lane & 1) * 8;
   auto pv_softmax = [&](const uint8_t* vt, auto&& step_hook) __attribute__((always_inline)) {
     constexpr int NPV = 4 * DB;
-    constexpr int VPF = 3;
+    constexpr int VPF = D >= 256 ? 2 : 3;
     constexpr int MAX_STEPS = NPV >= 16 ? 4 : 2;  // steps that carry the max reduction
     i16x4 vlo[NPV], vhi[NPV];
     auto load = [&](int i) __attribute__((always_inline)) {
@@ -676,6 +681,7 @@ hipError_t launch_attn_t(const AttnArgs& a, int grid, hipStream_t stream) {
 template <int D, class E>
 hipError_t launch_attn_p(const AttnArgs& a, bool paged, int grid, hipStream_t stream) {
   if (!paged) return launch_attn_t<D, E, Addr::Contig>(a, grid, stream);
+  if (a.log2_ps >= 6) return launch_attn_t<D, E, Addr::PageBig>(a, grid, stream);
   if (a.log2_ps >= 4) return launch_attn_t<D, E, Addr::Page16>(a, grid, stream);
   if (a.log2_ps == 3) return launch_attn_t<D, E, Addr::Page8>(a, grid, stream);
   return launch_attn_t<D, E, Addr::PageLane>(a, grid, stream);
