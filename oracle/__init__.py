@@ -16,6 +16,9 @@ It computes, in float64 with numpy, exactly what the pages define:
   Apple7/8", "What changed" and "Testing": the reduce sums S partials).
 * ``rules``: the page's split-count rule and piece-size rule, transcribed from
   the same PR ("What changed" and the explanatory note below "Testing").
+* ``kv_append``: the chunk's K/V rows written into their pages through the
+  block table (the issue's publishing of completed KV pages, after its
+  "Expected vs actual" table).
 
 Every function is pinned by ``tests/test_oracle_pins.py`` against brute force,
 closed forms, torch's CPU attention with an explicit mask, invariants, and the
@@ -35,3 +38,4 @@ from .attention import (  # noqa: F401
     causal_attention_rows,
 )
 from .rules import page_split_rule, page_piece_rows  # noqa: F401
+from .cache import kv_append  # noqa: F401

@@ -346,6 +346,90 @@ def pin_page_piece_rows(rules):
         assert rules.page_piece_rows(history) == piece, history
 
 
+# ---------------------------------------------------------------- KV append
+def _append_case(rng, history, rows, hkv, d, ps, extra_pool=3):
+    """A pool holding H tokens through a permuted table, every other slot
+    poisoned with NaN, and R new rows to append."""
+    ctx = history + rows
+    n_pages = max(1, -(-ctx // ps))
+    pool = n_pages + extra_pool
+    bt = rng.permutation(pool)[:n_pages].astype(np.int32)
+    kp = np.full((pool, ps, hkv, d), np.nan)
+    vp = np.full((pool, ps, hkv, d), np.nan)
+    k_hist = rng.standard_normal((history, hkv, d))
+    v_hist = rng.standard_normal((history, hkv, d))
+    for j in range(history):
+        kp[bt[j // ps], j % ps] = k_hist[j]
+        vp[bt[j // ps], j % ps] = v_hist[j]
+    k_new = rng.standard_normal((rows, hkv, d))
+    v_new = rng.standard_normal((rows, hkv, d))
+    return kp, vp, bt, k_hist, v_hist, k_new, v_new
+
+
+APPEND_SHAPES = [
+    # history, rows, Hkv, d, ps: page-aligned and not, one-token pages, a chunk inside one page
+    (0, 5, 1, 4, 2), (3, 6, 2, 3, 4), (8, 8, 1, 2, 4), (5, 1, 3, 2, 1), (2, 3, 2, 4, 16), (17, 30, 2, 5, 8),
+]
+
+
+def pin_append_gather(orc):
+    """After the append, reading the cache back through the block table (the
+    gather, pinned above) gives the old history followed by the new rows, and
+    every pool slot outside positions 0 .. H+R-1 keeps its old bits."""
+    import oracle as real
+    rng = np.random.default_rng(21)
+    for history, rows, hkv, d, ps in APPEND_SHAPES:
+        kp, vp, bt, k_hist, v_hist, k_new, v_new = _append_case(rng, history, rows, hkv, d, ps)
+        k_out, v_out = orc.kv_append(kp, vp, bt, history, ps, k_new, v_new)
+        ctx = history + rows
+        assert np.array_equal(real.gather_pages(k_out, bt, ctx, ps), np.concatenate([k_hist, k_new]))
+        assert np.array_equal(real.gather_pages(v_out, bt, ctx, ps), np.concatenate([v_hist, v_new]))
+        touched = np.zeros(kp.shape[:2], dtype=bool)
+        for j in range(ctx):
+            touched[bt[j // ps], j % ps] = True
+        assert np.array_equal(k_out[~touched], kp[~touched], equal_nan=True)
+        assert np.array_equal(v_out[~touched], vp[~touched], equal_nan=True)
+        # the inputs are not modified: the new rows' slots still hold NaN there
+        for i in range(rows):
+            pos = history + i
+            assert np.isnan(kp[bt[pos // ps], pos % ps]).all() and np.isnan(vp[bt[pos // ps], pos % ps]).all()
+
+
+def pin_append_pieces(orc):
+    """Appending R1 rows and then R2 rows at H + R1 equals appending R1 + R2
+    rows at once; appending nothing changes nothing."""
+    rng = np.random.default_rng(22)
+    kp, vp, bt, _, _, k_new, v_new = _append_case(rng, 7, 12, 2, 3, 4)
+    k1, v1 = orc.kv_append(kp, vp, bt, 7, 4, k_new, v_new)
+    k2, v2 = orc.kv_append(kp, vp, bt, 7, 4, k_new[:5], v_new[:5])
+    k2, v2 = orc.kv_append(k2, v2, bt, 12, 4, k_new[5:], v_new[5:])
+    assert np.array_equal(k1, k2, equal_nan=True) and np.array_equal(v1, v2, equal_nan=True)
+    k0, v0 = orc.kv_append(kp, vp, bt, 7, 4, k_new[:0], v_new[:0])
+    assert np.array_equal(k0, kp, equal_nan=True) and np.array_equal(v0, vp, equal_nan=True)
+
+
+def pin_append_contiguous(orc):
+    """With an identity table the pool is the contiguous layout: rows H ..
+    H+R-1 of its [tokens][Hkv][d] view are the new rows, bit for bit (16-bit
+    patterns, NaN payloads and -0 included)."""
+    rng = np.random.default_rng(23)
+    ps, hkv, d, history, rows = 4, 2, 3, 6, 9
+    n_pages = -(-(history + rows) // ps)
+    kp = rng.integers(0, 1 << 16, size=(n_pages, ps, hkv, d), dtype=np.uint16)
+    vp = rng.integers(0, 1 << 16, size=(n_pages, ps, hkv, d), dtype=np.uint16)
+    k_new = rng.integers(0, 1 << 16, size=(rows, hkv, d), dtype=np.uint16)
+    k_new[0, 0, :] = [0x7E01, 0x8000, 0xFC00]
+    v_new = rng.integers(0, 1 << 16, size=(rows, hkv, d), dtype=np.uint16)
+    bt = np.arange(n_pages, dtype=np.int32)
+    k_out, v_out = orc.kv_append(kp, vp, bt, history, ps, k_new, v_new)
+    kc, vc = k_out.reshape(-1, hkv, d), v_out.reshape(-1, hkv, d)
+    assert np.array_equal(kc[history:history + rows], k_new) and np.array_equal(vc[history:history + rows], v_new)
+    assert np.array_equal(kc[:history], kp.reshape(-1, hkv, d)[:history])
+    assert np.array_equal(vc[history + rows:], vp.reshape(-1, hkv, d)[history + rows:])
+
+
+CACHE_PINS = [pin_append_gather, pin_append_pieces, pin_append_contiguous]
+
 ATTENTION_PINS = [
     pin_decoders, pin_gather, pin_brute_force, pin_closed_forms, pin_weights, pin_torch_sdpa,
     pin_layout_invariance, pin_split_invariance, pin_split_partials, pin_piece_invariance,

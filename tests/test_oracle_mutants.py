@@ -66,6 +66,18 @@ RULE_MUTANTS = [
 ]
 
 
+CACHE_MUTANTS = [
+    ("history ignored", "pos = history_len + i", "pos = i"),
+    ("one position late", "pos = history_len + i", "pos = history_len + i + 1"),
+    ("block table ignored", "pool_page = block_table[pos // page_size]", "pool_page = pos // page_size"),
+    ("page and slot swapped", "pool_page = block_table[pos // page_size]", "pool_page = block_table[pos % page_size]"),
+    ("slot from the page index", "slot = pos % page_size", "slot = (pos // page_size) % page_size"),
+    ("V written into K", "k_out[pool_page, slot] = k_new[i]", "k_out[pool_page, slot] = v_new[i]"),
+    ("input pool modified in place", "k_out = np.array(k_pages, copy=True)", "k_out = k_pages"),
+    ("last row dropped", "for i in range(k_new.shape[0]):", "for i in range(k_new.shape[0] - 1):"),
+]
+
+
 def _mutated_module(filename, old, new):
     with open(os.path.join(ORACLE_DIR, filename)) as f:
         src = f.read()
@@ -100,3 +112,9 @@ def test_unmutated_copy_passes_every_pin():
     mod = _mutated_module("attention.py", "import math", "import math")
     for pin in _pins.ATTENTION_PINS:
         pin(mod)
+
+
+@pytest.mark.parametrize("label,old,new", CACHE_MUTANTS, ids=[m[0] for m in CACHE_MUTANTS])
+def test_cache_mutant_is_caught(label, old, new):
+    mod = _mutated_module("cache.py", old, new)
+    assert _caught(mod, _pins.CACHE_PINS), f"no pin caught: {label}"

@@ -16,3 +16,8 @@ def test_attention_pin(pin):
 @pytest.mark.parametrize("pin", _pins.RULE_PINS, ids=lambda f: f.__name__)
 def test_rule_pin(pin):
     pin(rules)
+
+
+@pytest.mark.parametrize("pin", _pins.CACHE_PINS, ids=lambda f: f.__name__)
+def test_cache_pin(pin):
+    pin(oracle)
