@@ -172,6 +172,26 @@ int32_t paged_prefill_piece_rows(int64_t history_len, int32_t chunk_rows, int64_
 int paged_prefill_check_block_table(const int32_t* block_table_host, int64_t n_entries,
                                     int64_t n_pool_pages);
 
+/*
+ * KV append: write a chunk's K and V rows into their pages (the issue's
+ * publishing of completed KV pages, after its "Expected vs actual" table;
+ * run it before the chunk's attention, whose keys include the chunk's own).
+ * Row i of k_new/v_new [rows][Hkv][d] is the token at position
+ * history_len + i and goes to slot (history_len + i) % page_size of pool page
+ * block_table[(history_len + i) / page_size] of k_pages/v_pages
+ * [n_pool_pages][page_size][Hkv][d].  Nothing else in the pools changes; the
+ * bits are copied unchanged (dtype only selects the 2-byte element type and
+ * is checked like the attention's).  The block table must cover positions
+ * 0 .. history_len + rows - 1.  rows == 0 is a no-op.  Errors as for the
+ * attention: PPA_ERR_ALIAS when a new-rows pointer equals a pool pointer or
+ * K and V share a pool; partial overlaps cannot be checked (the pool size is
+ * not an argument).  Asynchronous on `stream`; no workspace.
+ */
+int paged_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                    const int32_t* block_table, int64_t history_len, int32_t rows,
+                    int32_t n_kv_heads, int32_t head_dim, int32_t page_size, int32_t dtype,
+                    ppa_stream_t stream);
+
 /* Frees every split workspace; call only when no stream still uses one. */
 int paged_prefill_release_workspaces(void);
 

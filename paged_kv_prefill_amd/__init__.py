@@ -59,6 +59,7 @@ _SIGNATURES = {
     "paged_prefill_release_workspaces": (_I32, []),
     "paged_prefill_strerror": (ctypes.c_char_p, [_I32]),
     "paged_prefill_version": (_I32, []),
+    "paged_kv_append": (_I32, [_VP, _VP, _VP, _VP, _VP, _I64, _I32, _I32, _I32, _I32, _I32, _VP]),
 }
 
 
@@ -158,6 +159,23 @@ def contiguous_prefill_attention(q, k, v, history_len, n_splits=0, out=None, pie
         rc = lib().contiguous_prefill_attention(_ptr(q), _ptr(k), _ptr(v), *args, *tail)
         _check(rc, "contiguous_prefill_attention")
     return out
+
+
+def paged_kv_append(k_new, v_new, k_pages, v_pages, block_table, history_len, stream=None):
+    """Write k_new/v_new [R][Hkv][d] (tokens at positions history_len ..
+    history_len+R-1) into their slots of k_pages/v_pages
+    [pool][page_size][Hkv][d] through block_table (int32), in place."""
+    _need_cuda(k_new, v_new, k_pages, v_pages, block_table)
+    rows, n_kv_heads, head_dim = k_new.shape
+    _, page_size, pkv, pd = k_pages.shape
+    if (pkv, pd) != (n_kv_heads, head_dim) or tuple(v_pages.shape) != tuple(k_pages.shape) \
+            or tuple(v_new.shape) != tuple(k_new.shape) or k_new.dtype != k_pages.dtype:
+        raise ValueError("k_new/v_new/k_pages/v_pages shapes or dtypes do not match")
+    rc = lib().paged_kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+                               int(history_len), int(rows), int(n_kv_heads), int(head_dim), int(page_size),
+                               _dtype_code(k_new), _stream_handle(stream, k_new.device))
+    _check(rc, "paged_kv_append")
+    return k_pages, v_pages
 
 
 def paged_prefill_plan(history_len, chunk_rows, n_q_heads, n_kv_heads, head_dim, page_size=16, n_splits=0):

@@ -32,6 +32,7 @@ KERNEL_SOURCES = (
     ("attention.hip", "0"),
     ("attention_d64_d128.hip", os.environ.get("PPA_MFMA_VGPR_FORM", "1")),
     ("attention_d256.hip", os.environ.get("PPA_MFMA_VGPR_FORM", "1")),
+    ("kv_append.hip", "0"),
 )
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}"]
 

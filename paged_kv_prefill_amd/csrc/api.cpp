@@ -1,6 +1,7 @@
 // C ABI entry points: argument checks, planning, the split workspace and the
-// kernel launches.  Every step of the computation runs in the HIP kernels of
-// attention.hip; this file only validates, plans and enqueues.
+// kernel launches.  Every step of the computation runs in the HIP kernels
+// (attention*.hip, kv_append.hip); this file only validates, plans and
+// enqueues.
 #include <hip/hip_runtime.h>
 #include <stdlib.h>
 #include <string.h>
@@ -206,6 +207,45 @@ int contiguous_prefill_attention_pieces(const void* q, const void* k, const void
   return ppa::run_pieces(q, k, v, nullptr, false, history_len, chunk_rows, piece_rows, n_q_heads,
                          n_kv_heads, head_dim, 16, n_splits, out, dtype,
                          reinterpret_cast<hipStream_t>(stream));
+}
+
+int paged_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                    const int32_t* block_table, int64_t history_len, int32_t rows, int32_t n_kv_heads,
+                    int32_t head_dim, int32_t page_size, int32_t dtype, ppa_stream_t stream) {
+  const ppa::Shape shape{history_len, rows, n_kv_heads, n_kv_heads, head_dim, page_size, dtype};
+  int rc = ppa::check_shape(shape);
+  if (rc != PPA_OK) return rc;
+  if (rows == 0) return PPA_OK;
+  if (!k_new || !v_new || !k_pages || !v_pages || !block_table) return PPA_ERR_NULL_PTR;
+  if (!ppa::aligned16(k_new) || !ppa::aligned16(v_new) || !ppa::aligned16(k_pages) || !ppa::aligned16(v_pages))
+    return PPA_ERR_ALIGNMENT;
+  // The new rows must not start where a pool starts, and K and V need pools
+  // of their own (the pool sizes are not arguments, so partial overlaps cannot
+  // be checked).
+  const char* pools[2] = {static_cast<const char*>(k_pages), static_cast<const char*>(v_pages)};
+  const char* news[2] = {static_cast<const char*>(k_new), static_cast<const char*>(v_new)};
+  for (const char* nb : news)
+    for (const char* pb : pools)
+      if (nb == pb) return PPA_ERR_ALIAS;
+  if (k_pages == v_pages) return PPA_ERR_ALIAS;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (ppa::env_validate()) {
+    const int64_t first = history_len / page_size;
+    const int64_t last = (history_len + rows - 1) / page_size;
+    rc = ppa::validate_block_table(block_table + first, last - first + 1, s);
+    if (rc != PPA_OK) return rc;
+  }
+  ppa::AppendArgs a;
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.k_pages = static_cast<uint16_t*>(k_pages);
+  a.v_pages = static_cast<uint16_t*>(v_pages);
+  a.bt = block_table;
+  a.history = history_len;
+  a.rows = rows;
+  a.upr = n_kv_heads * head_dim * 2 / 16;
+  a.log2_ps = ppa::log2_exact(page_size);
+  return ppa::launch_kv_append(a, s) == hipSuccess ? PPA_OK : PPA_ERR_HIP;
 }
 
 int paged_prefill_release_workspaces(void) {

@@ -39,10 +39,24 @@ struct MergeArgs {
   int32_t n_splits;
 };
 
+// KV append: rows [R][Hkv][d] of K and V into their pages.
+struct AppendArgs {
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint16_t* k_pages;
+  uint16_t* v_pages;
+  const int32_t* bt;
+  int64_t history;
+  int32_t rows;
+  int32_t upr;      // 16-byte units per token row: Hkv * d * 2 / 16
+  int32_t log2_ps;
+};
+
 // dtype: 0 = fp16, 1 = bf16.  Returns hipSuccess or the launch error.
 hipError_t launch_attention(const AttnArgs& a, int head_dim, int dtype, bool paged, int grid,
                             hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int head_dim, int dtype, int grid, hipStream_t stream);
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 // The per-head-dimension halves of launch_attention (separate translation units).
 hipError_t launch_attention_d64_d128(const AttnArgs& a, int head_dim, int dtype, bool paged, int grid,
                                      hipStream_t stream);

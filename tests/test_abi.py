@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = pkg.lib()
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for name in names:
         assert hasattr(lib, name), name
     assert lib.paged_prefill_version() == 10000
@@ -124,3 +124,25 @@ def test_argument_errors_return_before_any_device_work(kw, code):
 
 def test_empty_chunk_is_a_no_op():
     assert _call_paged(R=0, q=0, kp=0, vp=0, bt=0, out=0) == 0
+
+
+def _call_append(**kw):
+    a = dict(kn=16, vn=32, kp=4096, vp=8192, bt=64, H=10, R=4, hkv=2, d=64, ps=16, dt=0)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return pkg.lib().paged_kv_append(vp(a["kn"]), vp(a["vn"]), vp(a["kp"]), vp(a["vp"]), vp(a["bt"]), a["H"],
+                                     a["R"], a["hkv"], a["d"], a["ps"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=3), -4), (dict(R=-1), -2), (dict(H=-1), -2), (dict(hkv=0), -2), (dict(d=32), -3),
+    (dict(ps=3), -3), (dict(ps=4096), -3), (dict(kn=0), -1), (dict(vp=0), -1), (dict(bt=0), -1),
+    (dict(kn=24), -8), (dict(vp=8200), -8), (dict(kn=4096), -9), (dict(vn=8192), -9), (dict(vp=4096), -9),
+    (dict(H=2 ** 31), -10),
+])
+def test_append_argument_errors_return_before_any_device_work(kw, code):
+    assert _call_append(**kw) == code
+
+
+def test_empty_append_is_a_no_op():
+    assert _call_append(R=0, kn=0, vn=0, kp=0, vp=0, bt=0) == 0
