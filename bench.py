@@ -13,8 +13,9 @@ runs on the same values right after each paged chunk (A/B), outside the
 step's value.  Also outside it (skip with --no-extra): per-chunk medians with
 a cold cache (a 512 MB scratch write before each call, more than the 256 MB
 Infinity Cache plus the 8 x 4 MB L2), the paged/contiguous ratio of the
-2048-row chunk at 1K-16K history, and a split-count sweep at 32K against the
-planner.  Prints one JSON line.
+2048-row chunk at 1K-16K history, a split-count sweep at 32K against the
+planner, and the KV append of each chunk (GB/s against HBM peak).  Prints one
+JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-ab] [--no-extra] [--copy-calibration]
 """
@@ -175,6 +176,32 @@ def extra_measurements(chunks, paged, contig, pkg, synth, to_dev, stream, reps=1
                                                                                   oc.view(torch.int16)))}
         del q, kp, vp, bt, k, v, o, oc
     out["history_sweep_2048_rows"] = sweep
+    # KV append of each chunk's own K/V rows into its pages (idempotent here):
+    # bytes = K and V rows read once and written once
+    app = {}
+    for c in chunks:
+        cs = c["case"]
+        kn, vn = c["k"][cs.history:cs.history + cs.rows], c["v"][cs.history:cs.history + cs.rows]
+        f = lambda: pkg.paged_kv_append(kn, vn, c["kp"], c["vp"], c["bt"], cs.history, stream=stream)
+        for _ in range(3):
+            f()
+        ms = timed(f, 2 * reps, stream)[0]
+        nbytes = 4 * cs.rows * cs.n_kv_heads * cs.head_dim * 2
+        app[c["name"]] = {"ms_median": round(ms, 5), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                          "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "bytes": nbytes}
+    out["kv_append_2048_rows"] = app
+    # steady state: the whole 32K history's K/V (positions 0 .. 32767) in one call
+    c = next((c for c in chunks if c["name"] == "sweep_32768"), None)
+    if c is not None:
+        n = c["case"].history
+        kn, vn = c["k"][:n], c["v"][:n]
+        f = lambda: pkg.paged_kv_append(kn, vn, c["kp"], c["vp"], c["bt"], 0, stream=stream)
+        f()
+        ms = timed(f, 2 * reps, stream)[0]
+        nbytes = 4 * n * c["case"].n_kv_heads * c["case"].head_dim * 2
+        out["kv_append_32k_rows"] = {"ms_median": round(ms, 5), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                                     "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                     "bytes": nbytes}
     c = next((c for c in chunks if c["name"] == "sweep_32768"), None)
     if c is not None:
         cs = c["case"]

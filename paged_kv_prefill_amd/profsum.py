@@ -23,8 +23,8 @@ def short(name, width=100):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("attn_kernel.h", "attention.hip", "attention_d64_d128.hip", "attention_d256.hip", "kv_append.hip",
-              "kernels.h"):
+    # the attention kernels' sources (the counters in profiles/ are theirs)
+    for f in ("attn_kernel.h", "attention.hip", "attention_d64_d128.hip", "attention_d256.hip", "kernels.h"):
         with open(os.path.join(ROOT, "paged_kv_prefill_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
