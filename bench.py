@@ -14,8 +14,9 @@ step's value.  Also outside it (skip with --no-extra): per-chunk medians with
 a cold cache (a 512 MB scratch write before each call, more than the 256 MB
 Infinity Cache plus the 8 x 4 MB L2), the paged/contiguous ratio of the
 2048-row chunk at 1K-16K history, a split-count sweep at 32K against the
-planner, and the KV append of each chunk (GB/s against HBM peak).  Prints one
-JSON line.
+planner, the KV append of each chunk (GB/s against HBM peak), and short
+appends / decode steps (1-288 rows) on each chunk's history.  Prints one JSON
+line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-ab] [--no-extra] [--copy-calibration]
 """
@@ -214,6 +215,33 @@ def extra_measurements(chunks, paged, contig, pkg, synth, to_dev, stream, reps=1
         out["split_sweep_32k_ms_median"] = res
         out["split_sweep_planner_splits"] = pkg.paged_prefill_plan(cs.history, cs.rows, cs.n_q_heads,
                                                                    cs.n_kv_heads, cs.head_dim)["n_splits"]
+    # Short appends and decode steps: the first R rows of each chunk as one
+    # call on the same history (planner splits).  KV-bound at small R, so
+    # reported as K/V bytes per second against HBM peak, with the paged /
+    # contiguous ratio (calls interleaved).
+    short = {}
+    for c in chunks:
+        cs = c["case"]
+        res = {}
+        for r in (1, 16, 128, 288):
+            q = c["q"][:r].contiguous()
+            o, oc = torch.empty_like(q), torch.empty_like(q)
+            fp = lambda: pkg.paged_prefill_attention(q, c["kp"], c["vp"], c["bt"], cs.history, out=o, stream=stream)
+            fc = lambda: pkg.contiguous_prefill_attention(q, c["k"], c["v"], cs.history, out=oc, stream=stream)
+            for _ in range(3):
+                fp()
+                fc()
+            mp, mc = timed_pair(fp, fc, 2 * reps, stream)
+            kvb = (cs.history + r) * cs.n_kv_heads * cs.head_dim * 2 * 2
+            fl = synth.exact_flops(cs.history, r, cs.n_q_heads, cs.head_dim)
+            res[f"R{r}"] = {"ms_median": round(mp, 5), "kv_gbs": round(kvb / (mp * 1e-3) / 1e9, 1),
+                            "hbm_frac": round(kvb / (mp * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                            "tflops": round(fl / (mp * 1e-3) / 1e12, 1),
+                            "splits": pkg.paged_prefill_plan(cs.history, r, cs.n_q_heads, cs.n_kv_heads,
+                                                             cs.head_dim)["n_splits"],
+                            "paged_over_contiguous": round(mp / mc, 4)}
+        short[c["name"]] = res
+    out["short_append_and_decode"] = short
     return out
 
 

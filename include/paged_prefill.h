@@ -141,7 +141,7 @@ int contiguous_prefill_attention_pieces(const void* q, const void* k, const void
  * follows the PR's split rule ("What changed": threadgroups per core times
  * cores over KV heads, capped at a full chunk's tile slots, divided by the
  * piece's tiles, clamped) with MI355X's numbers: one resident workgroup per
- * CU, 256 CUs, the tile slots of a 2048-row chunk as the cap, 64 splits at
+ * CU, 256 CUs, the tile slots of a 2048-row chunk as the cap, 128 splits at
  * most, and no split shorter than one kv-tile unit.
  */
 int paged_prefill_plan(int64_t history_len, int32_t chunk_rows, int32_t n_q_heads,

@@ -5,31 +5,94 @@
 namespace ppa {
 namespace {
 
+// Log-sum-exp merge of split partials.  A (row, head) pair is served by
+// kMergeGroups groups of D/4 threads, 4 output elements per thread; group g
+// sums its own contiguous quarter of the pair's splits, so that a pair with
+// many splits (a decode step or a short append on a long history) has four
+// waves' worth of loads in flight instead of one thread walking every split.
+// Each thread keeps 8 splits' loads in flight.  The weights are
+// exp2(lse_s - M) with M the pair's max lse; within a group the splits are
+// summed in index order, then the groups in index order: the order is fixed,
+// so results are reproducible.  Splits that start past the row's last key
+// hold nothing for it and are not read.
+constexpr int kMergeGroups = 4;
+
 template <int D, class E>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-  constexpr int TPP = D / 4;
-  constexpr int PPB = 256 / TPP;
+  constexpr int TPP = D / 4;                      // threads per (pair, group)
+  constexpr int TPAIR = TPP * kMergeGroups;       // threads per pair
+  constexpr int PPB = 256 / TPAIR;                // pairs per block
+  constexpr int WPP = TPAIR >= 64 ? TPAIR / 64 : 1;  // waves per pair
+  __shared__ float mx_part[PPB][WPP];
+  __shared__ f32x4 acc_part[PPB][kMergeGroups][TPP];
+  __shared__ float w_part[PPB][kMergeGroups];
+
   const int pairs = a.rows * a.n_q_heads;
-  const int pair = blockIdx.x * PPB + threadIdx.x / TPP;
-  if (pair >= pairs) return;
-  const int dl = (threadIdx.x % TPP) * 4;
+  const int pl = threadIdx.x / TPAIR;             // pair within the block
+  const int tp = threadIdx.x % TPAIR;             // thread within the pair
+  const int grp = tp / TPP;
+  const int t = tp % TPP;
+  const int pair_raw = blockIdx.x * PPB + pl;
+  const bool valid = pair_raw < pairs;
+  const int pair = valid ? pair_raw : pairs - 1;  // keep every thread's reads in range
   const int row = pair / a.n_q_heads;
   int nv = (int)((a.history + row) / a.split_tokens) + 1;
   if (nv > a.n_splits) nv = a.n_splits;
+  const float* lse = a.ws_lse + pair;
+
+  // The pair's max lse: strided over its threads, then across lanes and waves.
   float mx = kNegInf;
-  for (int s = 0; s < nv; ++s) mx = fmaxf(mx, a.ws_lse[(int64_t)s * pairs + pair]);
-  float wsum = 0.f;
+  for (int s = tp; s < nv; s += TPAIR) mx = fmaxf(mx, lse[(int64_t)s * pairs]);
+  constexpr int WIDTH = TPAIR < 64 ? TPAIR : 64;
+#pragma unroll
+  for (int o = WIDTH / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, WIDTH));
+  if (tp % WIDTH == 0) mx_part[pl][tp / WIDTH] = mx;
+  __syncthreads();
+  mx = mx_part[pl][0];
+#pragma unroll
+  for (int w = 1; w < WPP; ++w) mx = fmaxf(mx, mx_part[pl][w]);
+
+  // This group's splits [sb, se).
+  const int per = (nv + kMergeGroups - 1) / kMergeGroups;
+  const int sb = min(grp * per, nv);
+  const int se = min(sb + per, nv);
+  const float* op = a.ws_o + (int64_t)pair * D + 4 * t;
+  const int64_t ostride = (int64_t)pairs * D;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < nv; ++s) {
-    const float w = exp2f(a.ws_lse[(int64_t)s * pairs + pair] - mx);
-    const f32x4 ov = *(const f32x4*)(a.ws_o + ((int64_t)s * pairs + pair) * D + dl);
-    acc += w * ov;
-    wsum += w;
+  float wsum = 0.f;
+  for (int s0 = sb; s0 < se; s0 += 8) {
+    float l8[8];
+    f32x4 v8[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int s = min(s0 + j, se - 1);
+      l8[j] = lse[(int64_t)s * pairs];
+      v8[j] = *(const f32x4*)(op + s * ostride);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (s0 + j < se) {
+        const float w = exp2f(l8[j] - mx);
+        acc += w * v8[j];
+        wsum += w;
+      }
+    }
+  }
+  acc_part[pl][grp][t] = acc;
+  if (t == 0) w_part[pl][grp] = wsum;
+  __syncthreads();
+  if (grp != 0 || !valid) return;
+  acc = acc_part[pl][0][t];
+  wsum = w_part[pl][0];
+#pragma unroll
+  for (int g = 1; g < kMergeGroups; ++g) {
+    acc += acc_part[pl][g][t];
+    wsum += w_part[pl][g];
   }
   const float inv = 1.f / wsum;
   const uint32_t lo = E::bits(acc[0] * inv) | ((uint32_t)E::bits(acc[1] * inv) << 16);
   const uint32_t hi = E::bits(acc[2] * inv) | ((uint32_t)E::bits(acc[3] * inv) << 16);
-  *(u32x2*)(a.out + (int64_t)pair * D + dl) = u32x2{lo, hi};
+  *(u32x2*)(a.out + (int64_t)pair * D + 4 * t) = u32x2{lo, hi};
 }
 
 template <class E>

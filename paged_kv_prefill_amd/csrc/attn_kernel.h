@@ -668,10 +668,6 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   }
 }
 
-// Log-sum-exp merge of split partials, one (row, head) pair per D/4 threads,
-// 4 output elements per thread, splits summed in index order.  Splits that
-// start past a row's last key hold nothing for it and are not read.
-
 template <int D, class E, Addr AM>
 hipError_t launch_attn_t(const AttnArgs& a, int grid, hipStream_t stream) {
   hipLaunchKernelGGL((attn_partial_kernel<D, E, AM>), dim3(grid), dim3(256), 0, stream, a);

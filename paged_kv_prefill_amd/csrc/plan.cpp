@@ -92,7 +92,8 @@ int make_plan(const Shape& s, int32_t n_splits_req, int64_t max_ws_bytes, ppa_pl
     const int64_t o_bytes = (o_elems * 4 + 255) / 256 * 256;
     const int64_t lse_bytes = (n_eff * pairs * 4 + 255) / 256 * 256;
     out->workspace_bytes = o_bytes + lse_bytes;
-    const int threads_per_pair = s.head_dim / 4;
+    // the merge kernel: 4 groups of head_dim / 4 threads per pair
+    const int threads_per_pair = s.head_dim;
     const int pairs_per_block = kThreads / threads_per_pair;
     out->merge_grid = int32_t((pairs + pairs_per_block - 1) / pairs_per_block);
     if (n_splits_req > 0 && out->workspace_bytes > max_ws_bytes) return PPA_ERR_WORKSPACE;

@@ -13,7 +13,7 @@ constexpr int kKvTile = 64;      // keys per inner-loop tile
 constexpr int kThreads = 256;    // threads per workgroup
 constexpr int kNumCUs = 256;     // MI355X compute units
 constexpr int kWgPerCu = 1;      // resident attention workgroups per CU (LDS/VGPR bound)
-constexpr int kMaxSplits = 64;
+constexpr int kMaxSplits = 128;
 constexpr int kChunkRowsForCap = 2048;  // the cap: tile slots of a full 2048-row chunk
 
 struct Shape {

@@ -82,7 +82,7 @@ def test_plan_invariants(history, rows, hq, hkv, d, ps, req):
         assert p["n_splits"] <= max(1, min(req, -(-ctx // unit)))
     if p["n_splits"] > 1:
         assert p["workspace_bytes"] >= p["n_splits"] * rows * hq * (d + 1) * 4
-        assert p["merge_grid"] * (256 // (d // 4)) >= rows * hq
+        assert p["merge_grid"] * (256 // d) >= rows * hq
     else:
         assert p["workspace_bytes"] == 0 and p["merge_grid"] == 0
 
