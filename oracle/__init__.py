@@ -19,6 +19,9 @@ It computes, in float64 with numpy, exactly what the pages define:
 * ``kv_append``: the chunk's K/V rows written into their pages through the
   block table (the issue's publishing of completed KV pages, after its
   "Expected vs actual" table).
+* ``varlen_paged_attention``: a packed batch of sequences, each with its own
+  history, rows and block table over one shared pool (the serving setting of
+  the issue's problem statement: continuous batching, prefix caching).
 
 Every function is pinned by ``tests/test_oracle_pins.py`` against brute force,
 closed forms, torch's CPU attention with an explicit mask, invariants, and the
@@ -39,3 +42,4 @@ from .attention import (  # noqa: F401
 )
 from .rules import page_split_rule, page_piece_rows  # noqa: F401
 from .cache import kv_append  # noqa: F401
+from .varlen import varlen_paged_attention  # noqa: F401

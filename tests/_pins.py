@@ -430,6 +430,97 @@ def pin_append_contiguous(orc):
 
 CACHE_PINS = [pin_append_gather, pin_append_pieces, pin_append_contiguous]
 
+
+# ---------------------------------------------------------------- varlen
+UNUSED_ENTRY = 1 << 30   # block-table padding: indexing the pool with it raises
+
+
+def varlen_batch(rng, seqs, hq, hkv, d, ps, extra_pool=4):
+    """A packed batch of sequences [(history, rows)] over one NaN-poisoned
+    pool: each sequence gets its own pages in random pool order, its table row
+    padded with an entry that cannot be read.  Returns q, k_pages, v_pages,
+    block_tables, cu_rows, histories and the per-sequence contiguous (k, v)."""
+    n_pages = [max(1, -(-(h + r) // ps)) for h, r in seqs]
+    pool = sum(n_pages) + extra_pool
+    order = rng.permutation(pool)
+    width = max(n_pages)
+    tables = np.full((len(seqs), width), UNUSED_ENTRY, dtype=np.int64)
+    k_pages = np.full((pool, ps, hkv, d), np.nan)
+    v_pages = np.full((pool, ps, hkv, d), np.nan)
+    kv = []
+    at = 0
+    for s, (h, r) in enumerate(seqs):
+        tables[s, :n_pages[s]] = order[at:at + n_pages[s]]
+        at += n_pages[s]
+        k = rng.standard_normal((h + r, hkv, d))
+        v = rng.standard_normal((h + r, hkv, d))
+        for j in range(h + r):
+            k_pages[tables[s, j // ps], j % ps] = k[j]
+            v_pages[tables[s, j // ps], j % ps] = v[j]
+        kv.append((k, v))
+    cu = np.concatenate([[0], np.cumsum([r for _, r in seqs])]).astype(np.int64)
+    q = rng.standard_normal((int(cu[-1]), hq, d))
+    hist = np.array([h for h, _ in seqs], dtype=np.int64)
+    return q, k_pages, v_pages, tables, cu, hist, kv
+
+
+VARLEN_SEQS = [(5, 3), (0, 4), (13, 0), (2, 1), (9, 2)]
+
+
+def pin_varlen_brute_force(orc):
+    """Each sequence's rows equal the brute-force definition over that
+    sequence's own table and history (a batch with an empty sequence, a first
+    chunk, non-aligned histories)."""
+    rng = np.random.default_rng(31)
+    for hq, hkv, d, ps in ((4, 2, 3, 2), (3, 1, 4, 4)):
+        q, kp, vp, bt, cu, hist, _ = varlen_batch(rng, VARLEN_SEQS, hq, hkv, d, ps)
+        got = orc.varlen_paged_attention(q, kp, vp, bt, cu, hist, ps)
+        assert got.shape == q.shape
+        for s, (h, r) in enumerate(VARLEN_SEQS):
+            if r == 0:
+                continue
+            want = brute_force(q[cu[s]:cu[s + 1]], kp, vp, bt[s], h, ps)
+            assert max_rel(got[cu[s]:cu[s + 1]], want) < 1e-12, (s, h, r)
+
+
+def pin_varlen_sharing_and_isolation(orc):
+    """Two sequences naming the same pool pages with the same rows get the
+    same output (a shared prefix is read by both); poisoning the pages of a
+    third sequence leaves the first two bit-identical and makes only the
+    third's rows NaN."""
+    rng = np.random.default_rng(32)
+    ps = 2
+    q, kp, vp, bt, cu, hist, _ = varlen_batch(rng, [(6, 3), (6, 3), (4, 2)], 4, 2, 3, ps)
+    bt[1] = bt[0]
+    q[cu[1]:cu[2]] = q[cu[0]:cu[1]]
+    base = orc.varlen_paged_attention(q, kp, vp, bt, cu, hist, ps)
+    assert np.array_equal(base[cu[0]:cu[1]], base[cu[1]:cu[2]])
+    assert np.all(np.isfinite(base))
+    n2 = -(-(hist[2] + cu[3] - cu[2]) // ps)
+    kp2 = kp.copy()
+    kp2[bt[2, :n2]] = np.nan
+    got = orc.varlen_paged_attention(q, kp2, vp, bt, cu, hist, ps)
+    assert np.array_equal(got[:cu[2]], base[:cu[2]])
+    assert np.all(np.isnan(got[cu[2]:cu[3]]))
+
+
+def pin_varlen_permutation(orc):
+    """Reordering the sequences of a batch (rows, tables, histories together)
+    reorders the output's row blocks the same way, bit for bit."""
+    rng = np.random.default_rng(33)
+    ps = 4
+    q, kp, vp, bt, cu, hist, _ = varlen_batch(rng, VARLEN_SEQS, 4, 2, 3, ps)
+    base = orc.varlen_paged_attention(q, kp, vp, bt, cu, hist, ps)
+    perm = [3, 0, 4, 2, 1]
+    rows = [np.arange(cu[s], cu[s + 1]) for s in perm]
+    q2 = q[np.concatenate(rows)]
+    cu2 = np.concatenate([[0], np.cumsum([len(r) for r in rows])])
+    got = orc.varlen_paged_attention(q2, kp, vp, bt[perm], cu2, hist[perm], ps)
+    assert np.array_equal(got, base[np.concatenate(rows)])
+
+
+VARLEN_PINS = [pin_varlen_brute_force, pin_varlen_sharing_and_isolation, pin_varlen_permutation]
+
 ATTENTION_PINS = [
     pin_decoders, pin_gather, pin_brute_force, pin_closed_forms, pin_weights, pin_torch_sdpa,
     pin_layout_invariance, pin_split_invariance, pin_split_partials, pin_piece_invariance,

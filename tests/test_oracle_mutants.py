@@ -78,6 +78,22 @@ CACHE_MUTANTS = [
 ]
 
 
+VARLEN_MUTANTS = [
+    ("first sequence's table for every sequence", "gather_pages(k_pages, block_tables[s], ctx, page_size)",
+     "gather_pages(k_pages, block_tables[0], ctx, page_size)"),
+    ("first sequence's history for every sequence", "hist = int(history_lens[s])", "hist = int(history_lens[0])"),
+    ("row offset taken as the history", "hist = int(history_lens[s])", "hist = r0"),
+    ("context without the chunk's own keys", "ctx = hist + (r1 - r0)", "ctx = hist"),
+    ("last sequence dropped", "for s in range(len(history_lens)):", "for s in range(len(history_lens) - 1):"),
+    ("last row of each sequence dropped", "r0, r1 = int(cu_rows[s]), int(cu_rows[s + 1])",
+     "r0, r1 = int(cu_rows[s]), int(cu_rows[s + 1]) - 1"),
+    ("rows taken from the start of q", "causal_attention(q[r0:r1], k, v, hist)",
+     "causal_attention(q[:r1 - r0], k, v, hist)"),
+    ("V gathered from the K pool", "v = gather_pages(v_pages, block_tables[s], ctx, page_size)",
+     "v = gather_pages(k_pages, block_tables[s], ctx, page_size)"),
+]
+
+
 def _mutated_module(filename, old, new):
     with open(os.path.join(ORACLE_DIR, filename)) as f:
         src = f.read()
@@ -118,3 +134,9 @@ def test_unmutated_copy_passes_every_pin():
 def test_cache_mutant_is_caught(label, old, new):
     mod = _mutated_module("cache.py", old, new)
     assert _caught(mod, _pins.CACHE_PINS), f"no pin caught: {label}"
+
+
+@pytest.mark.parametrize("label,old,new", VARLEN_MUTANTS, ids=[m[0] for m in VARLEN_MUTANTS])
+def test_varlen_mutant_is_caught(label, old, new):
+    mod = _mutated_module("varlen.py", old, new)
+    assert _caught(mod, _pins.VARLEN_PINS), f"no pin caught: {label}"

@@ -21,3 +21,8 @@ def test_rule_pin(pin):
 @pytest.mark.parametrize("pin", _pins.CACHE_PINS, ids=lambda f: f.__name__)
 def test_cache_pin(pin):
     pin(oracle)
+
+
+@pytest.mark.parametrize("pin", _pins.VARLEN_PINS, ids=lambda f: f.__name__)
+def test_varlen_pin(pin):
+    pin(oracle)
