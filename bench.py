@@ -14,9 +14,9 @@ step's value.  Also outside it (skip with --no-extra): per-chunk medians with
 a cold cache (a 512 MB scratch write before each call, more than the 256 MB
 Infinity Cache plus the 8 x 4 MB L2), the paged/contiguous ratio of the
 2048-row chunk at 1K-16K history, a split-count sweep at 32K against the
-planner, the KV append of each chunk (GB/s against HBM peak), and short
-appends / decode steps (1-288 rows) on each chunk's history.  Prints one JSON
-line.
+planner, the KV append of each chunk (GB/s against HBM peak), short appends
+/ decode steps (1-288 rows) on each chunk's history, and multi-sequence
+batches in one launch against one call per sequence.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-ab] [--no-extra] [--copy-calibration]
 """
@@ -242,7 +242,65 @@ def extra_measurements(chunks, paged, contig, pkg, synth, to_dev, stream, reps=1
                             "paged_over_contiguous": round(mp / mc, 4)}
         short[c["name"]] = res
     out["short_append_and_decode"] = short
+    out["varlen"] = varlen_measurements(pkg, synth, stream, reps)
     return out
+
+
+def varlen_measurements(pkg, synth, stream, reps):
+    """Several sequences in one launch against one call per sequence: a batch
+    of 32 decode rows at histories 2K-16K (16/2 heads, d 256, bf16) and eight
+    256-row chunks at 8K-15K (fp16).  K/V GB/s counts each sequence's keys
+    once."""
+    import numpy as np
+    import torch
+    dev = stream.device
+    rng = np.random.default_rng(99)
+    batches = {
+        "decode_32x1_h2k_16k_bf16": ([(int(h), 1) for h in rng.integers(2048, 16384, size=32)], "bf16"),
+        "prefill_8x256_h8k_15k_f16": ([(8192 + 1024 * i, 256) for i in range(8)], "f16"),
+    }
+    res = {}
+    for name, (seqs, dtype) in batches.items():
+        case = synth.make_varlen_case(name, seqs, 16, 2, 256, 16, dtype, seed=41)
+        dt = torch.float16 if dtype == "f16" else torch.bfloat16
+
+        def dv(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(dt).to(dev)
+
+        q, kp, vp = dv(case.q), dv(case.k_pages), dv(case.v_pages)
+        bt = torch.from_numpy(case.block_tables).to(dev)
+        cu = torch.from_numpy(case.cu_rows).to(dev)
+        hist = torch.from_numpy(case.history_lens).to(dev)
+        o, o1 = torch.empty_like(q), torch.empty_like(q)
+        rows = [(int(case.cu_rows[i]), int(case.cu_rows[i + 1])) for i in range(len(seqs))]
+        qs = [q[a:b] for a, b in rows]
+        os_ = [o1[a:b] for a, b in rows]
+        bts = [bt[i] for i in range(len(seqs))]
+        fv = lambda: pkg.paged_prefill_attention_varlen(q, kp, vp, bt, cu, hist, case.max_rows, case.max_context,
+                                                        out=o, stream=stream)
+
+        def fs():
+            for i, (h, _) in enumerate(seqs):
+                pkg.paged_prefill_attention(qs[i], kp, vp, bts[i], h, out=os_[i], stream=stream)
+
+        for _ in range(3):
+            fv()
+            fs()
+        mv, ms = timed_pair(fv, fs, 2 * reps, stream)
+        kvb = sum((h + r) * 2 * 256 * 2 * 2 for h, r in seqs)
+        fl = sum(synth.exact_flops(h, r, 16, 256) for h, r in seqs)
+        plan = pkg.paged_prefill_plan_varlen(len(seqs), int(case.cu_rows[-1]), case.max_rows, case.max_context,
+                                             16, 2, 256)
+        res[name] = {"ms_median": round(mv, 5), "one_call_per_sequence_ms_median": round(ms, 5),
+                     "speedup_over_separate_calls": round(ms / mv, 3),
+                     "kv_gbs": round(kvb / (mv * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(kvb / (mv * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "tflops": round(fl / (mv * 1e-3) / 1e12, 1), "splits": plan["n_splits"],
+                     # the two plans cut the histories into different splits: rounding differs
+                     "max_abs_diff_vs_separate_calls": float((o.float() - o1.float()).abs().max())}
+        del q, kp, vp, bt, cu, hist, o, o1, qs, os_, bts
+        torch.cuda.empty_cache()
+    return res
 
 
 def main():

@@ -128,6 +128,45 @@ int paged_prefill_attention_pieces(const void* q, const void* k_pages, const voi
                                    int32_t n_kv_heads, int32_t head_dim, int32_t page_size,
                                    int32_t n_splits, void* out, int32_t dtype, ppa_stream_t stream);
 
+/*
+ * Several sequences in one launch (varlen chunked prefill; the issue's
+ * opening places paged KV in serving with continuous batching and prefix
+ * caching).  Sequence s owns rows [cu_rows[s], cu_rows[s+1]) of q and out,
+ * has history history_lens[s], and row s of block_tables as its block table
+ * (block_tables[s * block_table_stride + j] = pool page of its logical page
+ * j).  Each sequence's rows get exactly the single-sequence result: its rows
+ * attend to its own history and, causally, to themselves, never to another
+ * sequence's keys.  Tables may name the same pool pages (a shared prefix).
+ *
+ *   q, out          [total_rows][Hq][d], the sequences' rows back to back
+ *   k_pages/v_pages one pool, [n_pool_pages][page_size][Hkv][d]
+ *   block_tables    device int32 [n_seqs][block_table_stride],
+ *                   block_table_stride >= ceil(max_context / page_size)
+ *   cu_rows         device int32 [n_seqs + 1]: 0 = cu_rows[0] <= ... <=
+ *                   cu_rows[n_seqs] = total_rows
+ *   history_lens    device int64 [n_seqs], >= 0
+ *   max_rows        host: >= every sequence's rows (sizes the grid)
+ *   max_context     host: >= every history_lens[s] + rows_s (sizes the splits)
+ *
+ * The device arrays are not read on the host: if they break the bounds above,
+ * rows past max_rows or keys past the splits are silently not computed, and
+ * an entry of cu_rows past total_rows makes the kernels read outside q.
+ * PPA_VALIDATE=1 copies them to the host and checks them first
+ * (PPA_ERR_BAD_SHAPE, or PPA_ERR_BLOCK_TABLE for a negative table entry).
+ * Splits are cut for max_context (n_splits as in paged_prefill_attention);
+ * a shorter sequence uses the leading splits it reaches.  n_seqs == 0 or
+ * total_rows == 0 is a no-op.  Errors: PPA_ERR_BAD_SHAPE for negative
+ * counts, max_rows > total_rows, max_context < max_rows or a stride below
+ * ceil(max_context / page_size); PPA_ERR_TOO_LARGE for n_seqs > 65535.
+ */
+int paged_prefill_attention_varlen(const void* q, const void* k_pages, const void* v_pages,
+                                   const int32_t* block_tables, int32_t block_table_stride,
+                                   const int32_t* cu_rows, const int64_t* history_lens,
+                                   int32_t n_seqs, int32_t total_rows, int32_t max_rows,
+                                   int64_t max_context, int32_t n_q_heads, int32_t n_kv_heads,
+                                   int32_t head_dim, int32_t page_size, int32_t n_splits,
+                                   void* out, int32_t dtype, ppa_stream_t stream);
+
 /* Contiguous-KV counterpart of paged_prefill_attention_pieces. */
 int contiguous_prefill_attention_pieces(const void* q, const void* k, const void* v,
                                         int64_t history_len, int32_t chunk_rows,
@@ -147,6 +186,18 @@ int contiguous_prefill_attention_pieces(const void* q, const void* k, const void
 int paged_prefill_plan(int64_t history_len, int32_t chunk_rows, int32_t n_q_heads,
                        int32_t n_kv_heads, int32_t head_dim, int32_t page_size,
                        int32_t n_splits_req, ppa_plan* plan_out);
+
+/*
+ * Host-only: the plan paged_prefill_attention_varlen would use for a batch
+ * with these bounds (grid = n_seqs * tiles_m * Hkv * n_splits workgroups, of
+ * which those past a sequence's rows or splits exit at once; the split rule
+ * counts the m tiles of total_rows).  Arguments as there; n_seqs, total_rows
+ * and max_rows >= 1.
+ */
+int paged_prefill_plan_varlen(int32_t n_seqs, int32_t total_rows, int32_t max_rows,
+                              int64_t max_context, int32_t n_q_heads, int32_t n_kv_heads,
+                              int32_t head_dim, int32_t page_size, int32_t n_splits_req,
+                              ppa_plan* plan_out);
 
 /*
  * Host-only: the PR's split rule with explicit parameters,

@@ -60,6 +60,9 @@ _SIGNATURES = {
     "paged_prefill_strerror": (ctypes.c_char_p, [_I32]),
     "paged_prefill_version": (_I32, []),
     "paged_kv_append": (_I32, [_VP, _VP, _VP, _VP, _VP, _I64, _I32, _I32, _I32, _I32, _I32, _VP]),
+    "paged_prefill_attention_varlen": (_I32, [_VP, _VP, _VP, _VP, _I32, _VP, _VP, _I32, _I32, _I32, _I64, _I32,
+                                              _I32, _I32, _I32, _I32, _VP, _I32, _VP]),
+    "paged_prefill_plan_varlen": (_I32, [_I32, _I32, _I32, _I64, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(Plan)]),
 }
 
 
@@ -159,6 +162,48 @@ def contiguous_prefill_attention(q, k, v, history_len, n_splits=0, out=None, pie
         rc = lib().contiguous_prefill_attention(_ptr(q), _ptr(k), _ptr(v), *args, *tail)
         _check(rc, "contiguous_prefill_attention")
     return out
+
+
+def paged_prefill_attention_varlen(q, k_pages, v_pages, block_tables, cu_rows, history_lens, max_rows,
+                                   max_context, n_splits=0, out=None, stream=None):
+    """Several sequences in one launch.  q, out [total_rows][Hq][d] hold the
+    sequences' rows back to back; sequence s owns rows cu_rows[s] ..
+    cu_rows[s+1]-1 (cu_rows: int32 [n+1] on the GPU), has history
+    history_lens[s] (int64 [n] on the GPU) and block table block_tables[s]
+    (int32 [n][stride] on the GPU) into the shared k_pages/v_pages pool.
+    max_rows and max_context (host ints) bound every sequence's rows and
+    history + rows."""
+    import torch
+    _need_cuda(q, k_pages, v_pages, block_tables, cu_rows, history_lens, out)
+    if block_tables.dim() != 2 or block_tables.dtype != torch.int32 or cu_rows.dtype != torch.int32 \
+            or history_lens.dtype != torch.int64:
+        raise ValueError("block_tables int32 [n][stride], cu_rows int32 [n+1], history_lens int64 [n]")
+    n_seqs = history_lens.shape[0]
+    if block_tables.shape[0] != n_seqs or cu_rows.shape[0] != n_seqs + 1:
+        raise ValueError("block_tables, cu_rows and history_lens disagree on the sequence count")
+    total_rows, n_q_heads, head_dim = q.shape
+    _, page_size, n_kv_heads, kd = k_pages.shape
+    if kd != head_dim or tuple(v_pages.shape) != tuple(k_pages.shape):
+        raise ValueError("k_pages/v_pages shape mismatch")
+    if out is None:
+        out = q.new_empty(q.shape)
+    rc = lib().paged_prefill_attention_varlen(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_tables), int(block_tables.shape[1]), _ptr(cu_rows),
+        _ptr(history_lens), int(n_seqs), int(total_rows), int(max_rows), int(max_context), int(n_q_heads),
+        int(n_kv_heads), int(head_dim), int(page_size), int(n_splits), _ptr(out), _dtype_code(q),
+        _stream_handle(stream, q.device))
+    _check(rc, "paged_prefill_attention_varlen")
+    return out
+
+
+def paged_prefill_plan_varlen(n_seqs, total_rows, max_rows, max_context, n_q_heads, n_kv_heads, head_dim,
+                              page_size=16, n_splits=0):
+    plan = Plan()
+    rc = lib().paged_prefill_plan_varlen(int(n_seqs), int(total_rows), int(max_rows), int(max_context),
+                                         int(n_q_heads), int(n_kv_heads), int(head_dim), int(page_size),
+                                         int(n_splits), ctypes.byref(plan))
+    _check(rc, "paged_prefill_plan_varlen")
+    return plan.as_dict()
 
 
 def paged_kv_append(k_new, v_new, k_pages, v_pages, block_table, history_len, stream=None):

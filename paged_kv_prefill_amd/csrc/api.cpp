@@ -128,6 +128,11 @@ int run(const void* q, const void* k, const void* v, const int32_t* bt, bool pag
   a.tiles_m = plan.tiles_m;
   a.xcd_remap = (plan.grid % 8 == 0) ? 1 : 0;
   a.scale_log2 = float(1.4426950408889634 / std::sqrt(double(d)));
+  a.cu_rows = nullptr;
+  a.seq_history = nullptr;
+  a.n_seqs = 0;
+  a.bt_stride = 0;
+  a.ws_rows = rows;
 
   if (launch_attention(a, d, dtype, paged, plan.grid, stream) != hipSuccess) return PPA_ERR_HIP;
   if (plan.n_splits > 1) {
@@ -140,7 +145,122 @@ int run(const void* q, const void* k, const void* v, const int32_t* bt, bool pag
     m.n_q_heads = hq;
     m.split_tokens = plan.split_tokens;
     m.n_splits = plan.n_splits;
-    if (launch_merge(m, d, dtype, plan.merge_grid, stream) != hipSuccess) return PPA_ERR_HIP;
+    m.cu_rows = nullptr;
+    m.seq_history = nullptr;
+    m.n_seqs = 0;
+    m.ws_rows = rows;
+    if (launch_merge(m, d, dtype, plan.merge_grid, 1, stream) != hipSuccess) return PPA_ERR_HIP;
+  }
+  return PPA_OK;
+}
+
+// Host check of a varlen launch's device arrays (PPA_VALIDATE=1): row offsets
+// start at 0, never decrease and end at total_rows; each sequence fits the
+// host-side bounds; its block-table entries are not negative.
+int validate_varlen(const int32_t* bt, int32_t bt_stride, const int32_t* cu_rows,
+                    const int64_t* hist, int32_t n_seqs, int32_t total_rows, int32_t max_rows,
+                    int64_t max_context, int32_t ps, hipStream_t stream) {
+  std::vector<int32_t> cu(size_t(n_seqs) + 1), table(size_t(n_seqs) * size_t(bt_stride));
+  std::vector<int64_t> h(static_cast<size_t>(n_seqs));
+  if (hipMemcpyAsync(cu.data(), cu_rows, cu.size() * 4, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipMemcpyAsync(h.data(), hist, h.size() * 8, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipMemcpyAsync(table.data(), bt, table.size() * 4, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return PPA_ERR_HIP;
+  if (cu[0] != 0 || cu[size_t(n_seqs)] != total_rows) return PPA_ERR_BAD_SHAPE;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    const int64_t r = int64_t(cu[size_t(i) + 1]) - cu[size_t(i)];
+    if (r < 0 || r > max_rows || h[size_t(i)] < 0 || h[size_t(i)] + r > max_context) return PPA_ERR_BAD_SHAPE;
+    const int64_t pages = (h[size_t(i)] + r + ps - 1) / ps;
+    for (int64_t j = 0; j < pages; ++j)
+      if (table[size_t(i) * size_t(bt_stride) + size_t(j)] < 0) return PPA_ERR_BLOCK_TABLE;
+  }
+  return PPA_OK;
+}
+
+int run_varlen(const void* q, const void* k, const void* v, const int32_t* bt, int32_t bt_stride,
+               const int32_t* cu_rows, const int64_t* hist, int32_t n_seqs, int32_t total_rows,
+               int32_t max_rows, int64_t max_context, int32_t hq, int32_t hkv, int32_t d,
+               int32_t ps, int32_t n_splits, void* out, int32_t dtype, hipStream_t stream) {
+  if (n_seqs < 0 || total_rows < 0 || max_rows < 0 || max_rows > total_rows ||
+      max_context < max_rows || n_splits < 0)
+    return PPA_ERR_BAD_SHAPE;
+  if (n_seqs > 65535) return PPA_ERR_TOO_LARGE;  // the merge grid's y extent
+  // Shape checks with the batch's bounds: ctx = max_context, q/out rows = total_rows.
+  Shape shape{max_context > total_rows ? max_context - total_rows : 0, total_rows, hq, hkv, d, ps, dtype};
+  int rc = check_shape(shape);
+  if (rc != PPA_OK) return rc;
+  if (n_seqs == 0 || total_rows == 0 || max_rows == 0) return PPA_OK;
+  if (!q || !k || !v || !out || !bt || !cu_rows || !hist) return PPA_ERR_NULL_PTR;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return PPA_ERR_ALIGNMENT;
+  const int lps = log2_exact(ps);
+  if (int64_t(bt_stride) < (max_context + ps - 1) / ps) return PPA_ERR_BAD_SHAPE;
+  if (int64_t(n_seqs) * bt_stride >= (int64_t(1) << 31)) return PPA_ERR_TOO_LARGE;
+  const int64_t qbytes = int64_t(total_rows) * hq * d * 2;
+  const char* qb = static_cast<const char*>(q);
+  const char* ob = static_cast<const char*>(out);
+  if (ob < qb + qbytes && qb < ob + qbytes) return PPA_ERR_ALIAS;
+
+  Shape ps_shape{0, total_rows, hq, hkv, d, ps, dtype};
+  ppa_plan plan;
+  rc = make_plan_varlen(ps_shape, n_seqs, max_rows, max_context, n_splits, max_workspace_bytes(), &plan);
+  if (rc != PPA_OK) return rc;
+  if (plan.workspace_bytes > max_workspace_bytes()) return PPA_ERR_WORKSPACE;
+  if (env_validate()) {
+    rc = validate_varlen(bt, bt_stride, cu_rows, hist, n_seqs, total_rows, max_rows, max_context, ps,
+                         stream);
+    if (rc != PPA_OK) return rc;
+  }
+  void* ws = nullptr;
+  if (plan.n_splits > 1) {
+    rc = get_workspace(stream, plan.workspace_bytes, &ws);
+    if (rc != PPA_OK) return rc;
+  }
+  const int64_t pairs = int64_t(total_rows) * hq;
+  const int64_t o_bytes = (int64_t(plan.n_splits) * pairs * d * 4 + 255) / 256 * 256;
+
+  AttnArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.bt = bt;
+  a.out = static_cast<uint16_t*>(out);
+  a.ws_o = static_cast<float*>(ws);
+  a.ws_lse = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + o_bytes) : nullptr;
+  a.history = 0;  // per sequence
+  a.rows = 0;
+  a.n_q_heads = hq;
+  a.n_kv_heads = hkv;
+  a.group = hq / hkv;
+  a.log2_ps = lps;
+  a.ctx = 0;
+  a.split_tokens = plan.split_tokens;
+  a.n_splits = plan.n_splits;
+  a.tiles_m = plan.tiles_m;
+  a.xcd_remap = (plan.grid % 8 == 0) ? 1 : 0;
+  a.scale_log2 = float(1.4426950408889634 / std::sqrt(double(d)));
+  a.cu_rows = cu_rows;
+  a.seq_history = hist;
+  a.n_seqs = n_seqs;
+  a.bt_stride = bt_stride;
+  a.ws_rows = total_rows;
+
+  if (launch_attention(a, d, dtype, true, plan.grid, stream) != hipSuccess) return PPA_ERR_HIP;
+  if (plan.n_splits > 1) {
+    MergeArgs m;
+    m.ws_o = a.ws_o;
+    m.ws_lse = a.ws_lse;
+    m.out = a.out;
+    m.history = 0;
+    m.rows = 0;
+    m.n_q_heads = hq;
+    m.split_tokens = plan.split_tokens;
+    m.n_splits = plan.n_splits;
+    m.cu_rows = cu_rows;
+    m.seq_history = hist;
+    m.n_seqs = n_seqs;
+    m.ws_rows = total_rows;
+    if (launch_merge(m, d, dtype, plan.merge_grid / n_seqs, n_seqs, stream) != hipSuccess) return PPA_ERR_HIP;
   }
   return PPA_OK;
 }
@@ -206,6 +326,19 @@ int contiguous_prefill_attention_pieces(const void* q, const void* k, const void
                                         int32_t dtype, ppa_stream_t stream) {
   return ppa::run_pieces(q, k, v, nullptr, false, history_len, chunk_rows, piece_rows, n_q_heads,
                          n_kv_heads, head_dim, 16, n_splits, out, dtype,
+                         reinterpret_cast<hipStream_t>(stream));
+}
+
+int paged_prefill_attention_varlen(const void* q, const void* k_pages, const void* v_pages,
+                                   const int32_t* block_tables, int32_t block_table_stride,
+                                   const int32_t* cu_rows, const int64_t* history_lens,
+                                   int32_t n_seqs, int32_t total_rows, int32_t max_rows,
+                                   int64_t max_context, int32_t n_q_heads, int32_t n_kv_heads,
+                                   int32_t head_dim, int32_t page_size, int32_t n_splits,
+                                   void* out, int32_t dtype, ppa_stream_t stream) {
+  return ppa::run_varlen(q, k_pages, v_pages, block_tables, block_table_stride, cu_rows,
+                         history_lens, n_seqs, total_rows, max_rows, max_context, n_q_heads,
+                         n_kv_heads, head_dim, page_size, n_splits, out, dtype,
                          reinterpret_cast<hipStream_t>(stream));
 }
 

@@ -27,16 +27,28 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   __shared__ f32x4 acc_part[PPB][kMergeGroups][TPP];
   __shared__ float w_part[PPB][kMergeGroups];
 
-  const int pairs = a.rows * a.n_q_heads;
+  // The sequence (grid y with several sequences): its first row in the
+  // workspace and output, its rows and history.
+  int r0 = 0, rows = a.rows;
+  int64_t history = a.history;
+  if (a.n_seqs > 0) {
+    r0 = a.cu_rows[blockIdx.y];
+    rows = a.cu_rows[blockIdx.y + 1] - r0;
+    history = a.seq_history[blockIdx.y];
+  }
+  const int pairs_seq = rows * a.n_q_heads;
+  if ((int)blockIdx.x * PPB >= pairs_seq) return;   // the whole block
+  const int64_t pairs = (int64_t)a.ws_rows * a.n_q_heads;  // workspace stride per split
   const int pl = threadIdx.x / TPAIR;             // pair within the block
   const int tp = threadIdx.x % TPAIR;             // thread within the pair
   const int grp = tp / TPP;
   const int t = tp % TPP;
   const int pair_raw = blockIdx.x * PPB + pl;
-  const bool valid = pair_raw < pairs;
-  const int pair = valid ? pair_raw : pairs - 1;  // keep every thread's reads in range
-  const int row = pair / a.n_q_heads;
-  int nv = (int)((a.history + row) / a.split_tokens) + 1;
+  const bool valid = pair_raw < pairs_seq;
+  const int pair_l = valid ? pair_raw : pairs_seq - 1;  // keep every thread's reads in range
+  const int row = pair_l / a.n_q_heads;
+  const int64_t pair = (int64_t)r0 * a.n_q_heads + pair_l;
+  int nv = (int)((history + row) / a.split_tokens) + 1;
   if (nv > a.n_splits) nv = a.n_splits;
   const float* lse = a.ws_lse + pair;
 
@@ -56,7 +68,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int per = (nv + kMergeGroups - 1) / kMergeGroups;
   const int sb = min(grp * per, nv);
   const int se = min(sb + per, nv);
-  const float* op = a.ws_o + (int64_t)pair * D + 4 * t;
+  const float* op = a.ws_o + pair * D + 4 * t;
   const int64_t ostride = (int64_t)pairs * D;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
@@ -92,15 +104,16 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const float inv = 1.f / wsum;
   const uint32_t lo = E::bits(acc[0] * inv) | ((uint32_t)E::bits(acc[1] * inv) << 16);
   const uint32_t hi = E::bits(acc[2] * inv) | ((uint32_t)E::bits(acc[3] * inv) << 16);
-  *(u32x2*)(a.out + (int64_t)pair * D + 4 * t) = u32x2{lo, hi};
+  *(u32x2*)(a.out + pair * D + 4 * t) = u32x2{lo, hi};
 }
 
 template <class E>
-hipError_t launch_merge_d(const MergeArgs& a, int head_dim, int grid, hipStream_t stream) {
+hipError_t launch_merge_d(const MergeArgs& a, int head_dim, int grid, int grid_y, hipStream_t stream) {
+  const dim3 g(grid, grid_y);
   switch (head_dim) {
-    case 64: hipLaunchKernelGGL((merge_kernel<64, E>), dim3(grid), dim3(256), 0, stream, a); break;
-    case 128: hipLaunchKernelGGL((merge_kernel<128, E>), dim3(grid), dim3(256), 0, stream, a); break;
-    case 256: hipLaunchKernelGGL((merge_kernel<256, E>), dim3(grid), dim3(256), 0, stream, a); break;
+    case 64: hipLaunchKernelGGL((merge_kernel<64, E>), g, dim3(256), 0, stream, a); break;
+    case 128: hipLaunchKernelGGL((merge_kernel<128, E>), g, dim3(256), 0, stream, a); break;
+    case 256: hipLaunchKernelGGL((merge_kernel<256, E>), g, dim3(256), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -114,9 +127,9 @@ hipError_t launch_attention(const AttnArgs& a, int head_dim, int dtype, bool pag
   return launch_attention_d64_d128(a, head_dim, dtype, paged, grid, stream);
 }
 
-hipError_t launch_merge(const MergeArgs& a, int head_dim, int dtype, int grid, hipStream_t stream) {
-  return dtype == 1 ? launch_merge_d<BF16>(a, head_dim, grid, stream)
-                    : launch_merge_d<F16>(a, head_dim, grid, stream);
+hipError_t launch_merge(const MergeArgs& a, int head_dim, int dtype, int grid, int grid_y, hipStream_t stream) {
+  return dtype == 1 ? launch_merge_d<BF16>(a, head_dim, grid, grid_y, stream)
+                    : launch_merge_d<F16>(a, head_dim, grid, grid_y, stream);
 }
 
 }  // namespace ppa

@@ -12,6 +12,10 @@
 // is cut into splits whose partials (output normalised by its own softmax
 // sum, plus its log-sum-exp) are merged by a second kernel.
 //
+// A launch may also cover a packed batch of sequences, each with its own rows,
+// history and block-table row over one page pool: each workgroup then first
+// finds its sequence (see AttnArgs) and otherwise runs unchanged.
+//
 // Workgroup = 4 waves = 128 query vectors of one KV head.  A query vector is
 // one (row, head) pair of the head group, flattened row-major, so the G heads
 // of a row share a causal limit and every K/V byte staged in LDS serves
@@ -231,7 +235,24 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   const int mt = b % a.tiles_m;
   const int rest = b / a.tiles_m;
   const int g = rest % a.n_kv_heads;
-  const int s = rest / a.n_kv_heads;
+  const int rest2 = rest / a.n_kv_heads;
+  const int s = rest2 % a.n_splits;
+  // Several sequences: this workgroup's sequence, its rows and history.
+  // Workgroups past the sequence's m tiles or past its last split exit (the
+  // merge reads no split that starts after a row's last key).
+  int ws_row0 = 0;
+  if (a.n_seqs > 0) {
+    const int seq = rest2 / a.n_splits;
+    const int r0 = a.cu_rows[seq];
+    a.rows = a.cu_rows[seq + 1] - r0;
+    a.history = a.seq_history[seq];
+    a.ctx = (int)a.history + a.rows;
+    if (mt * 128 >= a.rows * a.group || s * a.split_tokens >= a.ctx) return;
+    a.q += (int64_t)r0 * a.n_q_heads * D;
+    a.out += (int64_t)r0 * a.n_q_heads * D;
+    a.bt += (int64_t)seq * a.bt_stride;
+    ws_row0 = r0;
+  }
 
   const int G = a.group;
   const int nqv = a.rows * G;
@@ -654,8 +675,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         *(u32x2*)(op + 32 * db + 8 * q4) = u32x2{lo, hi};
       }
   } else {
-    const int64_t pairs = (int64_t)a.rows * a.n_q_heads;
-    float* wp = a.ws_o + ((int64_t)s * pairs + pair) * D + 4 * h;
+    const int64_t pairs = (int64_t)a.ws_rows * a.n_q_heads;
+    const int64_t wpair = pair + (int64_t)ws_row0 * a.n_q_heads;
+    float* wp = a.ws_o + ((int64_t)s * pairs + wpair) * D + 4 * h;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -664,7 +686,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                     o[db][4 * q4 + 3] * inv};
         *(f32x4*)(wp + 32 * db + 8 * q4) = v4;
       }
-    if (h == 0) a.ws_lse[(int64_t)s * pairs + pair] = l_tot > 0.f ? m_ref + log2f(l_tot) : kNegInf;
+    if (h == 0) a.ws_lse[(int64_t)s * pairs + wpair] = l_tot > 0.f ? m_ref + log2f(l_tot) : kNegInf;
   }
 }
 

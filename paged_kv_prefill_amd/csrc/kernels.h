@@ -26,6 +26,17 @@ struct AttnArgs {
   int32_t tiles_m;         // m tiles per KV head
   int32_t xcd_remap;       // 1: spread consecutive logical tiles over one XCD
   float scale_log2;        // log2(e) / sqrt(D)
+  // Several sequences in one launch (n_seqs > 0): sequence s owns rows
+  // [cu_rows[s], cu_rows[s+1]) of q, out and the workspace, has history
+  // seq_history[s] and block-table row bt + s * bt_stride.  The workgroup
+  // then takes rows, history and ctx above from these arrays; tiles_m and
+  // n_splits are the launch's maxima and workgroups beyond a sequence's
+  // tiles or splits exit.  n_seqs == 0: one sequence, as described above.
+  const int32_t* cu_rows;
+  const int64_t* seq_history;
+  int32_t n_seqs;
+  int32_t bt_stride;
+  int32_t ws_rows;         // rows of the workspace layout (all sequences)
 };
 
 struct MergeArgs {
@@ -37,6 +48,11 @@ struct MergeArgs {
   int32_t n_q_heads;
   int32_t split_tokens;
   int32_t n_splits;
+  // As in AttnArgs; with n_seqs > 0 the grid's y index is the sequence.
+  const int32_t* cu_rows;
+  const int64_t* seq_history;
+  int32_t n_seqs;
+  int32_t ws_rows;
 };
 
 // KV append: rows [R][Hkv][d] of K and V into their pages.
@@ -55,7 +71,7 @@ struct AppendArgs {
 // dtype: 0 = fp16, 1 = bf16.  Returns hipSuccess or the launch error.
 hipError_t launch_attention(const AttnArgs& a, int head_dim, int dtype, bool paged, int grid,
                             hipStream_t stream);
-hipError_t launch_merge(const MergeArgs& a, int head_dim, int dtype, int grid, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, int head_dim, int dtype, int grid, int grid_y, hipStream_t stream);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 // The per-head-dimension halves of launch_attention (separate translation units).
 hipError_t launch_attention_d64_d128(const AttnArgs& a, int head_dim, int dtype, bool paged, int grid,

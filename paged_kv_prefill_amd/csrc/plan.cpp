@@ -55,17 +55,21 @@ static int split_rule(int32_t cores, int32_t kv_heads, int32_t tiles, int32_t pe
   return int(splits);
 }
 
-int make_plan(const Shape& s, int32_t n_splits_req, int64_t max_ws_bytes, ppa_plan* out) {
+// The plan of a launch: split units from the longest context `ctx`, the
+// split rule's m tiles `rule_tiles`, the grid's m tiles from `grid_rows`, the
+// workspace from `ws_rows`, times `n_seqs` sequences.
+static int plan_launch(const Shape& s, int64_t ctx, int64_t rule_tiles, int64_t grid_rows,
+                       int64_t ws_rows, int32_t n_seqs, int32_t n_splits_req, int64_t max_ws_bytes,
+                       ppa_plan* out) {
   const int32_t group = s.n_q_heads / s.n_kv_heads;
-  const int64_t ctx = s.history + s.rows;
   const int32_t unit = s.page_size > kKvTile ? s.page_size : kKvTile;
   const int64_t n_units = (ctx + unit - 1) / unit;
-  const int64_t tiles_m = (int64_t(s.rows) * group + kMTile - 1) / kMTile;
+  const int64_t tiles_m = (grid_rows * group + kMTile - 1) / kMTile;
   int64_t splits;
   if (n_splits_req <= 0) {
     const int32_t cap = int32_t((int64_t(kChunkRowsForCap) * group + kMTile - 1) / kMTile);
-    splits = split_rule(kNumCUs, s.n_kv_heads, int32_t(tiles_m > 0 ? tiles_m : 1), kWgPerCu, 1,
-                        cap, kMaxSplits);
+    const int64_t t = rule_tiles < 1 ? 1 : rule_tiles > cap ? cap : rule_tiles;
+    splits = split_rule(kNumCUs, s.n_kv_heads, int32_t(t), kWgPerCu, 1, cap, kMaxSplits);
   } else {
     splits = n_splits_req;
   }
@@ -81,27 +85,48 @@ int make_plan(const Shape& s, int32_t n_splits_req, int64_t max_ws_bytes, ppa_pl
   out->m_tile = kMTile;
   out->kv_tile = kKvTile;
   out->tiles_m = int32_t(tiles_m);
-  const int64_t grid = tiles_m * s.n_kv_heads * n_eff;
+  const int64_t grid = tiles_m * s.n_kv_heads * n_eff * n_seqs;
   if (grid >= (int64_t(1) << 31)) return PPA_ERR_TOO_LARGE;
   out->grid = int32_t(grid);
   out->reserved = 0;
   if (n_eff > 1) {
-    const int64_t pairs = int64_t(s.rows) * s.n_q_heads;
+    const int64_t pairs = ws_rows * s.n_q_heads;
     const int64_t o_elems = n_eff * pairs * s.head_dim;
     if (o_elems >= (int64_t(1) << 31)) return PPA_ERR_TOO_LARGE;
     const int64_t o_bytes = (o_elems * 4 + 255) / 256 * 256;
     const int64_t lse_bytes = (n_eff * pairs * 4 + 255) / 256 * 256;
     out->workspace_bytes = o_bytes + lse_bytes;
-    // the merge kernel: 4 groups of head_dim / 4 threads per pair
+    // the merge kernel: 4 groups of head_dim / 4 threads per pair; with
+    // several sequences one row of blocks per sequence
     const int threads_per_pair = s.head_dim;
     const int pairs_per_block = kThreads / threads_per_pair;
-    out->merge_grid = int32_t((pairs + pairs_per_block - 1) / pairs_per_block);
+    out->merge_grid = int32_t((grid_rows * s.n_q_heads + pairs_per_block - 1) / pairs_per_block * n_seqs);
     if (n_splits_req > 0 && out->workspace_bytes > max_ws_bytes) return PPA_ERR_WORKSPACE;
   } else {
     out->workspace_bytes = 0;
     out->merge_grid = 0;
   }
   return PPA_OK;
+}
+
+static int64_t m_tiles(int64_t rows, const Shape& s) {
+  return (rows * (s.n_q_heads / s.n_kv_heads) + kMTile - 1) / kMTile;
+}
+
+int make_plan(const Shape& s, int32_t n_splits_req, int64_t max_ws_bytes, ppa_plan* out) {
+  return plan_launch(s, s.history + s.rows, m_tiles(s.rows, s), s.rows, s.rows, 1, n_splits_req,
+                     max_ws_bytes, out);
+}
+
+int make_plan_varlen(const Shape& s, int32_t n_seqs, int32_t max_rows, int64_t max_context,
+                     int32_t n_splits_req, int64_t max_ws_bytes, ppa_plan* out) {
+  // Every sequence with rows has at least one m tile of its own, and at most
+  // total_rows sequences have rows: the split rule counts at least that many.
+  int64_t tiles = m_tiles(s.rows, s);
+  const int64_t nonempty = n_seqs < s.rows ? n_seqs : s.rows;
+  if (tiles < nonempty) tiles = nonempty;
+  return plan_launch(s, max_context, tiles, max_rows, s.rows, n_seqs, n_splits_req, max_ws_bytes,
+                     out);
 }
 
 }  // namespace ppa
@@ -117,6 +142,24 @@ int paged_prefill_plan(int64_t history_len, int32_t chunk_rows, int32_t n_q_head
   if (rc != PPA_OK) return rc;
   if (n_splits_req < 0) return PPA_ERR_BAD_SHAPE;
   return ppa::make_plan(s, n_splits_req, ppa::max_workspace_bytes(), plan_out);
+}
+
+int paged_prefill_plan_varlen(int32_t n_seqs, int32_t total_rows, int32_t max_rows,
+                              int64_t max_context, int32_t n_q_heads, int32_t n_kv_heads,
+                              int32_t head_dim, int32_t page_size, int32_t n_splits_req,
+                              ppa_plan* plan_out) {
+  if (!plan_out) return PPA_ERR_NULL_PTR;
+  if (n_seqs < 1 || total_rows < 1 || max_rows < 1 || max_rows > total_rows ||
+      max_context < max_rows || n_splits_req < 0)
+    return PPA_ERR_BAD_SHAPE;
+  if (n_seqs > 65535) return PPA_ERR_TOO_LARGE;
+  ppa::Shape s{max_context > total_rows ? max_context - total_rows : 0, total_rows, n_q_heads,
+               n_kv_heads, head_dim, page_size, PPA_F16};
+  int rc = ppa::check_shape(s);
+  if (rc != PPA_OK) return rc;
+  ppa::Shape ps{0, total_rows, n_q_heads, n_kv_heads, head_dim, page_size, PPA_F16};
+  return ppa::make_plan_varlen(ps, n_seqs, max_rows, max_context, n_splits_req,
+                               ppa::max_workspace_bytes(), plan_out);
 }
 
 int paged_prefill_split_rule(int32_t gpu_cores, int32_t kv_heads, int32_t tiles, int32_t per_core,

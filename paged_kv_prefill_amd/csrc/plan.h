@@ -28,6 +28,13 @@ int check_shape(const Shape& s);
 // explicitly requested split count.
 int make_plan(const Shape& s, int32_t n_splits_req, int64_t max_ws_bytes, ppa_plan* out);
 
+// The plan of a launch over n_seqs sequences: s.rows is the total row
+// count, max_rows the longest sequence's rows, max_context the longest
+// history + rows.  Splits are cut for max_context; shorter sequences use the
+// leading ones.
+int make_plan_varlen(const Shape& s, int32_t n_seqs, int32_t max_rows, int64_t max_context,
+                     int32_t n_splits_req, int64_t max_ws_bytes, ppa_plan* out);
+
 // Split workspace cap: PPA_MAX_WORKSPACE_BYTES or 2 GiB.
 int64_t max_workspace_bytes();
 

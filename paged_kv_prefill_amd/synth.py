@@ -134,3 +134,69 @@ def exact_flops(history, rows, n_q_heads, head_dim):
     """Attention FLOPs of one chunk call, counting each row's visible keys:
     4 * d * Hq * sum_i (H + i + 1) = 4 d Hq (R H + R (R + 1) / 2)."""
     return 4 * head_dim * n_q_heads * (rows * history + rows * (rows + 1) // 2)
+
+
+@dataclass
+class VarlenCase:
+    """A packed batch of sequences over one page pool (see make_varlen_case)."""
+    name: str
+    seqs: list             # [(history, rows)] per sequence
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    page_size: int
+    dtype: str
+    q: np.ndarray          # [total_rows][Hq][d] uint16
+    k_pages: np.ndarray    # [pool][ps][Hkv][d] uint16
+    v_pages: np.ndarray
+    block_tables: np.ndarray   # [n][stride] int32
+    cu_rows: np.ndarray        # [n + 1] int32
+    history_lens: np.ndarray   # [n] int64
+
+    @property
+    def max_rows(self):
+        return max([r for _, r in self.seqs] + [0])
+
+    @property
+    def max_context(self):
+        return max([h + r for h, r in self.seqs] + [0])
+
+
+def make_varlen_case(name, seqs, n_q_heads, n_kv_heads, head_dim, page_size, dtype, seed,
+                     value_scale=1.0, shared=(), extra_pool=3):
+    """A batch of sequences [(history, rows)]: per sequence, in order, K then
+    V [ctx][Hkv][d] N(0, 1) * value_scale; then the pool order (a permutation
+    handing each sequence its own pages); then Q [total_rows][Hq][d].
+    shared = [(dst, src, n_pages)]: sequence dst's first n_pages logical pages
+    are src's (a shared prefix: dst's own tokens there are not stored, so
+    its keys there are src's).  Table rows are padded with page 0 (a valid
+    page that the kernels never read for that sequence)."""
+    rng = np.random.default_rng(seed)
+    enc = ENCODERS[dtype]
+    ctxs = [h + r for h, r in seqs]
+    n_pages = [-(-c // page_size) for c in ctxs]
+    pool = sum(n_pages) + extra_pool
+    order = rng.permutation(pool)
+    stride = max(n_pages + [1])
+    tables = np.zeros((len(seqs), stride), dtype=np.int32)
+    at = 0
+    for s, n in enumerate(n_pages):
+        tables[s, :n] = order[at:at + n]
+        at += n
+    skip = {}
+    for dst, src, n in shared:
+        tables[dst, :n] = tables[src, :n]
+        skip[dst] = n * page_size
+    k_pages = np.full((pool, page_size, n_kv_heads, head_dim), POISON, dtype=np.uint16)
+    v_pages = np.full((pool, page_size, n_kv_heads, head_dim), POISON, dtype=np.uint16)
+    for s, c in enumerate(ctxs):
+        k = enc(rng.standard_normal((c, n_kv_heads, head_dim), dtype=np.float32) * np.float32(value_scale))
+        v = enc(rng.standard_normal((c, n_kv_heads, head_dim), dtype=np.float32) * np.float32(value_scale))
+        j = np.arange(skip.get(s, 0), c)
+        k_pages[tables[s, j // page_size], j % page_size] = k[j]
+        v_pages[tables[s, j // page_size], j % page_size] = v[j]
+    cu = np.concatenate([[0], np.cumsum([r for _, r in seqs])]).astype(np.int32)
+    q = enc(rng.standard_normal((int(cu[-1]), n_q_heads, head_dim), dtype=np.float32) * np.float32(value_scale))
+    hist = np.array([h for h, _ in seqs], dtype=np.int64)
+    return VarlenCase(name, list(seqs), n_q_heads, n_kv_heads, head_dim, page_size, dtype, q, k_pages, v_pages,
+                      tables, cu, hist)

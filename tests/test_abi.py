@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = pkg.lib()
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     for name in names:
         assert hasattr(lib, name), name
     assert lib.paged_prefill_version() == 10000
@@ -146,3 +146,58 @@ def test_append_argument_errors_return_before_any_device_work(kw, code):
 
 def test_empty_append_is_a_no_op():
     assert _call_append(R=0, kn=0, vn=0, kp=0, vp=0, bt=0) == 0
+
+
+def _call_varlen(**kw):
+    a = dict(q=16, kp=16, vp=16, bt=16, stride=8, cu=32, hist=48, n=3, total=12, maxr=6, maxc=100, hq=4, hkv=2,
+             d=64, ps=16, S=0, out=4096, dt=0)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return pkg.lib().paged_prefill_attention_varlen(
+        vp(a["q"]), vp(a["kp"]), vp(a["vp"]), vp(a["bt"]), a["stride"], vp(a["cu"]), vp(a["hist"]), a["n"],
+        a["total"], a["maxr"], a["maxc"], a["hq"], a["hkv"], a["d"], a["ps"], a["S"], vp(a["out"]), a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=2), -4), (dict(n=-1), -2), (dict(total=-1), -2), (dict(maxr=13), -2), (dict(maxc=5), -2),
+    (dict(stride=6), -2), (dict(S=-1), -2), (dict(n=70000), -10), (dict(d=96), -3), (dict(ps=12), -3),
+    (dict(hq=5), -2), (dict(q=0), -1), (dict(bt=0), -1), (dict(cu=0), -1), (dict(hist=0), -1), (dict(out=0), -1),
+    (dict(q=24), -8), (dict(out=16 + 64), -9), (dict(maxc=2 ** 31), -10),
+])
+def test_varlen_argument_errors_return_before_any_device_work(kw, code):
+    assert _call_varlen(**kw) == code
+
+
+def test_empty_varlen_batches_are_no_ops():
+    assert _call_varlen(n=0, q=0, kp=0, vp=0, bt=0, cu=0, hist=0, out=0) == 0
+    assert _call_varlen(total=0, maxr=0, q=0, kp=0, vp=0, bt=0, cu=0, hist=0, out=0) == 0
+
+
+@pytest.mark.parametrize("n,total,max_rows,max_ctx,hq,hkv,d,ps,req", [
+    (32, 32, 1, 32769, 16, 2, 256, 16, 0), (8, 2048, 256, 65792, 32, 4, 128, 16, 0), (5, 383, 200, 5016, 8, 2, 128, 16, 3),
+    (3, 73, 50, 1000, 4, 1, 64, 8, 0), (2, 40, 33, 433, 2, 2, 256, 32, 500), (1, 1, 1, 1, 4, 1, 64, 1, 0),
+])
+def test_varlen_plan_invariants(n, total, max_rows, max_ctx, hq, hkv, d, ps, req):
+    p = pkg.paged_prefill_plan_varlen(n, total, max_rows, max_ctx, hq, hkv, d, ps, req)
+    g = hq // hkv
+    assert p["tiles_m"] == -(-max_rows * g // 128)
+    assert p["grid"] == n * p["tiles_m"] * hkv * p["n_splits"]
+    assert p["split_tokens"] % max(64, ps) == 0
+    assert p["n_splits"] * p["split_tokens"] >= max_ctx > (p["n_splits"] - 1) * p["split_tokens"]
+    if req == 0:
+        # the split rule counts at least one m tile per sequence: a batch of
+        # decode rows does not get a one-sequence split count
+        tiles = max(-(-total * g // 128), min(n, total))
+        assert p["n_splits"] <= max(1, (256 // hkv) // tiles)
+    if p["n_splits"] > 1:
+        assert p["workspace_bytes"] >= p["n_splits"] * total * hq * (d + 1) * 4
+        assert p["merge_grid"] == -(-max_rows * hq // (256 // d)) * n
+    else:
+        assert p["workspace_bytes"] == 0 and p["merge_grid"] == 0
+
+
+def test_varlen_plan_of_one_sequence_is_the_single_call_plan():
+    for h, r in ((32768, 2048), (65536, 256), (131072, 128), (1000, 77)):
+        a = pkg.paged_prefill_plan(h, r, 16, 2, 256)
+        b = pkg.paged_prefill_plan_varlen(1, r, r, h + r, 16, 2, 256)
+        assert a == b, (h, r, a, b)
