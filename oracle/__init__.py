@@ -19,6 +19,9 @@ It computes, in float64 with numpy, exactly what the pages define:
 * ``kv_append``: the chunk's K/V rows written into their pages through the
   block table (the issue's publishing of completed KV pages, after its
   "Expected vs actual" table).
+* ``quant``: 8-bit K/V pages (q8_0's 32-value blocks with an fp16 scale),
+  dequantized in the gather, and the quantizing append (the 8-bit KV cache
+  types of the KVarN report and of the speculative-decoding page).
 * ``varlen_paged_attention``: a packed batch of sequences, each with its own
   history, rows and block table over one shared pool (the serving setting of
   the issue's problem statement: continuous batching, prefix caching).
@@ -43,3 +46,10 @@ from .attention import (  # noqa: F401
 from .rules import page_split_rule, page_piece_rows  # noqa: F401
 from .cache import kv_append  # noqa: F401
 from .varlen import varlen_paged_attention  # noqa: F401
+from .quant import (  # noqa: F401
+    quantize_q8,
+    dequantize_q8,
+    decode_scales,
+    paged_q8_attention,
+    kv_append_q8,
+)

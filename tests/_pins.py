@@ -527,3 +527,141 @@ ATTENTION_PINS = [
     pin_causality, pin_gqa_is_mha_with_repeated_kv, pin_row_subset,
 ]
 RULE_PINS = [pin_page_split_table, pin_page_piece_rows]
+
+
+# ---------------------------------------------------------------- q8 pages
+def load_q8_golden():
+    vals, qs, bits = [], [], None
+    with open(os.path.join(GOLDEN, "q8_block.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            a, b = line.split()
+            if a == "scale_bits":
+                bits = int(b, 16)
+            else:
+                vals.append(float(a))
+                qs.append(int(b))
+    return vals, qs, bits
+
+
+def pin_q8_golden_block(orc):
+    """The hand-quantized block (tests/golden/q8_block.txt), as block 1 of a
+    64-value row whose block 0 is all zero (scale 0, quants 0)."""
+    vals, qs, bits = load_q8_golden()
+    row = np.zeros(64)
+    row[32:32 + len(vals)] = vals
+    q, scale = orc.quantize_q8(row[None])
+    assert q.dtype == np.int8 and q.shape == (1, 64) and scale.shape == (1, 2)
+    want = np.zeros(64, dtype=np.int8)
+    want[32:32 + len(qs)] = qs
+    assert np.array_equal(q[0], want), q[0]
+    assert np.asarray(scale, dtype=np.float16).view(np.uint16)[0, 1] == bits
+    assert float(scale[0, 0]) == 0.0
+
+
+def pin_q8_round_trip(orc):
+    """For random blocks over six orders of magnitude (fp16-exact values):
+    every value comes back within half a step (|scale q - x| <= scale / 2),
+    the block's largest |x| maps to +-127, and (scales in fp16's normal
+    range) scaling a block by 4 scales its scale by 4 and leaves its quants
+    unchanged."""
+    rng = np.random.default_rng(41)
+    for mag in (1e-3, 0.1, 1.0, 30.0, 500.0):
+        x = (rng.standard_normal((7, 3, 128)) * mag).astype(np.float16).astype(np.float64)
+        q, scale = orc.quantize_q8(x)
+        back = orc.dequantize_q8(q, scale)
+        step = np.repeat(np.asarray(scale, dtype=np.float64), 32, axis=-1)
+        assert np.all(np.abs(back - x) <= step / 2 + 1e-300), mag
+        qb = np.abs(q.astype(np.int64)).reshape(7, 3, 4, 32).max(axis=-1)
+        assert np.all(qb == 127), mag
+        if mag >= 0.1:   # scales in fp16's normal range (subnormals round on a fixed grid)
+            q2, scale2 = orc.quantize_q8(x * 4.0)
+            assert np.array_equal(q2, q)
+            assert np.array_equal(np.asarray(scale2, np.float64), 4.0 * np.asarray(scale, np.float64))
+
+
+def pin_q8_exact_multiples_and_saturation(orc):
+    """Blocks of integer multiples k s of an fp16 step s (max |k| = 127) come
+    back exactly, with scale s; all-zero blocks give scale 0 and quants 0;
+    beyond fp16 range the scale saturates at 65504 and quants at +-127."""
+    rng = np.random.default_rng(42)
+    for s in (2.0 ** -9, 0.375, 3.0):
+        k = rng.integers(-127, 128, size=(5, 64))
+        k[:, 0] = 127
+        k[:, 40] = -127
+        q, scale = orc.quantize_q8(k * s)
+        assert np.array_equal(q.astype(np.int64), k) and np.all(np.asarray(scale, np.float64) == s)
+    q, scale = orc.quantize_q8(np.zeros((2, 64)))
+    assert not q.any() and not np.asarray(scale, np.float64).any()
+    big = np.zeros((1, 32))
+    big[0, :3] = [1.0e7, -2.0e7, 1.0e3]
+    q, scale = orc.quantize_q8(big)
+    assert float(scale[0, 0]) == 65504.0
+    assert list(q[0, :3]) == [127, -127, 0]
+
+
+def _q8_pool(rng, history, rows, hkv, d, ps, extra_pool=2):
+    ctx = history + rows
+    n_pages = -(-ctx // ps)
+    pool = n_pages + extra_pool
+    bt = rng.permutation(pool)[:n_pages].astype(np.int32)
+    kq = rng.integers(-127, 128, size=(pool, ps, hkv, d)).astype(np.int8)
+    vq = rng.integers(-127, 128, size=(pool, ps, hkv, d)).astype(np.int8)
+    ks = (rng.random((pool, ps, hkv, d // 32)) * 0.02 + 0.001).astype(np.float16)
+    vs = (rng.random((pool, ps, hkv, d // 32)) * 0.02 + 0.001).astype(np.float16)
+    return kq, ks, vq, vs, bt
+
+
+def pin_q8_attention(orc):
+    """Attention over q8 pages equals brute force over the dequantized pages
+    (tiny shapes), and equals the 16-bit attention of the dequantized
+    contiguous K/V with the table permuted."""
+    import oracle as real
+    rng = np.random.default_rng(43)
+    for rows, history, hq, hkv, d, ps in ((4, 9, 4, 2, 32, 4), (3, 0, 2, 1, 64, 2), (5, 20, 6, 3, 32, 8)):
+        kq, ks, vq, vs, bt = _q8_pool(rng, history, rows, hkv, d, ps)
+        q = rng.standard_normal((rows, hq, d))
+        got = orc.paged_q8_attention(q, kq, ks, vq, vs, bt, history, ps)
+        kd = orc.dequantize_q8(kq, ks)
+        vd = orc.dequantize_q8(vq, vs)
+        assert max_rel(got, brute_force(q, kd, vd, bt, history, ps)) < 1e-12
+        ctx = history + rows
+        kc = real.dequantize_q8(real.gather_pages(kq, bt, ctx, ps), real.gather_pages(ks, bt, ctx, ps))
+        vc = real.dequantize_q8(real.gather_pages(vq, bt, ctx, ps), real.gather_pages(vs, bt, ctx, ps))
+        assert max_rel(got, real.causal_attention(q, kc, vc, history)) < 1e-12
+
+
+def pin_q8_append(orc):
+    """Quantizing appends: the new rows' quants and scales read back through
+    the table are quantize_q8 of the rows; other slots keep their bits; two
+    appends in a row equal one."""
+    import oracle as real
+    rng = np.random.default_rng(44)
+    for history, rows, hkv, d, ps in ((5, 7, 2, 64, 4), (0, 3, 1, 32, 2), (16, 16, 2, 32, 16)):
+        kq, ks, vq, vs, bt = _q8_pool(rng, history, rows, hkv, d, ps)
+        ks, vs = ks.view(np.uint16), vs.view(np.uint16)
+        kn = rng.standard_normal((rows, hkv, d)).astype(np.float16).astype(np.float64)
+        vn = rng.standard_normal((rows, hkv, d)).astype(np.float16).astype(np.float64)
+        out = orc.kv_append_q8(kq, ks, vq, vs, bt, history, ps, kn, vn)
+        wq, wsc = real.quantize_q8(kn)
+        ctx = history + rows
+        assert np.array_equal(real.gather_pages(out[0], bt, ctx, ps)[history:], wq)
+        assert np.array_equal(real.gather_pages(out[1], bt, ctx, ps)[history:], wsc.view(np.uint16))
+        wq, wsc = real.quantize_q8(vn)
+        assert np.array_equal(real.gather_pages(out[2], bt, ctx, ps)[history:], wq)
+        assert np.array_equal(real.gather_pages(out[3], bt, ctx, ps)[history:], wsc.view(np.uint16))
+        touched = np.zeros(kq.shape[:2], dtype=bool)
+        for j in range(history, ctx):
+            touched[bt[j // ps], j % ps] = True
+        for a, b in zip(out, (kq, ks, vq, vs)):
+            assert np.array_equal(a[~touched], b[~touched])
+        half = rows // 2
+        two = orc.kv_append_q8(kq, ks, vq, vs, bt, history, ps, kn[:half], vn[:half])
+        two = orc.kv_append_q8(*two, bt, history + half, ps, kn[half:], vn[half:])
+        assert all(np.array_equal(a, b) for a, b in zip(out, two))
+
+
+QUANT_PINS = [pin_q8_golden_block, pin_q8_round_trip, pin_q8_exact_multiples_and_saturation, pin_q8_attention,
+              pin_q8_append]

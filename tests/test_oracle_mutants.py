@@ -94,6 +94,26 @@ VARLEN_MUTANTS = [
 ]
 
 
+QUANT_MUTANTS = [
+    ("scale over 128", "(amax / np.float32(127.0))", "(amax / np.float32(128.0))"),
+    ("scale kept in fp32", "scale = (amax / np.float32(127.0)).astype(np.float16)",
+     "scale = (amax / np.float32(127.0))"),
+    ("scale from the signed max", "amax = np.abs(blocks).max(axis=-1)", "amax = blocks.max(axis=-1)"),
+    ("ties rounded away from zero", "np.rint(blocks / safe)",
+     "np.trunc(blocks / safe + np.copysign(np.float32(0.5), blocks))"),
+    ("truncation instead of rounding", "np.rint(blocks / safe)", "np.trunc(blocks / safe)"),
+    ("blocks of 16", "QBLOCK = 32", "QBLOCK = 16"),
+    ("no clamp to 127", "q = np.clip(q, -127, 127).astype(np.int8)", "q = q.astype(np.int8)"),
+    ("no saturation of the scale", "scale = np.minimum(scale, np.float16(FP16_MAX))", "scale = scale"),
+    ("neighbouring block's scale", "s = np.asarray(scale).astype(np.float64)[..., None]",
+     "s = np.roll(np.asarray(scale).astype(np.float64), 1, axis=-1)[..., None]"),
+    ("V scales read from the K pool", "gather_pages(v_scale, block_table, ctx, page_size)",
+     "gather_pages(k_scale, block_table, ctx, page_size)"),
+    ("append one position late", "pos = history_len + i", "pos = history_len + i + 1"),
+    ("append of V quantized from K", "vq, vs = quantize_q8(v_new)", "vq, vs = quantize_q8(k_new)"),
+]
+
+
 def _mutated_module(filename, old, new):
     with open(os.path.join(ORACLE_DIR, filename)) as f:
         src = f.read()
@@ -140,3 +160,9 @@ def test_cache_mutant_is_caught(label, old, new):
 def test_varlen_mutant_is_caught(label, old, new):
     mod = _mutated_module("varlen.py", old, new)
     assert _caught(mod, _pins.VARLEN_PINS), f"no pin caught: {label}"
+
+
+@pytest.mark.parametrize("label,old,new", QUANT_MUTANTS, ids=[m[0] for m in QUANT_MUTANTS])
+def test_quant_mutant_is_caught(label, old, new):
+    mod = _mutated_module("quant.py", old, new)
+    assert _caught(mod, _pins.QUANT_PINS), f"no pin caught: {label}"

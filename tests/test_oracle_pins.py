@@ -26,3 +26,8 @@ def test_cache_pin(pin):
 @pytest.mark.parametrize("pin", _pins.VARLEN_PINS, ids=lambda f: f.__name__)
 def test_varlen_pin(pin):
     pin(oracle)
+
+
+@pytest.mark.parametrize("pin", _pins.QUANT_PINS, ids=lambda f: f.__name__)
+def test_quant_pin(pin):
+    pin(oracle)
