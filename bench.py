@@ -15,8 +15,9 @@ a cold cache (a 512 MB scratch write before each call, more than the 256 MB
 Infinity Cache plus the 8 x 4 MB L2), the paged/contiguous ratio of the
 2048-row chunk at 1K-16K history, a split-count sweep at 32K against the
 planner, the KV append of each chunk (GB/s against HBM peak), short appends
-/ decode steps (1-288 rows) on each chunk's history, and multi-sequence
-batches in one launch against one call per sequence.  Prints one JSON line.
+/ decode steps (1-288 rows) on each chunk's history, multi-sequence batches
+in one launch against one call per sequence, and each chunk over 8-bit K/V
+pages.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-ab] [--no-extra] [--copy-calibration]
 """
@@ -243,7 +244,49 @@ def extra_measurements(chunks, paged, contig, pkg, synth, to_dev, stream, reps=1
         short[c["name"]] = res
     out["short_append_and_decode"] = short
     out["varlen"] = varlen_measurements(pkg, synth, stream, reps)
+    out["q8_pages"] = q8_measurements(chunks, paged, pkg, synth, stream, reps)
     return out
+
+
+def q8_measurements(chunks, paged, pkg, synth, stream, reps):
+    """Each chunk over 8-bit pages of the same shapes (random quants and
+    scales), interleaved with the 16-bit paged chunk; and a one-row decode step
+    on each history, K/V bytes (quants + scales) against HBM peak."""
+    import numpy as np
+    import torch
+    dev = stream.device
+    res = {}
+    for c in chunks:
+        cs = c["case"]
+        qc = synth.make_q8_case(cs.name, cs.history, cs.rows, cs.n_q_heads, cs.n_kv_heads, cs.head_dim, cs.page_size,
+                                cs.dtype, seed=51, table="scatter" if cs.name == "long_128k" else "permute",
+                                pool_pages=65536 if cs.name == "long_128k" else None, piece_rows=cs.piece_rows)
+        kq, vq = torch.from_numpy(qc.k_quant).to(dev), torch.from_numpy(qc.v_quant).to(dev)
+        ks = torch.from_numpy(qc.k_scale.view(np.int16)).to(dev)
+        vs = torch.from_numpy(qc.v_scale.view(np.int16)).to(dev)
+        bt = torch.from_numpy(qc.block_table).to(dev)
+        o = torch.empty_like(c["q"])
+        f8 = lambda: pkg.paged_prefill_attention_q8(c["q"], kq, ks, vq, vs, bt, cs.history, out=o,
+                                                    piece_rows=cs.piece_rows, stream=stream)
+        f16 = lambda: paged(c)
+        for _ in range(3):
+            f8()
+            f16()
+        m8, m16 = timed_pair(f8, f16, reps, stream)
+        q1, o1 = c["q"][:1].contiguous(), torch.empty_like(c["q"][:1])
+        fd = lambda: pkg.paged_prefill_attention_q8(q1, kq, ks, vq, vs, bt, cs.history, out=o1, stream=stream)
+        for _ in range(3):
+            fd()
+        md = timed(fd, 2 * reps, stream)[0]
+        kvb = (cs.history + 1) * cs.n_kv_heads * (cs.head_dim + cs.head_dim // 16) * 2
+        res[c["name"]] = {"ms_median": round(m8, 4), "tflops": round(c["flops"] / (m8 * 1e-3) / 1e12, 1),
+                          "over_16bit_pages": round(m8 / m16, 3),
+                          "decode_1row_ms_median": round(md, 5),
+                          "decode_kv_gbs": round(kvb / (md * 1e-3) / 1e9, 1),
+                          "decode_hbm_frac": round(kvb / (md * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        del kq, vq, ks, vs, bt, o, qc
+        torch.cuda.empty_cache()
+    return res
 
 
 def varlen_measurements(pkg, synth, stream, reps):

@@ -167,6 +167,48 @@ int paged_prefill_attention_varlen(const void* q, const void* k_pages, const voi
                                    int32_t head_dim, int32_t page_size, int32_t n_splits,
                                    void* out, int32_t dtype, ppa_stream_t stream);
 
+/*
+ * Attention over 8-bit K/V pages, dequantized in the gather (the 8-bit KV
+ * cache types of the report "Research: KVarN V-store per-call latency grows
+ * with n_kv at fixed grid", which measures against q8_0, and of the
+ * speculative-decoding page's "--kv int8").  Each (token, KV head) row of d
+ * values is stored as d int8 quants plus one fp16 scale per block of 32
+ * consecutive values; a value reads back as scale * quant:
+ *
+ *   k_quant, v_quant  int8 [n_pool_pages][page_size][Hkv][d]
+ *   k_scale, v_scale  fp16 [n_pool_pages][page_size][Hkv][d / 32]
+ *
+ * addressed by the same block table as 16-bit pages.  q and out are fp16 or
+ * bf16 (dtype) as in paged_prefill_attention; inside, the dequantized K/V,
+ * the scores' operands and the softmax weights are fp16 (a bf16 q is
+ * converted to fp16, exact for |q| in fp16's normal range; dequantized values
+ * above 65504 overflow), accumulation is fp32.  piece_rows as in
+ * paged_prefill_attention_pieces (0 = one call).  page_size must be at least
+ * 16 (PPA_ERR_UNSUPPORTED otherwise: a 16-row load group then lies in one
+ * page).  Quants and scales 16-byte aligned.
+ */
+int paged_prefill_attention_q8(const void* q, const void* k_quant, const void* k_scale,
+                               const void* v_quant, const void* v_scale, const int32_t* block_table,
+                               int64_t history_len, int32_t chunk_rows, int32_t piece_rows,
+                               int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                               int32_t page_size, int32_t n_splits, void* out, int32_t dtype,
+                               ppa_stream_t stream);
+
+/*
+ * Quantizing KV append into 8-bit pages: rows k_new/v_new [R][Hkv][d] (fp16
+ * or bf16, dtype) at positions H .. H+R-1 go to slot (H+i) % page_size of
+ * pool page block_table[(H+i) / page_size], as in paged_kv_append.  Per
+ * block of 32 values: scale = fp16(max|x| / 127) (fp32 division, rounded to
+ * nearest even, saturated at 65504); quant = x / scale (fp32 division)
+ * rounded to nearest, ties to even, clamped to [-127, 127]; an all-zero block
+ * gets scale 0 and quants 0.  Deterministic bit for bit.  The six buffers
+ * must be distinct (PPA_ERR_ALIAS) and 16-byte aligned.
+ */
+int paged_kv_append_q8(const void* k_new, const void* v_new, void* k_quant, void* k_scale,
+                       void* v_quant, void* v_scale, const int32_t* block_table, int64_t history_len,
+                       int32_t rows, int32_t n_kv_heads, int32_t head_dim, int32_t page_size,
+                       int32_t dtype, ppa_stream_t stream);
+
 /* Contiguous-KV counterpart of paged_prefill_attention_pieces. */
 int contiguous_prefill_attention_pieces(const void* q, const void* k, const void* v,
                                         int64_t history_len, int32_t chunk_rows,

@@ -63,6 +63,9 @@ _SIGNATURES = {
     "paged_prefill_attention_varlen": (_I32, [_VP, _VP, _VP, _VP, _I32, _VP, _VP, _I32, _I32, _I32, _I64, _I32,
                                               _I32, _I32, _I32, _I32, _VP, _I32, _VP]),
     "paged_prefill_plan_varlen": (_I32, [_I32, _I32, _I32, _I64, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(Plan)]),
+    "paged_prefill_attention_q8": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                          _VP, _I32, _VP]),
+    "paged_kv_append_q8": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _I32, _I32, _I32, _I32, _I32, _VP]),
 }
 
 
@@ -204,6 +207,49 @@ def paged_prefill_plan_varlen(n_seqs, total_rows, max_rows, max_context, n_q_hea
                                          int(n_splits), ctypes.byref(plan))
     _check(rc, "paged_prefill_plan_varlen")
     return plan.as_dict()
+
+
+def paged_prefill_attention_q8(q, k_quant, k_scale, v_quant, v_scale, block_table, history_len, n_splits=0,
+                               out=None, piece_rows=0, stream=None):
+    """Attention over 8-bit pages: k_quant/v_quant int8 [pool][page_size][Hkv][d],
+    k_scale/v_scale fp16 [pool][page_size][Hkv][d/32] (value = scale * quant per
+    block of 32 along d).  q and out fp16 or bf16 [R][Hq][d]."""
+    import torch
+    _need_cuda(q, k_quant, k_scale, v_quant, v_scale, block_table, out)
+    rows, n_q_heads, head_dim = q.shape
+    _, page_size, n_kv_heads, kd = k_quant.shape
+    if kd != head_dim or tuple(v_quant.shape) != tuple(k_quant.shape) or k_quant.dtype != torch.int8 \
+            or v_quant.dtype != torch.int8 or tuple(k_scale.shape) != (k_quant.shape[0], page_size, n_kv_heads, kd // 32) \
+            or tuple(v_scale.shape) != tuple(k_scale.shape) or k_scale.element_size() != 2 or v_scale.element_size() != 2:
+        raise ValueError("int8 quants [pool][ps][Hkv][d] and 16-bit scales [pool][ps][Hkv][d/32] expected")
+    if out is None:
+        out = q.new_empty(q.shape)
+    rc = lib().paged_prefill_attention_q8(
+        _ptr(q), _ptr(k_quant), _ptr(k_scale), _ptr(v_quant), _ptr(v_scale), _ptr(block_table), int(history_len),
+        int(rows), int(piece_rows), int(n_q_heads), int(n_kv_heads), int(head_dim), int(page_size), int(n_splits),
+        _ptr(out), _dtype_code(q), _stream_handle(stream, q.device))
+    _check(rc, "paged_prefill_attention_q8")
+    return out
+
+
+def paged_kv_append_q8(k_new, v_new, k_quant, k_scale, v_quant, v_scale, block_table, history_len, stream=None):
+    """Quantize k_new/v_new [R][Hkv][d] (fp16 or bf16) into their slots of the
+    8-bit pools, in place."""
+    import torch
+    _need_cuda(k_new, v_new, k_quant, k_scale, v_quant, v_scale, block_table)
+    rows, n_kv_heads, head_dim = k_new.shape
+    _, page_size, pkv, pd = k_quant.shape
+    if (pkv, pd) != (n_kv_heads, head_dim) or tuple(v_new.shape) != tuple(k_new.shape) \
+            or k_quant.dtype != torch.int8 or v_quant.dtype != torch.int8 or tuple(v_quant.shape) != tuple(k_quant.shape) \
+            or tuple(k_scale.shape) != (k_quant.shape[0], page_size, n_kv_heads, head_dim // 32) \
+            or tuple(v_scale.shape) != tuple(k_scale.shape):
+        raise ValueError("k_new/v_new/quant/scale shapes do not match")
+    rc = lib().paged_kv_append_q8(_ptr(k_new), _ptr(v_new), _ptr(k_quant), _ptr(k_scale), _ptr(v_quant),
+                                  _ptr(v_scale), _ptr(block_table), int(history_len), int(rows), int(n_kv_heads),
+                                  int(head_dim), int(page_size), _dtype_code(k_new),
+                                  _stream_handle(stream, k_new.device))
+    _check(rc, "paged_kv_append_q8")
+    return k_quant, k_scale, v_quant, v_scale
 
 
 def paged_kv_append(k_new, v_new, k_pages, v_pages, block_table, history_len, stream=None):

@@ -32,6 +32,10 @@ KERNEL_SOURCES = (
     ("attention.hip", "0"),
     ("attention_d64_d128.hip", os.environ.get("PPA_MFMA_VGPR_FORM", "1")),
     ("attention_d256.hip", os.environ.get("PPA_MFMA_VGPR_FORM", "1")),
+    # 8-bit pages: the widening step needs registers the VGPR form does not
+    # leave at head dimension 256 (it spills there); the AGPR form does not spill
+    ("attention_q8_d64_d128.hip", os.environ.get("PPA_MFMA_VGPR_FORM_Q8", "0")),
+    ("attention_q8_d256.hip", os.environ.get("PPA_MFMA_VGPR_FORM_Q8", "0")),
     ("kv_append.hip", "0"),
 )
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}"]

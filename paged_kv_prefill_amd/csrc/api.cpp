@@ -75,16 +75,25 @@ int validate_block_table(const int32_t* bt_dev, int64_t n_entries, hipStream_t s
   return PPA_OK;
 }
 
+// Scale pools of 8-bit K/V pages (null: 16-bit pages).
+struct Q8Scales {
+  const void* k;
+  const void* v;
+};
+
 int run(const void* q, const void* k, const void* v, const int32_t* bt, bool paged,
         int64_t history, int32_t rows, int32_t hq, int32_t hkv, int32_t d, int32_t ps,
-        int32_t n_splits, void* out, int32_t dtype, hipStream_t stream) {
+        int32_t n_splits, void* out, int32_t dtype, hipStream_t stream, const Q8Scales* q8 = nullptr) {
   Shape shape{history, rows, hq, hkv, d, ps, dtype};
   int rc = check_shape(shape);
   if (rc != PPA_OK) return rc;
   if (n_splits < 0) return PPA_ERR_BAD_SHAPE;
+  if (q8 && ps < 16) return PPA_ERR_UNSUPPORTED;
   if (rows == 0) return PPA_OK;
   if (!q || !k || !v || !out || (paged && !bt)) return PPA_ERR_NULL_PTR;
+  if (q8 && (!q8->k || !q8->v)) return PPA_ERR_NULL_PTR;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return PPA_ERR_ALIGNMENT;
+  if (q8 && (!aligned16(q8->k) || !aligned16(q8->v))) return PPA_ERR_ALIGNMENT;
   const int64_t qbytes = int64_t(rows) * hq * d * 2;
   const char* qb = static_cast<const char*>(q);
   const char* ob = static_cast<const char*>(out);
@@ -133,8 +142,12 @@ int run(const void* q, const void* k, const void* v, const int32_t* bt, bool pag
   a.n_seqs = 0;
   a.bt_stride = 0;
   a.ws_rows = rows;
+  a.k_scale = q8 ? static_cast<const uint16_t*>(q8->k) : nullptr;
+  a.v_scale = q8 ? static_cast<const uint16_t*>(q8->v) : nullptr;
 
-  if (launch_attention(a, d, dtype, paged, plan.grid, stream) != hipSuccess) return PPA_ERR_HIP;
+  const hipError_t le = q8 ? launch_attention_q8(a, d, dtype, plan.grid, stream)
+                           : launch_attention(a, d, dtype, paged, plan.grid, stream);
+  if (le != hipSuccess) return PPA_ERR_HIP;
   if (plan.n_splits > 1) {
     MergeArgs m;
     m.ws_o = a.ws_o;
@@ -244,6 +257,8 @@ int run_varlen(const void* q, const void* k, const void* v, const int32_t* bt, i
   a.n_seqs = n_seqs;
   a.bt_stride = bt_stride;
   a.ws_rows = total_rows;
+  a.k_scale = nullptr;
+  a.v_scale = nullptr;
 
   if (launch_attention(a, d, dtype, true, plan.grid, stream) != hipSuccess) return PPA_ERR_HIP;
   if (plan.n_splits > 1) {
@@ -268,18 +283,18 @@ int run_varlen(const void* q, const void* k, const void* v, const int32_t* bt, i
 int run_pieces(const void* q, const void* k, const void* v, const int32_t* bt, bool paged,
                int64_t history, int32_t rows, int32_t piece_rows, int32_t hq, int32_t hkv,
                int32_t d, int32_t ps, int32_t n_splits, void* out, int32_t dtype,
-               hipStream_t stream) {
+               hipStream_t stream, const Q8Scales* q8 = nullptr) {
   if (piece_rows < 0) return PPA_ERR_BAD_SHAPE;
   Shape shape{history, rows, hq, hkv, d, ps, dtype};
   int rc = check_shape(shape);
   if (rc != PPA_OK) return rc;
   if (piece_rows == 0 || piece_rows >= rows)
-    return run(q, k, v, bt, paged, history, rows, hq, hkv, d, ps, n_splits, out, dtype, stream);
+    return run(q, k, v, bt, paged, history, rows, hq, hkv, d, ps, n_splits, out, dtype, stream, q8);
   const int64_t row_bytes = int64_t(hq) * d * 2;
   for (int32_t r0 = 0; r0 < rows; r0 += piece_rows) {
     const int32_t n = rows - r0 < piece_rows ? rows - r0 : piece_rows;
     rc = run(static_cast<const char*>(q) + r0 * row_bytes, k, v, bt, paged, history + r0, n, hq,
-             hkv, d, ps, n_splits, static_cast<char*>(out) + r0 * row_bytes, dtype, stream);
+             hkv, d, ps, n_splits, static_cast<char*>(out) + r0 * row_bytes, dtype, stream, q8);
     if (rc != PPA_OK) return rc;
   }
   return PPA_OK;
@@ -340,6 +355,58 @@ int paged_prefill_attention_varlen(const void* q, const void* k_pages, const voi
                          history_lens, n_seqs, total_rows, max_rows, max_context, n_q_heads,
                          n_kv_heads, head_dim, page_size, n_splits, out, dtype,
                          reinterpret_cast<hipStream_t>(stream));
+}
+
+int paged_prefill_attention_q8(const void* q, const void* k_quant, const void* k_scale,
+                               const void* v_quant, const void* v_scale, const int32_t* block_table,
+                               int64_t history_len, int32_t chunk_rows, int32_t piece_rows,
+                               int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                               int32_t page_size, int32_t n_splits, void* out, int32_t dtype,
+                               ppa_stream_t stream) {
+  const ppa::Q8Scales scales{k_scale, v_scale};
+  return ppa::run_pieces(q, k_quant, v_quant, block_table, true, history_len, chunk_rows, piece_rows,
+                         n_q_heads, n_kv_heads, head_dim, page_size, n_splits, out, dtype,
+                         reinterpret_cast<hipStream_t>(stream), &scales);
+}
+
+int paged_kv_append_q8(const void* k_new, const void* v_new, void* k_quant, void* k_scale,
+                       void* v_quant, void* v_scale, const int32_t* block_table, int64_t history_len,
+                       int32_t rows, int32_t n_kv_heads, int32_t head_dim, int32_t page_size,
+                       int32_t dtype, ppa_stream_t stream) {
+  const ppa::Shape shape{history_len, rows, n_kv_heads, n_kv_heads, head_dim, page_size, dtype};
+  int rc = ppa::check_shape(shape);
+  if (rc != PPA_OK) return rc;
+  if (rows == 0) return PPA_OK;
+  if (!k_new || !v_new || !k_quant || !k_scale || !v_quant || !v_scale || !block_table)
+    return PPA_ERR_NULL_PTR;
+  const void* all[6] = {k_new, v_new, k_quant, k_scale, v_quant, v_scale};
+  for (const void* p : all)
+    if (!ppa::aligned16(p)) return PPA_ERR_ALIGNMENT;
+  // the four pools must be distinct and none may start where a new-row buffer starts
+  for (int i = 0; i < 6; ++i)
+    for (int j = i + 1; j < 6; ++j)
+      if (all[i] == all[j]) return PPA_ERR_ALIAS;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (ppa::env_validate()) {
+    const int64_t first = history_len / page_size;
+    const int64_t last = (history_len + rows - 1) / page_size;
+    rc = ppa::validate_block_table(block_table + first, last - first + 1, s);
+    if (rc != PPA_OK) return rc;
+  }
+  ppa::AppendQ8Args a;
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.k_quant = static_cast<int8_t*>(k_quant);
+  a.v_quant = static_cast<int8_t*>(v_quant);
+  a.k_scale = static_cast<uint16_t*>(k_scale);
+  a.v_scale = static_cast<uint16_t*>(v_scale);
+  a.bt = block_table;
+  a.history = history_len;
+  a.rows = rows;
+  a.n_kv_heads = n_kv_heads;
+  a.head_dim = head_dim;
+  a.log2_ps = ppa::log2_exact(page_size);
+  return ppa::launch_kv_append_q8(a, dtype, s) == hipSuccess ? PPA_OK : PPA_ERR_HIP;
 }
 
 int paged_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_pages,

@@ -127,6 +127,11 @@ hipError_t launch_attention(const AttnArgs& a, int head_dim, int dtype, bool pag
   return launch_attention_d64_d128(a, head_dim, dtype, paged, grid, stream);
 }
 
+hipError_t launch_attention_q8(const AttnArgs& a, int head_dim, int dtype, int grid, hipStream_t stream) {
+  if (head_dim == 256) return launch_attention_q8_d256(a, dtype, grid, stream);
+  return launch_attention_q8_d64_d128(a, head_dim, dtype, grid, stream);
+}
+
 hipError_t launch_merge(const MergeArgs& a, int head_dim, int dtype, int grid, int grid_y, hipStream_t stream) {
   return dtype == 1 ? launch_merge_d<BF16>(a, head_dim, grid, grid_y, stream)
                     : launch_merge_d<F16>(a, head_dim, grid, grid_y, stream);

@@ -205,10 +205,16 @@ enum class Addr { Contig, PageBig, Page16, Page8, PageLane };
 // Either way the result is the same softmax; only rounding differs.
 constexpr float kRefMarginLog2 = 15.0f;
 
-template <int D, class E, Addr AM>
+// Q8: K and V pages hold 8-bit quants with an fp16 scale per 32 values along
+// d (see the q8 loader below); the tiles are widened to fp16 in LDS and the
+// MFMA, softmax and P arithmetic run in fp16 whatever the type of q and out.
+template <int D, class E, Addr AM, bool Q8 = false>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_partial_kernel(AttnArgs a) {
+  static_assert(!Q8 || AM == Addr::Page16 || AM == Addr::PageBig, "8-bit pages need pages of 16 tokens or more");
   using Gm = Geom<D>;
-  using vec8 = typename E::vec8;
+  using M = std::conditional_t<Q8, F16, E>;   // element type of the MFMA operands
+  using vec8 = typename M::vec8;
+  constexpr int EB = Q8 ? 1 : 2;              // bytes per K/V element in memory
   constexpr int CH = Gm::CH;
   constexpr int LPW = Gm::LPW;
   constexpr int KS = D / 16;   // 16-wide d steps of QK
@@ -284,7 +290,14 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 raw = qv_valid ? *(const u32x4*)(qp + 16 * ks) : u32x4{0u, 0u, 0u, 0u};
-      qf[ks] = __builtin_bit_cast(vec8, raw);
+      if constexpr (std::is_same_v<M, E>) {
+        qf[ks] = __builtin_bit_cast(vec8, raw);
+      } else {
+        // bf16 q for the fp16 MFMA: exact for |q| in fp16's normal range
+        const bf16x8 qb = __builtin_bit_cast(bf16x8, raw);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[ks][e] = (_Float16)(float)qb[e];
+      }
     }
   }
   // Wait for Q here, on every path: otherwise the compiler's wait before the
@@ -301,7 +314,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   // ---- loader -------------------------------------------------------------
   // Block b = wave * LPW + i of a tile holds rows 8 (b % 8) .. +7 and chunks
   // 8 (b / 8) .. +7 (lds_off).
-  const int hkvd2 = a.n_kv_heads * D * 2;  // bytes per token (all KV heads)
+  const int hkvd = a.n_kv_heads * D * EB;  // bytes per token (all KV heads)
   const int ps_mask = (1 << a.log2_ps) - 1;
   const int cg = (wave * LPW) >> 3;        // the wave's chunk group (same for all its blocks)
   // Lane L fills unit L of a block: row 8 rg + L / 8, chunk 8 cg + ((L % 8) ^ g(row)),
@@ -311,19 +324,19 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   const int cpart_odd = (cg * 8 + ((lane & 7) ^ lds_g(8 + lrow))) << 4;
   // Lane byte offsets within an 8-row group for whole tiles (tile to tile only
   // the group's scalar base changes).
-  const uint32_t voff_even = lrow * hkvd2 + cpart_even;
-  const uint32_t voff_odd = lrow * hkvd2 + cpart_odd;
+  const uint32_t voff_even = lrow * hkvd + cpart_even;
+  const uint32_t voff_odd = lrow * hkvd + cpart_odd;
   // Row group rg_i = (wave LPW + i) % 8 of load i starts soff[i] bytes past
   // its base: into the tile (contiguous, PageBig) or into its page.
   int soff[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     const int rg = (wave * LPW + i) & 7;
-    soff[i] = (AM == Addr::Page16 || AM == Addr::Page8 ? ((8 * rg) & ps_mask) : 8 * rg) * hkvd2;
+    soff[i] = (AM == Addr::Page16 || AM == Addr::Page8 ? ((8 * rg) & ps_mask) : 8 * rg) * hkvd;
   }
-  const char* kg = (const char*)a.k + g * D * 2;
-  const char* vg = (const char*)a.v + g * D * 2;
-  const uint32_t page_bytes = (uint32_t)hkvd2 << a.log2_ps;
+  const char* kg = (const char*)a.k + g * D * EB;
+  const char* vg = (const char*)a.v + g * D * EB;
+  const uint32_t page_bytes = (uint32_t)hkvd << a.log2_ps;
   // Scalar bases of one whole tile's loads for this wave: the tile start
   // (contiguous; with PageBig the tile's place in its page) or the page of
   // each 8-row group the wave loads (Page16: two neighbouring groups share a
@@ -343,13 +356,13 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const int t0 = k0 + j * kTK;
     const char* src = is_v ? vg : kg;
     if constexpr (AM == Addr::Contig) {
-      tb.base[0] = src + (int64_t)t0 * hkvd2;
+      tb.base[0] = src + (int64_t)t0 * hkvd;
     } else if constexpr (AM == Addr::PageBig) {
       // lane 0 holds key t0's page, which holds the whole tile
       const uint64_t paddr = (uint64_t)src + (uint64_t)(uint32_t)page * page_bytes;
       const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)paddr, 0);
       const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(paddr >> 32), 0);
-      tb.base[0] = (const char*)(((uint64_t)hi << 32) | lo) + (t0 & ps_mask) * hkvd2;
+      tb.base[0] = (const char*)(((uint64_t)hi << 32) | lo) + (t0 & ps_mask) * hkvd;
     } else {
       // per lane: address of pool page `page`
       const uint64_t paddr = (uint64_t)src + (uint64_t)(uint32_t)page * page_bytes;
@@ -400,23 +413,96 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
       const int rr = min(8 * (b & 7) + lrow, last);
       const int pg = __shfl(page, rr, 64);
       const int64_t tok = ((int64_t)pg << a.log2_ps) + ((t0 + rr) & ps_mask);
-      __builtin_amdgcn_global_load_lds((const void*)(src + tok * hkvd2 + cpart), LDS_PTR(void, dst + b * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(src + tok * hkvd + cpart), LDS_PTR(void, dst + b * 1024), 16, 0, 0);
     } else {
       const int r0c = __builtin_amdgcn_readfirstlane(min(8 * (b & 7), last & ~7));
       const int lrow_c = min(lrow, last - r0c);
       const char* base;
       if constexpr (AM == Addr::Contig) {
-        base = src + (int64_t)(t0 + r0c) * hkvd2;
+        base = src + (int64_t)(t0 + r0c) * hkvd;
       } else {
         const int pg = __builtin_amdgcn_readlane(page, r0c);
-        base = src + (((int64_t)pg << a.log2_ps) + ((t0 + r0c) & ps_mask)) * hkvd2;
+        base = src + (((int64_t)pg << a.log2_ps) + ((t0 + r0c) & ps_mask)) * hkvd;
       }
-      load_lds16(base, (uint32_t)(lrow_c * hkvd2 + cpart), 0, dst + b * 1024);
+      load_lds16(base, (uint32_t)(lrow_c * hkvd + cpart), 0, dst + b * 1024);
     }
   };
   auto issue = [&](int j, int page, bool is_v, uint8_t* dst) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) issue_one(j, page, TileBases{}, is_v, dst, i, std::false_type{});
+  };
+
+  // ---- 8-bit pages (Q8) ---------------------------------------------------
+  // A tile arrives as quants, half the bytes of a 16-bit tile, and is widened
+  // to fp16 in LDS.  Load i (of NQ = LPW / 2) of a wave covers the rows and
+  // values of its 16-bit blocks 2i and 2i+1: rows 8 rg .. 8 rg + 15 (rg even,
+  // so one page when pages hold 16 tokens or more) and values 64 cg .. +63.
+  // Lane L reads the 16 quants of row 8 rg + L / 4 at value 64 cg + 16 (L % 4)
+  // into a staging kilobyte in the upper half of the wave's own part of the
+  // destination tile, which no other wave writes.  After reading all of its
+  // staging data, the wave writes each lane's 16 values, quant * scale rounded
+  // once to fp16, into the two 16-byte chunks they occupy in the tile layout.
+  // The scales come with one 4-byte load per lane: lane l holds the scales of
+  // blocks 2 cg and 2 cg + 1 of row rbase + l.
+  constexpr int NQ = Q8 ? LPW / 2 : 1;
+  constexpr int ROWS_W = 8 * LPW < 64 ? 8 * LPW : 64;   // rows one wave's loads cover
+  const int rbase = 8 * ((wave * LPW) & 7);
+  const uint32_t voff_q = (lane >> 2) * hkvd + 64 * cg + 16 * (lane & 3);
+  const int sc_row_bytes = a.n_kv_heads * (D / 32) * 2;   // scale bytes per token
+  auto issue_q8 = [&](int j, int page, const TileBases& tb, bool is_v, uint8_t* buf, int i, auto whole)
+                      __attribute__((always_inline)) {
+    constexpr bool WHOLE = decltype(whole)::value;
+    uint8_t* dst = buf + (wave * LPW + NQ + i) * 1024;
+    if constexpr (WHOLE) {
+      load_lds16(tb.base[AM == Addr::Page16 ? i : 0], voff_q, soff[2 * i], dst);
+    } else {
+      // rows past kend - 1 read row kend - 1 (same 16-row group, same page)
+      const int t0 = k0 + j * kTK;
+      const int last = kend - 1 - t0;
+      const int rg = (wave * LPW + 2 * i) & 7;
+      const int r0c = __builtin_amdgcn_readfirstlane(min(8 * rg, last & ~15));
+      const int lrow_c = min(lane >> 2, last - r0c);
+      const int pg = __builtin_amdgcn_readlane(page, r0c);
+      const char* base = (is_v ? vg : kg) + (((int64_t)pg << a.log2_ps) + ((t0 + r0c) & ps_mask)) * hkvd;
+      load_lds16(base, (uint32_t)(lrow_c * hkvd + 64 * cg + 16 * (lane & 3)), 0, dst);
+    }
+  };
+  auto load_scales = [&](int j, int page, bool is_v) __attribute__((always_inline)) -> uint32_t {
+    const int t0 = k0 + j * kTK;
+    const int r = min(rbase + (lane % ROWS_W), kend - 1 - t0);
+    const int pg = __shfl(page, r, 64);
+    const char* sp = (const char*)(is_v ? a.v_scale : a.k_scale);
+    const int64_t tok = ((int64_t)pg << a.log2_ps) + ((t0 + r) & ps_mask);
+    return *(const uint32_t*)(sp + tok * sc_row_bytes + g * (D / 32) * 2 + 4 * cg);
+  };
+  // Load i's staging kilobyte (wave block NQ + i) is read before load i
+  // writes its blocks 2i and 2i+1, and 2i + 1 < NQ + j for every later j: the
+  // writes never reach staging data still to be read.
+  auto convert_q8 = [&](uint8_t* buf, uint32_t scales) __attribute__((always_inline)) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const u32x4 raw = *LDS_PTR(const u32x4, buf + (wave * LPW + NQ + i) * 1024 + 16 * lane);
+      const int r = 8 * ((wave * LPW + 2 * i) & 7) + (lane >> 2);
+      const uint32_t s2 = __shfl(scales, r - rbase, 64);
+      const uint32_t sb = (lane & 2) ? (s2 >> 16) : (s2 & 0xffffu);
+      const h2 ss = __builtin_bit_cast(h2, sb | (sb << 16));
+      const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+      uint32_t w[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        // byte u = quant ^ 0x80 under exponent byte 0x64 is the fp16 1024 + u:
+        // minus 1152 gives the quant exactly, times the scale rounds once
+        const uint32_t x = raw[k] ^ 0x80808080u;
+        const h2 lo = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x, 0x04010400u));
+        const h2 hi = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u));
+        w[2 * k] = __builtin_bit_cast(uint32_t, (lo - bias) * ss);
+        w[2 * k + 1] = __builtin_bit_cast(uint32_t, (hi - bias) * ss);
+      }
+      const int c0 = 8 * cg + 2 * (lane & 3);
+      *LDS_PTR(u32x4, buf + lds_off(r, c0)) = u32x4{w[0], w[1], w[2], w[3]};
+      *LDS_PTR(u32x4, buf + lds_off(r, c0 + 1)) = u32x4{w[4], w[5], w[6], w[7]};
+    }
   };
 
   // ---- MFMA phases --------------------------------------------------------
@@ -444,8 +530,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (ks + QPF < KS) load(ks + QPF);
-      sc[0] = E::mfma(__builtin_bit_cast(vec8, k0r[ks]), qf[ks], sc[0]);
-      sc[1] = E::mfma(__builtin_bit_cast(vec8, k1r[ks]), qf[ks], sc[1]);
+      sc[0] = M::mfma(__builtin_bit_cast(vec8, k0r[ks]), qf[ks], sc[0]);
+      sc[1] = M::mfma(__builtin_bit_cast(vec8, k1r[ks]), qf[ks], sc[1]);
       step_hook(ks);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -508,8 +594,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         p32[e] = __builtin_amdgcn_exp2f(fmaf(sc[e >> 4][e & 15], c, -base));
         if ((e & 7) == 7) {
           // The sum takes the rounded weights, the ones the PV product uses.
-          pb_new[e >> 3] = E::from_f32(p32 + (e & ~7));
-          rs = E::sum8(pb_new[e >> 3], rs);
+          pb_new[e >> 3] = M::from_f32(p32 + (e & ~7));
+          rs = M::sum8(pb_new[e >> 3], rs);
         }
       }
     };
@@ -520,7 +606,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
       if (i + VPF < NPV) load(i + VPF);
       const int kstep = i / DB, db = i % DB;
       i16x8 av = __builtin_shufflevector(vlo[i], vhi[i], 0, 1, 2, 3, 4, 5, 6, 7);
-      o[db] = E::mfma(__builtin_bit_cast(vec8, av), pb[kstep], o[db]);
+      o[db] = M::mfma(__builtin_bit_cast(vec8, av), pb[kstep], o[db]);
       valu(i);
       step_hook(i);
       __builtin_amdgcn_sched_barrier(0);
@@ -540,7 +626,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vt + (vofs1 ^ ((db & 1) << 6)) + imm));
         i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vt + (vofs2 ^ ((db & 1) << 6)) + imm));
         i16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[db] = E::mfma(__builtin_bit_cast(vec8, av), pb[kstep], o[db]);
+        o[db] = M::mfma(__builtin_bit_cast(vec8, av), pb[kstep], o[db]);
       }
   };
 
@@ -564,8 +650,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // This wave's loads in flight, oldest first: K(it) (issued during the QK
     // of it-1), V(it-1) (during the PV phase of it-1), LPW each.  Wait for
     // K(it) only; after the barrier K(it) is in LDS and the buffers of K(it-1)
-    // and V(it-2) are free (every wave is done with body it-1).
-    __builtin_amdgcn_s_waitcnt(kWaitVmcntLPW);
+    // and V(it-2) are free (every wave is done with body it-1).  Q8: nothing
+    // is in flight; the previous body widened K(it) and V(it-1) in LDS.
+    __builtin_amdgcn_s_waitcnt(Q8 ? kWaitVmcnt0 & ~0x0F00 : kWaitVmcntLPW);
     lds_barrier();
     // The loads of K(it+1) and V(it) are spread over the MFMA steps (one per
     // few MFMAs) rather than issued in a burst, which would stall the waves on
@@ -581,10 +668,18 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
       kb = tile_bases(it + 1, pk, false);
       vb = tile_bases(it, pv, true);
     }
+    uint32_t ksc = 0, vsc = 0;   // Q8: scales of K(it+1) and V(it)
     qk(ODD ? kbuf1 : kbuf0, [&](int ks) {
-      constexpr int EVERY = KS / LPW;
-      if (ks % EVERY == 0)
-        issue_one(it + 1, pk, kb, false, ODD ? kbuf0 : kbuf1, ks / EVERY, std::bool_constant<!MASKED>{});
+      if constexpr (Q8) {
+        constexpr int EVERY = KS / NQ;
+        if (ks % EVERY == 0)
+          issue_q8(it + 1, pk, kb, false, ODD ? kbuf0 : kbuf1, ks / EVERY, std::bool_constant<!MASKED>{});
+        if (ks == 1) ksc = load_scales(it + 1, pk, false);
+      } else {
+        constexpr int EVERY = KS / LPW;
+        if (ks % EVERY == 0)
+          issue_one(it + 1, pk, kb, false, ODD ? kbuf0 : kbuf1, ks / EVERY, std::bool_constant<!MASKED>{});
+      }
     });
     if constexpr (MASKED) {
       const int rel = lim - t0;
@@ -598,14 +693,33 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     }
     // Now in flight: V(it-1), then K(it+1).  Wait for V(it-1), which the PV
     // below reads, so that its load latency hides behind the QK phase.
-    __builtin_amdgcn_s_waitcnt(kWaitVmcntLPW);
-    lds_barrier();
+    if constexpr (!Q8) {
+      __builtin_amdgcn_s_waitcnt(kWaitVmcntLPW);
+      lds_barrier();
+    } else {
+      __builtin_amdgcn_sched_barrier(0);   // keep the two phases apart
+    }
     // PV(it-1) with the previous weights, fused with this tile's softmax.
     pv_softmax(ODD ? vbuf0 : vbuf1, [&](int i) {
-      constexpr int EVERY = 4 * DB / LPW;
-      if (i % EVERY == 0)
-        issue_one(it, pv, vb, true, ODD ? vbuf1 : vbuf0, i / EVERY, std::bool_constant<!MASKED>{});
+      if constexpr (Q8) {
+        constexpr int EVERY = 4 * DB / NQ;
+        if (i % EVERY == 0)
+          issue_q8(it, pv, vb, true, ODD ? vbuf1 : vbuf0, i / EVERY, std::bool_constant<!MASKED>{});
+        if (i == 1) vsc = load_scales(it, pv, true);
+      } else {
+        constexpr int EVERY = 4 * DB / LPW;
+        if (i % EVERY == 0)
+          issue_one(it, pv, vb, true, ODD ? vbuf1 : vbuf0, i / EVERY, std::bool_constant<!MASKED>{});
+      }
     });
+    if constexpr (Q8) {
+      // Widen K(it+1) and V(it): their buffers' last readers (QK(it-1) and
+      // PV(it-2)) finished before this body's barrier.
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      convert_q8(ODD ? kbuf0 : kbuf1, ksc);
+      convert_q8(ODD ? vbuf1 : vbuf0, vsc);
+    }
   };
   // Tiles in even/odd pairs so that each body has its buffers fixed at compile
   // time and the output accumulators flow through one chain of code.
@@ -634,10 +748,19 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     for (int i = tid; i < Gm::TILE_BYTES / 16; i += 256) *LDS_PTR(u32x4, vbuf1 + i * 16) = u32x4{0u, 0u, 0u, 0u};
     if (n_tiles > 0) {
       pg0 = pages(0);
-      issue(0, pg0, false, kbuf0);
-      pg1 = pages(1);
-      // K(0) is the only load in flight: the first body's vmcnt(LPW) would not wait for it.
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      if constexpr (Q8) {
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) issue_q8(0, pg0, TileBases{}, false, kbuf0, i, std::false_type{});
+        const uint32_t s0 = load_scales(0, pg0, false);
+        pg1 = pages(1);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        convert_q8(kbuf0, s0);
+      } else {
+        issue(0, pg0, false, kbuf0);
+        pg1 = pages(1);
+        // K(0) is the only load in flight: the first body's vmcnt(LPW) would not wait for it.
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      }
     }
     int it = 0;
     run(it, n_fast, std::false_type{});
@@ -690,10 +813,18 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   }
 }
 
-template <int D, class E, Addr AM>
+template <int D, class E, Addr AM, bool Q8 = false>
 hipError_t launch_attn_t(const AttnArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_partial_kernel<D, E, AM>), dim3(grid), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((attn_partial_kernel<D, E, AM, Q8>), dim3(grid), dim3(256), 0, stream, a);
   return hipGetLastError();
+}
+
+// 8-bit pages: 16 tokens per page or more (the host checks).
+template <int D, class E>
+hipError_t launch_attn_q8(const AttnArgs& a, int grid, hipStream_t stream) {
+  if (a.log2_ps >= 6) return launch_attn_t<D, E, Addr::PageBig, true>(a, grid, stream);
+  if (a.log2_ps >= 4) return launch_attn_t<D, E, Addr::Page16, true>(a, grid, stream);
+  return hipErrorInvalidValue;
 }
 
 template <int D, class E>

@@ -37,6 +37,10 @@ struct AttnArgs {
   int32_t n_seqs;
   int32_t bt_stride;
   int32_t ws_rows;         // rows of the workspace layout (all sequences)
+  // 8-bit pages: k and v point to int8 quants [pool][ps][Hkv][D], these to
+  // their fp16 scales [pool][ps][Hkv][D / 32] (one per 32 values along D).
+  const uint16_t* k_scale;
+  const uint16_t* v_scale;
 };
 
 struct MergeArgs {
@@ -68,14 +72,38 @@ struct AppendArgs {
   int32_t log2_ps;
 };
 
+// Quantizing KV append into 8-bit pages: rows [R][Hkv][D] (fp16 or bf16) to
+// int8 quants [pool][ps][Hkv][D] and fp16 scales [pool][ps][Hkv][D / 32].
+struct AppendQ8Args {
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  int8_t* k_quant;
+  int8_t* v_quant;
+  uint16_t* k_scale;
+  uint16_t* v_scale;
+  const int32_t* bt;
+  int64_t history;
+  int32_t rows;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t log2_ps;
+};
+
 // dtype: 0 = fp16, 1 = bf16.  Returns hipSuccess or the launch error.
 hipError_t launch_attention(const AttnArgs& a, int head_dim, int dtype, bool paged, int grid,
                             hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int head_dim, int dtype, int grid, int grid_y, hipStream_t stream);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
-// The per-head-dimension halves of launch_attention (separate translation units).
+hipError_t launch_kv_append_q8(const AppendQ8Args& a, int dtype, hipStream_t stream);
+// The attention kernel over 8-bit pages (page_size >= 16).
+hipError_t launch_attention_q8(const AttnArgs& a, int head_dim, int dtype, int grid, hipStream_t stream);
+
+// The per-head-dimension halves of launch_attention and launch_attention_q8
+// (separate translation units).
 hipError_t launch_attention_d64_d128(const AttnArgs& a, int head_dim, int dtype, bool paged, int grid,
                                      hipStream_t stream);
 hipError_t launch_attention_d256(const AttnArgs& a, int dtype, bool paged, int grid, hipStream_t stream);
+hipError_t launch_attention_q8_d64_d128(const AttnArgs& a, int head_dim, int dtype, int grid, hipStream_t stream);
+hipError_t launch_attention_q8_d256(const AttnArgs& a, int dtype, int grid, hipStream_t stream);
 
 }  // namespace ppa

@@ -36,7 +36,76 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
   }
 }
 
+// Quantizing append into 8-bit pages: one thread per 32-value block of a
+// token row (the q8_0 block structure named by the KVarN report's format
+// comparison).  The block's max |x| over 127, an fp32 division rounded once to
+// fp16 (saturated at 65504), is its scale; each value becomes x / scale (fp32
+// division) rounded to the nearest integer, ties to even, clamped to
+// [-127, 127]; an all-zero block has scale 0 and quants 0.  Every step is a
+// correctly rounded fp32 operation, so the result is reproducible bit for bit.
+template <bool BF>
+__global__ __launch_bounds__(256) void kv_append_q8_kernel(AppendQ8Args a) {
+  const int nb = a.head_dim / 32;
+  const int64_t per_tensor = int64_t(a.rows) * a.n_kv_heads * nb;   // blocks per tensor
+  const int64_t ps_mask = (int64_t(1) << a.log2_ps) - 1;
+  for (int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x; t < 2 * per_tensor; t += int64_t(gridDim.x) * 256) {
+    const bool is_v = t >= per_tensor;
+    const int64_t u = is_v ? t - per_tensor : t;
+    const int blk = int(u % nb);
+    const int64_t rh = u / nb;                 // row * Hkv + head
+    const int64_t row = rh / a.n_kv_heads;
+    const int head = int(rh % a.n_kv_heads);
+    const u32x4* src = reinterpret_cast<const u32x4*>((is_v ? a.v_new : a.k_new) + rh * a.head_dim + blk * 32);
+    float x[32];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const u32x4 w = src[k];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t bits = (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+        x[8 * k + e] = BF ? __uint_as_float(bits << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+      }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(x[e]));
+    _Float16 s16 = (_Float16)(amax / 127.0f);
+    if (!(s16 <= (_Float16)65504.0f)) s16 = (_Float16)65504.0f;
+    const float sf = (float)s16;
+    uint32_t qw[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float q = sf > 0.f ? rintf(x[4 * k + e] / sf) : 0.f;
+        q = fminf(fmaxf(q, -127.f), 127.f);
+        word |= (uint32_t)((int)q & 0xff) << (8 * e);
+      }
+      qw[k] = word;
+    }
+    const int64_t pos = a.history + row;
+    const int64_t page = a.bt[pos >> a.log2_ps];
+    const int64_t slot_row = ((page << a.log2_ps) + (pos & ps_mask)) * a.n_kv_heads + head;   // token-head row
+    u32x4* qdst = reinterpret_cast<u32x4*>((is_v ? a.v_quant : a.k_quant) + slot_row * a.head_dim + blk * 32);
+    qdst[0] = u32x4{qw[0], qw[1], qw[2], qw[3]};
+    qdst[1] = u32x4{qw[4], qw[5], qw[6], qw[7]};
+    (is_v ? a.v_scale : a.k_scale)[slot_row * nb + blk] = __builtin_bit_cast(uint16_t, s16);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_kv_append_q8(const AppendQ8Args& a, int dtype, hipStream_t stream) {
+  const int64_t blocks = 2 * int64_t(a.rows) * a.n_kv_heads * (a.head_dim / 32);
+  int64_t grid = (blocks + 255) / 256;
+  if (grid > 8192) grid = 8192;
+  if (dtype == 1)
+    hipLaunchKernelGGL(kv_append_q8_kernel<true>, dim3(uint32_t(grid)), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(kv_append_q8_kernel<false>, dim3(uint32_t(grid)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream) {
   const int64_t units = 2 * int64_t(a.rows) * a.upr;

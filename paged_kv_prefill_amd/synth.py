@@ -91,10 +91,11 @@ def make_case(name, history, rows, n_q_heads, n_kv_heads, head_dim, page_size, d
                 q, k_pages, v_pages, bt, k, v, piece_rows)
 
 
-def lay_out_pages(tokens, block_table, pool_pages, page_size):
-    """Scatter logical tokens [ctx][Hkv][d] into a NaN-poisoned page pool."""
+def lay_out_pages(tokens, block_table, pool_pages, page_size, fill=POISON):
+    """Scatter logical tokens [ctx][Hkv][...] into a page pool filled with
+    `fill` (for 16-bit data 0xFFFF, a NaN in fp16 and bf16)."""
     ctx = tokens.shape[0]
-    pages = np.full((pool_pages, page_size) + tokens.shape[1:], POISON, dtype=np.uint16)
+    pages = np.full((pool_pages, page_size) + tokens.shape[1:], fill, dtype=tokens.dtype)
     n_full = ctx // page_size
     if n_full:
         pages[block_table[:n_full]] = tokens[:n_full * page_size].reshape((n_full, page_size) + tokens.shape[1:])
@@ -200,3 +201,63 @@ def make_varlen_case(name, seqs, n_q_heads, n_kv_heads, head_dim, page_size, dty
     hist = np.array([h for h, _ in seqs], dtype=np.int64)
     return VarlenCase(name, list(seqs), n_q_heads, n_kv_heads, head_dim, page_size, dtype, q, k_pages, v_pages,
                       tables, cu, hist)
+
+
+
+@dataclass
+class Q8Case:
+    """A chunk over 8-bit K/V pages (see make_q8_case)."""
+    name: str
+    history: int
+    rows: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    page_size: int
+    dtype: str
+    q: np.ndarray          # [R][Hq][d] uint16 (fp16 or bf16 bits)
+    k_quant: np.ndarray    # [pool][ps][Hkv][d] int8
+    k_scale: np.ndarray    # [pool][ps][Hkv][d/32] uint16 (fp16 bits)
+    v_quant: np.ndarray
+    v_scale: np.ndarray
+    block_table: np.ndarray
+    piece_rows: int = 0
+
+
+def make_q8_case(name, history, rows, n_q_heads, n_kv_heads, head_dim, page_size, dtype, seed,
+                 table="permute", pool_pages=None, piece_rows=0):
+    """Q as in make_case; then per tensor K, V (logical token order) quants
+    uniform in [-127, 127] and fp16 scales 0.002 + 0.01 |N(0, 1)| per block
+    of 32 values (values of roughly unit spread); then the block table.  Pool
+    slots no token uses hold random quants under 0xFFFF scales (fp16 NaN), so
+    reading them poisons the result."""
+    rng = np.random.default_rng(seed)
+    ctx = history + rows
+    q = ENCODERS[dtype](rng.standard_normal((rows, n_q_heads, head_dim), dtype=np.float32))
+    nb = head_dim // 32
+    tensors = []
+    for _ in range(2):
+        quant = rng.integers(-127, 128, size=(ctx, n_kv_heads, head_dim), dtype=np.int8)
+        scale = (np.float32(0.002) + np.float32(0.01) * np.abs(rng.standard_normal((ctx, n_kv_heads, nb),
+                                                                                   dtype=np.float32)))
+        tensors.append((quant, scale.astype(np.float16).view(np.uint16)))
+    n_pages = -(-ctx // page_size)
+    if table == "permute":
+        pool = n_pages if pool_pages is None else pool_pages
+        bt = rng.permutation(pool)[:n_pages].astype(np.int32)
+    elif table == "scatter":
+        pool = pool_pages
+        bt = rng.choice(pool, size=n_pages, replace=False).astype(np.int32)
+    else:
+        raise ValueError(table)
+    out = []
+    for quant, scale in tensors:
+        qp = lay_out_pages(quant, bt, pool, page_size, fill=np.int8(0))
+        # unused slots: random quants, NaN scales
+        used = np.zeros((pool, page_size), dtype=bool)
+        j = np.arange(ctx)
+        used[bt[j // page_size], j % page_size] = True
+        qp[~used] = rng.integers(-127, 128, size=(int((~used).sum()), n_kv_heads, head_dim), dtype=np.int8)
+        out += [qp, lay_out_pages(scale, bt, pool, page_size)]
+    return Q8Case(name, history, rows, n_q_heads, n_kv_heads, head_dim, page_size, dtype, q, out[0], out[1],
+                  out[2], out[3], bt, piece_rows)

@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = pkg.lib()
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     for name in names:
         assert hasattr(lib, name), name
     assert lib.paged_prefill_version() == 10000
@@ -201,3 +201,45 @@ def test_varlen_plan_of_one_sequence_is_the_single_call_plan():
         a = pkg.paged_prefill_plan(h, r, 16, 2, 256)
         b = pkg.paged_prefill_plan_varlen(1, r, r, h + r, 16, 2, 256)
         assert a == b, (h, r, a, b)
+
+
+def _call_q8(**kw):
+    a = dict(q=16, kq=32, ks=48, vq=64, vs=80, bt=96, H=10, R=4, P=0, hq=4, hkv=2, d=64, ps=16, S=0, out=4096, dt=0)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return pkg.lib().paged_prefill_attention_q8(
+        vp(a["q"]), vp(a["kq"]), vp(a["ks"]), vp(a["vq"]), vp(a["vs"]), vp(a["bt"]), a["H"], a["R"], a["P"], a["hq"],
+        a["hkv"], a["d"], a["ps"], a["S"], vp(a["out"]), a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=2), -4), (dict(R=-1), -2), (dict(H=-1), -2), (dict(d=96), -3), (dict(ps=8), -3), (dict(ps=1), -3),
+    (dict(ps=12), -3), (dict(S=-1), -2), (dict(P=-1), -2), (dict(q=0), -1), (dict(ks=0), -1), (dict(vs=0), -1),
+    (dict(bt=0), -1), (dict(ks=50), -8), (dict(vq=72), -8), (dict(out=16 + 64), -9),
+])
+def test_q8_argument_errors_return_before_any_device_work(kw, code):
+    assert _call_q8(**kw) == code
+
+
+def test_empty_q8_chunk_is_a_no_op():
+    assert _call_q8(R=0, q=0, kq=0, ks=0, vq=0, vs=0, bt=0, out=0) == 0
+
+
+def _call_append_q8(**kw):
+    a = dict(kn=16, vn=32, kq=4096, ks=8192, vq=12288, vs=16384, bt=64, H=10, R=4, hkv=2, d=64, ps=16, dt=0)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return pkg.lib().paged_kv_append_q8(vp(a["kn"]), vp(a["vn"]), vp(a["kq"]), vp(a["ks"]), vp(a["vq"]), vp(a["vs"]),
+                                        vp(a["bt"]), a["H"], a["R"], a["hkv"], a["d"], a["ps"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=3), -4), (dict(R=-1), -2), (dict(d=32), -3), (dict(ps=3), -3), (dict(kn=0), -1), (dict(vs=0), -1),
+    (dict(bt=0), -1), (dict(ks=8200), -8), (dict(kq=8192), -9), (dict(vs=16), -9),
+])
+def test_append_q8_argument_errors_return_before_any_device_work(kw, code):
+    assert _call_append_q8(**kw) == code
+
+
+def test_empty_q8_append_is_a_no_op():
+    assert _call_append_q8(R=0, kn=0, vn=0, kq=0, ks=0, vq=0, vs=0, bt=0) == 0
