@@ -30,8 +30,12 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # device sources and their MFMA register form
 KERNEL_SOURCES = (
     ("attention.hip", "0"),
-    ("attention_d64_d128.hip", os.environ.get("PPA_MFMA_VGPR_FORM", "1")),
+    # head dims 64/128 with two query blocks per wave: only the AGPR form fits
+    ("attention_d64_d128.hip", os.environ.get("PPA_MFMA_VGPR_FORM_D128", "0")),
+    ("attention_d64_d128_qb1.hip", os.environ.get("PPA_MFMA_VGPR_FORM", "1")),
     ("attention_d256.hip", os.environ.get("PPA_MFMA_VGPR_FORM", "1")),
+    # the VGPR form's AGPR-rewrite pass crashes the compiler on these
+    ("attention_d256_small_pages.hip", "0"),
     # 8-bit pages: the widening step needs registers the VGPR form does not
     # leave at head dimension 256 (it spills there); the AGPR form does not spill
     ("attention_q8_d64_d128.hip", os.environ.get("PPA_MFMA_VGPR_FORM_Q8", "0")),

@@ -85,6 +85,7 @@ int run(const void* q, const void* k, const void* v, const int32_t* bt, bool pag
         int64_t history, int32_t rows, int32_t hq, int32_t hkv, int32_t d, int32_t ps,
         int32_t n_splits, void* out, int32_t dtype, hipStream_t stream, const Q8Scales* q8 = nullptr) {
   Shape shape{history, rows, hq, hkv, d, ps, dtype};
+  shape.q8 = q8 ? 1 : 0;
   int rc = check_shape(shape);
   if (rc != PPA_OK) return rc;
   if (n_splits < 0) return PPA_ERR_BAD_SHAPE;
@@ -144,6 +145,7 @@ int run(const void* q, const void* k, const void* v, const int32_t* bt, bool pag
   a.ws_rows = rows;
   a.k_scale = q8 ? static_cast<const uint16_t*>(q8->k) : nullptr;
   a.v_scale = q8 ? static_cast<const uint16_t*>(q8->v) : nullptr;
+  a.query_blocks = plan.m_tile / 128;
 
   const hipError_t le = q8 ? launch_attention_q8(a, d, dtype, plan.grid, stream)
                            : launch_attention(a, d, dtype, paged, plan.grid, stream);
@@ -259,6 +261,7 @@ int run_varlen(const void* q, const void* k, const void* v, const int32_t* bt, i
   a.ws_rows = total_rows;
   a.k_scale = nullptr;
   a.v_scale = nullptr;
+  a.query_blocks = plan.m_tile / 128;
 
   if (launch_attention(a, d, dtype, true, plan.grid, stream) != hipSuccess) return PPA_ERR_HIP;
   if (plan.n_splits > 1) {

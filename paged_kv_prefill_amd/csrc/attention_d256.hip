@@ -1,10 +1,14 @@
-// Split-partial attention kernels for head dimension 256.
+// Split-partial attention kernels for head dimension 256, contiguous K/V and
+// pages of 16 tokens or more (the smaller page classes are in
+// attention_d256_small_pages.hip, built with other register options).
 #include "attn_kernel.h"
 
 namespace ppa {
 
 hipError_t launch_attention_d256(const AttnArgs& a, int dtype, bool paged, int grid, hipStream_t stream) {
-  return dtype == 1 ? launch_attn_p<256, BF16>(a, paged, grid, stream) : launch_attn_p<256, F16>(a, paged, grid, stream);
+  if (paged && a.log2_ps < 4) return launch_attention_d256_small_pages(a, dtype, grid, stream);
+  return dtype == 1 ? launch_attn_p_large<256, BF16>(a, paged, grid, stream)
+                    : launch_attn_p_large<256, F16>(a, paged, grid, stream);
 }
 
 }  // namespace ppa

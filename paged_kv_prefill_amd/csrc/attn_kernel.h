@@ -111,6 +111,10 @@ struct BF16 {
 
 constexpr int kTK = 64;        // keys per tile
 constexpr int kWaves = 4;
+// QB: query blocks of 32 vectors per wave.  With 2 (head dimensions up to
+// 128), each K/V operand read and each loaded tile feed twice the MFMAs; the
+// planner picks it for calls with more than one 128-vector m tile, and its m
+// tile (query vectors per workgroup, 4 waves x 32 x QB) is the kernel's.
 constexpr float kNegInf = -__builtin_inff();
 
 template <int D>
@@ -208,13 +212,14 @@ constexpr float kRefMarginLog2 = 15.0f;
 // Q8: K and V pages hold 8-bit quants with an fp16 scale per 32 values along
 // d (see the q8 loader below); the tiles are widened to fp16 in LDS and the
 // MFMA, softmax and P arithmetic run in fp16 whatever the type of q and out.
-template <int D, class E, Addr AM, bool Q8 = false>
+template <int D, class E, Addr AM, bool Q8 = false, int QB = 1>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_partial_kernel(AttnArgs a) {
   static_assert(!Q8 || AM == Addr::Page16 || AM == Addr::PageBig, "8-bit pages need pages of 16 tokens or more");
   using Gm = Geom<D>;
   using M = std::conditional_t<Q8, F16, E>;   // element type of the MFMA operands
   using vec8 = typename M::vec8;
   constexpr int EB = Q8 ? 1 : 2;              // bytes per K/V element in memory
+  constexpr int MT = kWaves * 32 * QB;        // query vectors per workgroup
   constexpr int CH = Gm::CH;
   constexpr int LPW = Gm::LPW;
   constexpr int KS = D / 16;   // 16-wide d steps of QK
@@ -253,28 +258,37 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     a.rows = a.cu_rows[seq + 1] - r0;
     a.history = a.seq_history[seq];
     a.ctx = (int)a.history + a.rows;
-    if (mt * 128 >= a.rows * a.group || s * a.split_tokens >= a.ctx) return;
+    if (mt * MT >= a.rows * a.group || s * a.split_tokens >= a.ctx) return;
     a.q += (int64_t)r0 * a.n_q_heads * D;
     a.out += (int64_t)r0 * a.n_q_heads * D;
     a.bt += (int64_t)seq * a.bt_stride;
     ws_row0 = r0;
   }
 
+  // Query vector f = (row, head) pair of the head group, row-major; wave w
+  // holds blocks of 32 at mt MT + 32 (QB w + b), lane % 32 within the block.
   const int G = a.group;
   const int nqv = a.rows * G;
-  const int f = mt * 128 + wave * 32 + (lane & 31);
-  const bool qv_valid = f < nqv;
-  const int row = qv_valid ? f / G : a.rows - 1;
-  const int head = g * G + (qv_valid ? f % G : 0);
-  const int f_last = min(mt * 128 + 127, nqv - 1);
-  const int r_first = (mt * 128) / G;
+  bool qv_valid[QB];
+  int row[QB], head[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int f = mt * MT + 32 * (QB * wave + qb) + (lane & 31);
+    qv_valid[qb] = f < nqv;
+    row[qb] = qv_valid[qb] ? f / G : a.rows - 1;
+    head[qb] = g * G + (qv_valid[qb] ? f % G : 0);
+  }
+  const int f_last = min(mt * MT + MT - 1, nqv - 1);
+  const int r_first = (mt * MT) / G;
   const int r_last = f_last / G;
 
   const int k0 = s * a.split_tokens;
   const int k1 = min(k0 + a.split_tokens, a.ctx);
   const int kend = min(k1, (int)(a.history + r_last + 1));
   const int n_tiles = kend > k0 ? (kend - k0 + kTK - 1) / kTK : 0;
-  const int lim = (int)a.history + row;             // last key this query vector sees
+  int lim[QB];                                      // last key each query vector sees
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) lim[qb] = (int)a.history + row[qb];
   // Tiles ending at or before the first row's last key need no mask, and they
   // are whole (split bounds are multiples of the tile).  A body works on tile
   // it and loads tile it+1, so the fast body (no mask, no load clamp) runs
@@ -284,19 +298,20 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   const int n_fast = n_plain > 0 ? n_plain - 1 : 0;
 
   // Q fragments (B operand of QK): lane holds Q[f][16 ks + 8 h .. +7].
-  vec8 qf[KS];
-  {
-    const uint16_t* qp = a.q + ((int64_t)row * a.n_q_heads + head) * D + 8 * h;
+  vec8 qf[QB][KS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const uint16_t* qp = a.q + ((int64_t)row[qb] * a.n_q_heads + head[qb]) * D + 8 * h;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      u32x4 raw = qv_valid ? *(const u32x4*)(qp + 16 * ks) : u32x4{0u, 0u, 0u, 0u};
+      u32x4 raw = qv_valid[qb] ? *(const u32x4*)(qp + 16 * ks) : u32x4{0u, 0u, 0u, 0u};
       if constexpr (std::is_same_v<M, E>) {
-        qf[ks] = __builtin_bit_cast(vec8, raw);
+        qf[qb][ks] = __builtin_bit_cast(vec8, raw);
       } else {
         // bf16 q for the fp16 MFMA: exact for |q| in fp16's normal range
-        const bf16x8 qb = __builtin_bit_cast(bf16x8, raw);
+        const bf16x8 qbf = __builtin_bit_cast(bf16x8, raw);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qf[ks][e] = (_Float16)(float)qb[e];
+        for (int e = 0; e < 8; ++e) qf[qb][ks][e] = (_Float16)(float)qbf[e];
       }
     }
   }
@@ -305,10 +320,14 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   // iteration.
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
-  f32x16 o[DB];
-  float m_ref = kNegInf;  // softmax reference, scaled log2 domain
-  float m_true = kNegInf; // running max of the scaled scores
-  float l = 0.f;          // this lane's share of the softmax sum
+  f32x16 o[QB][DB];
+  float m_ref[QB], m_true[QB], l[QB];  // per query block:
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_ref[qb] = kNegInf;   // softmax reference, scaled log2 domain
+    m_true[qb] = kNegInf;  // running max of the scaled scores
+    l[qb] = 0.f;           // this lane's share of the softmax sum
+  }
   const float c = a.scale_log2;
 
   // ---- loader -------------------------------------------------------------
@@ -507,8 +526,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
   // ---- MFMA phases --------------------------------------------------------
   // S^T[key][qv] = K Q^T for the 64 keys of a tile: lane holds qv = lane & 31
-  // and keys 32 kb + 8 (r / 4) + 4 h + r % 4.
-  f32x16 sc[2];
+  // of each query block and keys 32 kb + 8 (r / 4) + 4 h + r % 4.  Each K
+  // operand read feeds the MFMAs of all QB query blocks.
+  f32x16 sc[QB][2];
   // lds_off(lane % 32 + 32 kb, 2 ks + h) = (kofs ^ (ks % 4) 32) + (ks / 4) 8192 + kb 4096
   const int kofs = ((lane >> 3) & 3) * 1024 + (lane & 7) * 128 + ((h ^ lds_g(lane & 15)) << 4);
   // The operand reads run QPF steps ahead of their MFMAs; sched_barrier pins
@@ -516,8 +536,11 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   // MFMA).
   auto qk = [&](const uint8_t* kt, auto&& step_hook) __attribute__((always_inline)) {
     constexpr int QPF = 3;
-    sc[0] = f32x16{};
-    sc[1] = f32x16{};
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      sc[qb][0] = f32x16{};
+      sc[qb][1] = f32x16{};
+    }
     i16x8 k0r[KS], k1r[KS];
     auto load = [&](int ks) __attribute__((always_inline)) {
       const uint8_t* kl = kt + (kofs ^ ((ks & 3) << 5));
@@ -530,8 +553,11 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (ks + QPF < KS) load(ks + QPF);
-      sc[0] = M::mfma(__builtin_bit_cast(vec8, k0r[ks]), qf[ks], sc[0]);
-      sc[1] = M::mfma(__builtin_bit_cast(vec8, k1r[ks]), qf[ks], sc[1]);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        sc[qb][0] = M::mfma(__builtin_bit_cast(vec8, k0r[ks]), qf[qb][ks], sc[qb][0]);
+        sc[qb][1] = M::mfma(__builtin_bit_cast(vec8, k1r[ks]), qf[qb][ks], sc[qb][1]);
+      }
       step_hook(ks);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -547,7 +573,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   // step i + VPF, one MFMA and a slice of the VALU work; sched_barrier pins
   // the interleave.  The two halves are independent: PV reads pb, softmax
   // writes pb_new.
-  vec8 pb[4], pb_new[4];
+  vec8 pb[QB][4], pb_new[QB][4];
   // lds_off(16 kstep + vr (+ 8), 4 db + cc) + within = (vofs1 (vofs2) ^ (db % 2) 64)
   // + (db / 2) 8192 + kstep 2048, vr = 4 h + (lane % 16) / 4, cc = 2 ((lane / 16) % 2) + (lane % 4) / 2
   const int v_r = 4 * h + ((lane & 15) >> 2);
@@ -565,37 +591,51 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
       vlo[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vt + (vofs1 ^ ((db & 1) << 6)) + imm));
       vhi[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vt + (vofs2 ^ ((db & 1) << 6)) + imm));
     };
-    // VALU work: max over the 32 scores (MAX_STEPS steps), then 32 weights.
+    // VALU work: max over the lane's 32 QB scores (MAX_STEPS steps, each within
+    // one query block), then their weights.  Element e is score e % 32 of
+    // block e / 32 (kstep-major, 8 per pb entry).
+    constexpr int ET = 32 * QB;
+    constexpr int PER = ET / MAX_STEPS;
+    static_assert(32 % PER == 0, "a max step stays within one query block");
+    auto elem = [&](int e) __attribute__((always_inline)) -> float { return sc[e >> 5][(e >> 4) & 1][e & 15]; };
     float part[MAX_STEPS];
-    float base = 0.f, rs = 0.f, p32[32];
+    float base[QB], rs[QB], p32[ET];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      base[qb] = 0.f;
+      rs[qb] = 0.f;
+    }
     auto valu = [&](int i) __attribute__((always_inline)) {
       if (i < MAX_STEPS) {
-        constexpr int PER = 32 / MAX_STEPS;
-        float mx = sc[(i * PER) >> 4][(i * PER) & 15];
+        float mx = elem(i * PER);
 #pragma unroll
-        for (int e = 1; e < PER; ++e) mx = fmaxf(mx, sc[(i * PER + e) >> 4][(i * PER + e) & 15]);
+        for (int e = 1; e < PER; ++e) mx = fmaxf(mx, elem(i * PER + e));
         part[i] = mx;
         if (i == MAX_STEPS - 1) {
-          float m = part[0];
 #pragma unroll
-          for (int j = 1; j < MAX_STEPS; ++j) m = fmaxf(m, part[j]);
-          const float mxs = max_with_partner(m) * c;
-          m_true = fmaxf(m_true, mxs);
-          if (m_ref == kNegInf) m_ref = mxs;  // first tile with a visible key (O and l are still 0)
-          base = m_ref == kNegInf ? 0.f : m_ref;
+          for (int qb = 0; qb < QB; ++qb) {
+            constexpr int SPB = MAX_STEPS / QB;   // max steps per block
+            float m = part[qb * SPB];
+#pragma unroll
+            for (int j = 1; j < SPB; ++j) m = fmaxf(m, part[qb * SPB + j]);
+            const float mxs = max_with_partner(m) * c;
+            m_true[qb] = fmaxf(m_true[qb], mxs);
+            if (m_ref[qb] == kNegInf) m_ref[qb] = mxs;  // first tile with a visible key (O and l are still 0)
+            base[qb] = m_ref[qb] == kNegInf ? 0.f : m_ref[qb];
+          }
         }
         return;
       }
-      // weights of elements [e0, e1) of the 32 (kstep-major, 8 per pb entry)
+      // weights of elements [e0, e1)
       const int n = NPV - MAX_STEPS;
-      const int e0 = ((i - MAX_STEPS) * 32) / n, e1 = ((i - MAX_STEPS + 1) * 32) / n;
+      const int e0 = ((i - MAX_STEPS) * ET) / n, e1 = ((i - MAX_STEPS + 1) * ET) / n;
 #pragma unroll
       for (int e = e0; e < e1; ++e) {
-        p32[e] = __builtin_amdgcn_exp2f(fmaf(sc[e >> 4][e & 15], c, -base));
+        p32[e] = __builtin_amdgcn_exp2f(fmaf(elem(e), c, -base[e >> 5]));
         if ((e & 7) == 7) {
           // The sum takes the rounded weights, the ones the PV product uses.
-          pb_new[e >> 3] = M::from_f32(p32 + (e & ~7));
-          rs = M::sum8(pb_new[e >> 3], rs);
+          pb_new[e >> 5][(e >> 3) & 3] = M::from_f32(p32 + (e & ~7));
+          rs[e >> 5] = M::sum8(pb_new[e >> 5][(e >> 3) & 3], rs[e >> 5]);
         }
       }
     };
@@ -606,14 +646,18 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
       if (i + VPF < NPV) load(i + VPF);
       const int kstep = i / DB, db = i % DB;
       i16x8 av = __builtin_shufflevector(vlo[i], vhi[i], 0, 1, 2, 3, 4, 5, 6, 7);
-      o[db] = M::mfma(__builtin_bit_cast(vec8, av), pb[kstep], o[db]);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) o[qb][db] = M::mfma(__builtin_bit_cast(vec8, av), pb[qb][kstep], o[qb][db]);
       valu(i);
       step_hook(i);
       __builtin_amdgcn_sched_barrier(0);
     }
-    l += rs;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) pb[k] = pb_new[k];
+    for (int qb = 0; qb < QB; ++qb) {
+      l[qb] += rs[qb];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) pb[qb][k] = pb_new[qb][k];
+    }
   };
 
   // PV of the last tile (no softmax left to overlap).
@@ -626,7 +670,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vt + (vofs1 ^ ((db & 1) << 6)) + imm));
         i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vt + (vofs2 ^ ((db & 1) << 6)) + imm));
         i16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[db] = M::mfma(__builtin_bit_cast(vec8, av), pb[kstep], o[db]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) o[qb][db] = M::mfma(__builtin_bit_cast(vec8, av), pb[qb][kstep], o[qb][db]);
       }
   };
 
@@ -682,14 +727,17 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
       }
     });
     if constexpr (MASKED) {
-      const int rel = lim - t0;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int qb = 0; qb < QB; ++qb) {
+        const int rel = lim[qb] - t0;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-          sc[kb][r] = key > rel ? kNegInf : sc[kb][r];
-        }
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+            sc[qb][kb][r] = key > rel ? kNegInf : sc[qb][kb][r];
+          }
+      }
     }
     // Now in flight: V(it-1), then K(it+1).  Wait for V(it-1), which the PV
     // below reads, so that its load latency hides behind the QK phase.
@@ -741,10 +789,13 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   __shared__ int wg_redo[kWaves];
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+    for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-    for (int kstep = 0; kstep < 4; ++kstep) pb[kstep] = vec8{};
-    l = 0.f;
+      for (int db = 0; db < DB; ++db) o[qb][db] = f32x16{};
+#pragma unroll
+      for (int kstep = 0; kstep < 4; ++kstep) pb[qb][kstep] = vec8{};
+      l[qb] = 0.f;
+    }
     for (int i = tid; i < Gm::TILE_BYTES / 16; i += 256) *LDS_PTR(u32x4, vbuf1 + i * 16) = u32x4{0u, 0u, 0u, 0u};
     if (n_tiles > 0) {
       pg0 = pages(0);
@@ -773,65 +824,89 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     }
     if (pass == 1) break;
     // Did any query vector of the workgroup outgrow its reference?
-    const bool redo = __ballot(m_true > m_ref + kRefMarginLog2) != 0;
+    bool outgrown = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) outgrown |= m_true[qb] > m_ref[qb] + kRefMarginLog2;
+    const bool redo = __ballot(outgrown) != 0;
     if (lane == 0) wg_redo[wave] = redo;
     __syncthreads();
     const bool any = wg_redo[0] | wg_redo[1] | wg_redo[2] | wg_redo[3];
     __syncthreads();
     if (!any) break;
-    m_ref = m_true;  // the exact max: every weight is at most 1 now
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) m_ref[qb] = m_true[qb];  // the exact max: every weight is at most 1 now
   }
 
   // Epilogue: combine the two lanes' sums; lane holds d = 32 db + 8 q + 4 h + 0..3.
-  const float l_tot = sum_with_partner(l);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (!qv_valid) return;
-  const int64_t pair = (int64_t)row * a.n_q_heads + head;
-  if (a.n_splits == 1) {
-    uint16_t* op = a.out + pair * D + 4 * h;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = sum_with_partner(l[qb]);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (!qv_valid[qb]) continue;
+    const int64_t pair = (int64_t)row[qb] * a.n_q_heads + head[qb];
+    if (a.n_splits == 1) {
+      uint16_t* op = a.out + pair * D + 4 * h;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const uint32_t lo = E::bits(o[db][4 * q4 + 0] * inv) | ((uint32_t)E::bits(o[db][4 * q4 + 1] * inv) << 16);
-        const uint32_t hi = E::bits(o[db][4 * q4 + 2] * inv) | ((uint32_t)E::bits(o[db][4 * q4 + 3] * inv) << 16);
-        *(u32x2*)(op + 32 * db + 8 * q4) = u32x2{lo, hi};
-      }
-  } else {
-    const int64_t pairs = (int64_t)a.ws_rows * a.n_q_heads;
-    const int64_t wpair = pair + (int64_t)ws_row0 * a.n_q_heads;
-    float* wp = a.ws_o + ((int64_t)s * pairs + wpair) * D + 4 * h;
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x16& ov = o[qb][db];
+          const uint32_t lo = E::bits(ov[4 * q4 + 0] * inv) | ((uint32_t)E::bits(ov[4 * q4 + 1] * inv) << 16);
+          const uint32_t hi = E::bits(ov[4 * q4 + 2] * inv) | ((uint32_t)E::bits(ov[4 * q4 + 3] * inv) << 16);
+          *(u32x2*)(op + 32 * db + 8 * q4) = u32x2{lo, hi};
+        }
+    } else {
+      const int64_t pairs = (int64_t)a.ws_rows * a.n_q_heads;
+      const int64_t wpair = pair + (int64_t)ws_row0 * a.n_q_heads;
+      float* wp = a.ws_o + ((int64_t)s * pairs + wpair) * D + 4 * h;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        f32x4 v4 = {o[db][4 * q4 + 0] * inv, o[db][4 * q4 + 1] * inv, o[db][4 * q4 + 2] * inv,
-                    o[db][4 * q4 + 3] * inv};
-        *(f32x4*)(wp + 32 * db + 8 * q4) = v4;
-      }
-    if (h == 0) a.ws_lse[(int64_t)s * pairs + wpair] = l_tot > 0.f ? m_ref + log2f(l_tot) : kNegInf;
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x16& ov = o[qb][db];
+          f32x4 v4 = {ov[4 * q4 + 0] * inv, ov[4 * q4 + 1] * inv, ov[4 * q4 + 2] * inv, ov[4 * q4 + 3] * inv};
+          *(f32x4*)(wp + 32 * db + 8 * q4) = v4;
+        }
+      if (h == 0) a.ws_lse[(int64_t)s * pairs + wpair] = l_tot > 0.f ? m_ref[qb] + log2f(l_tot) : kNegInf;
+    }
   }
 }
 
-template <int D, class E, Addr AM, bool Q8 = false>
+template <int D, class E, Addr AM, bool Q8 = false, int QB = 1>
 hipError_t launch_attn_t(const AttnArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_partial_kernel<D, E, AM, Q8>), dim3(grid), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((attn_partial_kernel<D, E, AM, Q8, QB>), dim3(grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 // 8-bit pages: 16 tokens per page or more (the host checks).
-template <int D, class E>
+template <int D, class E, int QB = 1>
 hipError_t launch_attn_q8(const AttnArgs& a, int grid, hipStream_t stream) {
-  if (a.log2_ps >= 6) return launch_attn_t<D, E, Addr::PageBig, true>(a, grid, stream);
-  if (a.log2_ps >= 4) return launch_attn_t<D, E, Addr::Page16, true>(a, grid, stream);
+  if (a.log2_ps >= 6) return launch_attn_t<D, E, Addr::PageBig, true, QB>(a, grid, stream);
+  if (a.log2_ps >= 4) return launch_attn_t<D, E, Addr::Page16, true, QB>(a, grid, stream);
   return hipErrorInvalidValue;
 }
 
-template <int D, class E>
+// Every addressing class: contiguous K/V, then pages by size.
+template <int D, class E, int QB = 1>
 hipError_t launch_attn_p(const AttnArgs& a, bool paged, int grid, hipStream_t stream) {
+  if (!paged) return launch_attn_t<D, E, Addr::Contig, false, QB>(a, grid, stream);
+  if (a.log2_ps >= 6) return launch_attn_t<D, E, Addr::PageBig, false, QB>(a, grid, stream);
+  if (a.log2_ps >= 4) return launch_attn_t<D, E, Addr::Page16, false, QB>(a, grid, stream);
+  if (a.log2_ps == 3) return launch_attn_t<D, E, Addr::Page8, false, QB>(a, grid, stream);
+  return launch_attn_t<D, E, Addr::PageLane, false, QB>(a, grid, stream);
+}
+
+// Contiguous K/V or pages of 16 tokens or more.
+template <int D, class E>
+hipError_t launch_attn_p_large(const AttnArgs& a, bool paged, int grid, hipStream_t stream) {
   if (!paged) return launch_attn_t<D, E, Addr::Contig>(a, grid, stream);
   if (a.log2_ps >= 6) return launch_attn_t<D, E, Addr::PageBig>(a, grid, stream);
-  if (a.log2_ps >= 4) return launch_attn_t<D, E, Addr::Page16>(a, grid, stream);
+  return launch_attn_t<D, E, Addr::Page16>(a, grid, stream);
+}
+
+// Pages of fewer than 16 tokens.
+template <int D, class E>
+hipError_t launch_attn_p_small(const AttnArgs& a, int grid, hipStream_t stream) {
   if (a.log2_ps == 3) return launch_attn_t<D, E, Addr::Page8>(a, grid, stream);
   return launch_attn_t<D, E, Addr::PageLane>(a, grid, stream);
 }

@@ -41,6 +41,7 @@ struct AttnArgs {
   // their fp16 scales [pool][ps][Hkv][D / 32] (one per 32 values along D).
   const uint16_t* k_scale;
   const uint16_t* v_scale;
+  int32_t query_blocks;    // 32-vector query blocks per wave (m tile / 128): 1 or 2
 };
 
 struct MergeArgs {
@@ -103,6 +104,9 @@ hipError_t launch_attention_q8(const AttnArgs& a, int head_dim, int dtype, int g
 hipError_t launch_attention_d64_d128(const AttnArgs& a, int head_dim, int dtype, bool paged, int grid,
                                      hipStream_t stream);
 hipError_t launch_attention_d256(const AttnArgs& a, int dtype, bool paged, int grid, hipStream_t stream);
+hipError_t launch_attention_d256_small_pages(const AttnArgs& a, int dtype, int grid, hipStream_t stream);
+hipError_t launch_attention_d64_d128_qb1(const AttnArgs& a, int head_dim, int dtype, bool paged, int grid,
+                                         hipStream_t stream);
 hipError_t launch_attention_q8_d64_d128(const AttnArgs& a, int head_dim, int dtype, int grid, hipStream_t stream);
 hipError_t launch_attention_q8_d256(const AttnArgs& a, int dtype, int grid, hipStream_t stream);
 

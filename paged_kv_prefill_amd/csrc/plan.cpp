@@ -64,10 +64,11 @@ static int plan_launch(const Shape& s, int64_t ctx, int64_t rule_tiles, int64_t 
   const int32_t group = s.n_q_heads / s.n_kv_heads;
   const int32_t unit = s.page_size > kKvTile ? s.page_size : kKvTile;
   const int64_t n_units = (ctx + unit - 1) / unit;
-  const int64_t tiles_m = (grid_rows * group + kMTile - 1) / kMTile;
+  const int32_t mt = m_tile_for(s.head_dim, s.q8 != 0, grid_rows * group);
+  const int64_t tiles_m = (grid_rows * group + mt - 1) / mt;
   int64_t splits;
   if (n_splits_req <= 0) {
-    const int32_t cap = int32_t((int64_t(kChunkRowsForCap) * group + kMTile - 1) / kMTile);
+    const int32_t cap = int32_t((int64_t(kChunkRowsForCap) * group + mt - 1) / mt);
     const int64_t t = rule_tiles < 1 ? 1 : rule_tiles > cap ? cap : rule_tiles;
     splits = split_rule(kNumCUs, s.n_kv_heads, int32_t(t), kWgPerCu, 1, cap, kMaxSplits);
   } else {
@@ -82,7 +83,7 @@ static int plan_launch(const Shape& s, int64_t ctx, int64_t rule_tiles, int64_t 
   if (split_tokens >= (int64_t(1) << 31)) return PPA_ERR_TOO_LARGE;
   out->n_splits = int32_t(n_eff);
   out->split_tokens = int32_t(split_tokens);
-  out->m_tile = kMTile;
+  out->m_tile = mt;
   out->kv_tile = kKvTile;
   out->tiles_m = int32_t(tiles_m);
   const int64_t grid = tiles_m * s.n_kv_heads * n_eff * n_seqs;
@@ -109,12 +110,15 @@ static int plan_launch(const Shape& s, int64_t ctx, int64_t rule_tiles, int64_t 
   return PPA_OK;
 }
 
-static int64_t m_tiles(int64_t rows, const Shape& s) {
-  return (rows * (s.n_q_heads / s.n_kv_heads) + kMTile - 1) / kMTile;
+// m tiles of `rows` rows with the m tile a launch of `grid_rows` rows uses
+static int64_t m_tiles(int64_t rows, int64_t grid_rows, const Shape& s) {
+  const int64_t group = s.n_q_heads / s.n_kv_heads;
+  const int32_t mt = m_tile_for(s.head_dim, s.q8 != 0, grid_rows * group);
+  return (rows * group + mt - 1) / mt;
 }
 
 int make_plan(const Shape& s, int32_t n_splits_req, int64_t max_ws_bytes, ppa_plan* out) {
-  return plan_launch(s, s.history + s.rows, m_tiles(s.rows, s), s.rows, s.rows, 1, n_splits_req,
+  return plan_launch(s, s.history + s.rows, m_tiles(s.rows, s.rows, s), s.rows, s.rows, 1, n_splits_req,
                      max_ws_bytes, out);
 }
 
@@ -122,7 +126,7 @@ int make_plan_varlen(const Shape& s, int32_t n_seqs, int32_t max_rows, int64_t m
                      int32_t n_splits_req, int64_t max_ws_bytes, ppa_plan* out) {
   // Every sequence with rows has at least one m tile of its own, and at most
   // total_rows sequences have rows: the split rule counts at least that many.
-  int64_t tiles = m_tiles(s.rows, s);
+  int64_t tiles = m_tiles(s.rows, max_rows, s);
   const int64_t nonempty = n_seqs < s.rows ? n_seqs : s.rows;
   if (tiles < nonempty) tiles = nonempty;
   return plan_launch(s, max_context, tiles, max_rows, s.rows, n_seqs, n_splits_req, max_ws_bytes,

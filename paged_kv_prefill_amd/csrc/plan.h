@@ -8,7 +8,14 @@
 namespace ppa {
 
 // Work decomposition of the attention kernel (fixed by the kernel design).
-constexpr int kMTile = 128;      // query vectors per workgroup (4 waves x 32)
+// Query vectors per workgroup: 4 waves x 32 x query blocks per wave.  Two
+// blocks for head_dim <= 128 (not for 8-bit pages at 128) when the call has
+// more query vectors (rows x heads per KV head) than one 128-vector tile,
+// else one; the attention kernel is built for both.
+constexpr int m_tile_for(int head_dim, bool q8, int64_t query_vectors) {
+  const bool two = head_dim <= 64 || (head_dim <= 128 && !q8);
+  return two && query_vectors > 128 ? 256 : 128;
+}
 constexpr int kKvTile = 64;      // keys per inner-loop tile
 constexpr int kThreads = 256;    // threads per workgroup
 constexpr int kNumCUs = 256;     // MI355X compute units
@@ -19,6 +26,7 @@ constexpr int kChunkRowsForCap = 2048;  // the cap: tile slots of a full 2048-ro
 struct Shape {
   int64_t history;
   int32_t rows, n_q_heads, n_kv_heads, head_dim, page_size, dtype;
+  int32_t q8 = 0;  // 8-bit K/V pages (changes the m tile at head_dim 128)
 };
 
 // Shape checks shared by every entry point (no pointers).

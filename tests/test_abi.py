@@ -54,9 +54,10 @@ def test_plan_matches_the_workloads():
     # 2048-row chunk, 16/2 heads, d 256: 128 m-tiles x 2 KV heads fill 256 CUs with one split
     p = pkg.paged_prefill_plan(32768, 2048, 16, 2, 256)
     assert p["n_splits"] == 1 and p["grid"] == 256 and p["workspace_bytes"] == 0
-    # 256-row piece, 32/4 heads, d 128: 16 m-tiles x 4 heads -> 4 splits
+    # 256-row piece, 32/4 heads, d 128: 256-vector m tiles (two query blocks per
+    # wave), 8 m-tiles x 4 heads -> 8 splits
     p = pkg.paged_prefill_plan(65536, 256, 32, 4, 128)
-    assert p["n_splits"] == 4 and p["grid"] == 256
+    assert p["m_tile"] == 256 and p["n_splits"] == 8 and p["grid"] == 256
     # 128-row piece, 16/2 heads, d 256 at 128K: 8 x 2 -> 16 splits, the PR's count at 128K
     p = pkg.paged_prefill_plan(131072, 128, 16, 2, 256)
     assert p["n_splits"] == 16 and p["grid"] == 256
@@ -76,7 +77,10 @@ def test_plan_invariants(history, rows, hq, hkv, d, ps, req):
     assert 1 <= p["n_splits"] <= 64
     # the splits cover [0, ctx) and none is empty
     assert (p["n_splits"] - 1) * p["split_tokens"] < ctx <= p["n_splits"] * p["split_tokens"]
-    assert p["tiles_m"] == -(-rows * (hq // hkv) // 128)
+    # two query blocks per wave (256-vector m tiles) at d <= 128 once the call
+    # has more query vectors than one 128-vector tile
+    assert p["m_tile"] == (256 if d <= 128 and rows * (hq // hkv) > 128 else 128)
+    assert p["tiles_m"] == -(-rows * (hq // hkv) // p["m_tile"])
     assert p["grid"] == p["tiles_m"] * hkv * p["n_splits"]
     if req:
         assert p["n_splits"] <= max(1, min(req, -(-ctx // unit)))
@@ -180,14 +184,14 @@ def test_empty_varlen_batches_are_no_ops():
 def test_varlen_plan_invariants(n, total, max_rows, max_ctx, hq, hkv, d, ps, req):
     p = pkg.paged_prefill_plan_varlen(n, total, max_rows, max_ctx, hq, hkv, d, ps, req)
     g = hq // hkv
-    assert p["tiles_m"] == -(-max_rows * g // 128)
+    assert p["tiles_m"] == -(-max_rows * g // p["m_tile"])
     assert p["grid"] == n * p["tiles_m"] * hkv * p["n_splits"]
     assert p["split_tokens"] % max(64, ps) == 0
     assert p["n_splits"] * p["split_tokens"] >= max_ctx > (p["n_splits"] - 1) * p["split_tokens"]
     if req == 0:
         # the split rule counts at least one m tile per sequence: a batch of
         # decode rows does not get a one-sequence split count
-        tiles = max(-(-total * g // 128), min(n, total))
+        tiles = max(-(-total * g // p["m_tile"]), min(n, total))
         assert p["n_splits"] <= max(1, (256 // hkv) // tiles)
     if p["n_splits"] > 1:
         assert p["workspace_bytes"] >= p["n_splits"] * total * hq * (d + 1) * 4
