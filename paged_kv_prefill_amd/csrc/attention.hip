@@ -5,27 +5,26 @@
 namespace ppa {
 namespace {
 
-// Log-sum-exp merge of split partials.  A (row, head) pair is served by
-// kMergeGroups groups of D/4 threads, 4 output elements per thread; group g
-// sums its own contiguous quarter of the pair's splits, so that a pair with
-// many splits (a decode step or a short append on a long history) has four
-// waves' worth of loads in flight instead of one thread walking every split.
+// Log-sum-exp merge of split partials.  A (row, head) pair is served by GR
+// groups of D/4 threads, 4 output elements per thread; group g sums its own
+// contiguous share of the pair's splits.  GR = 4 for 16 splits or more (a
+// decode step or a short append on a long history: four times the loads in
+// flight per pair instead of one thread walking every split), GR = 1 below
+// (many pairs, few splits: no cross-group exchange).
 // Each thread keeps 8 splits' loads in flight.  The weights are
 // exp2(lse_s - M) with M the pair's max lse; within a group the splits are
 // summed in index order, then the groups in index order: the order is fixed,
 // so results are reproducible.  Splits that start past the row's last key
 // hold nothing for it and are not read.
-constexpr int kMergeGroups = 4;
-
-template <int D, class E>
+template <int D, class E, int GR>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   constexpr int TPP = D / 4;                      // threads per (pair, group)
-  constexpr int TPAIR = TPP * kMergeGroups;       // threads per pair
+  constexpr int TPAIR = TPP * GR;                 // threads per pair
   constexpr int PPB = 256 / TPAIR;                // pairs per block
   constexpr int WPP = TPAIR >= 64 ? TPAIR / 64 : 1;  // waves per pair
   __shared__ float mx_part[PPB][WPP];
-  __shared__ f32x4 acc_part[PPB][kMergeGroups][TPP];
-  __shared__ float w_part[PPB][kMergeGroups];
+  __shared__ f32x4 acc_part[PPB][GR][TPP];
+  __shared__ float w_part[PPB][GR];
 
   // The sequence (grid y with several sequences): its first row in the
   // workspace and output, its rows and history.
@@ -65,7 +64,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   for (int w = 1; w < WPP; ++w) mx = fmaxf(mx, mx_part[pl][w]);
 
   // This group's splits [sb, se).
-  const int per = (nv + kMergeGroups - 1) / kMergeGroups;
+  const int per = (nv + GR - 1) / GR;
   const int sb = min(grp * per, nv);
   const int se = min(sb + per, nv);
   const float* op = a.ws_o + pair * D + 4 * t;
@@ -97,7 +96,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   acc = acc_part[pl][0][t];
   wsum = w_part[pl][0];
 #pragma unroll
-  for (int g = 1; g < kMergeGroups; ++g) {
+  for (int g = 1; g < GR; ++g) {
     acc += acc_part[pl][g][t];
     wsum += w_part[pl][g];
   }
@@ -110,10 +109,20 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 template <class E>
 hipError_t launch_merge_d(const MergeArgs& a, int head_dim, int grid, int grid_y, hipStream_t stream) {
   const dim3 g(grid, grid_y);
+  const bool four = merge_groups_for(a.n_splits) == 4;
   switch (head_dim) {
-    case 64: hipLaunchKernelGGL((merge_kernel<64, E>), g, dim3(256), 0, stream, a); break;
-    case 128: hipLaunchKernelGGL((merge_kernel<128, E>), g, dim3(256), 0, stream, a); break;
-    case 256: hipLaunchKernelGGL((merge_kernel<256, E>), g, dim3(256), 0, stream, a); break;
+    case 64:
+      if (four) hipLaunchKernelGGL((merge_kernel<64, E, 4>), g, dim3(256), 0, stream, a);
+      else hipLaunchKernelGGL((merge_kernel<64, E, 1>), g, dim3(256), 0, stream, a);
+      break;
+    case 128:
+      if (four) hipLaunchKernelGGL((merge_kernel<128, E, 4>), g, dim3(256), 0, stream, a);
+      else hipLaunchKernelGGL((merge_kernel<128, E, 1>), g, dim3(256), 0, stream, a);
+      break;
+    case 256:
+      if (four) hipLaunchKernelGGL((merge_kernel<256, E, 4>), g, dim3(256), 0, stream, a);
+      else hipLaunchKernelGGL((merge_kernel<256, E, 1>), g, dim3(256), 0, stream, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

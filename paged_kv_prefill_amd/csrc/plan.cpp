@@ -97,9 +97,10 @@ static int plan_launch(const Shape& s, int64_t ctx, int64_t rule_tiles, int64_t 
     const int64_t o_bytes = (o_elems * 4 + 255) / 256 * 256;
     const int64_t lse_bytes = (n_eff * pairs * 4 + 255) / 256 * 256;
     out->workspace_bytes = o_bytes + lse_bytes;
-    // the merge kernel: 4 groups of head_dim / 4 threads per pair; with
-    // several sequences one row of blocks per sequence
-    const int threads_per_pair = s.head_dim;
+    // the merge kernel: groups of head_dim / 4 threads per pair (4 groups for
+    // 16 splits or more, else 1); with several sequences one row of blocks per
+    // sequence
+    const int threads_per_pair = s.head_dim / 4 * (n_eff >= 16 ? 4 : 1);
     const int pairs_per_block = kThreads / threads_per_pair;
     out->merge_grid = int32_t((grid_rows * s.n_q_heads + pairs_per_block - 1) / pairs_per_block * n_seqs);
     if (n_splits_req > 0 && out->workspace_bytes > max_ws_bytes) return PPA_ERR_WORKSPACE;

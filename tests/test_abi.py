@@ -86,7 +86,8 @@ def test_plan_invariants(history, rows, hq, hkv, d, ps, req):
         assert p["n_splits"] <= max(1, min(req, -(-ctx // unit)))
     if p["n_splits"] > 1:
         assert p["workspace_bytes"] >= p["n_splits"] * rows * hq * (d + 1) * 4
-        assert p["merge_grid"] * (256 // d) >= rows * hq
+        groups = 4 if p["n_splits"] >= 16 else 1
+        assert p["merge_grid"] == -(-rows * hq // (256 // (d // 4 * groups)))
     else:
         assert p["workspace_bytes"] == 0 and p["merge_grid"] == 0
 
@@ -195,7 +196,8 @@ def test_varlen_plan_invariants(n, total, max_rows, max_ctx, hq, hkv, d, ps, req
         assert p["n_splits"] <= max(1, (256 // hkv) // tiles)
     if p["n_splits"] > 1:
         assert p["workspace_bytes"] >= p["n_splits"] * total * hq * (d + 1) * 4
-        assert p["merge_grid"] == -(-max_rows * hq // (256 // d)) * n
+        groups = 4 if p["n_splits"] >= 16 else 1
+        assert p["merge_grid"] == -(-max_rows * hq // (256 // (d // 4 * groups))) * n
     else:
         assert p["workspace_bytes"] == 0 and p["merge_grid"] == 0
 
