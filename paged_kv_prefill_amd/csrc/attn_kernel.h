@@ -1,9 +1,8 @@
 // Device code of the split-partial attention kernel, included by the
-// translation units that instantiate it for each head dimension (they are
-// compiled with their own register-allocation options).
-//
-// Chunked prefill attention over a paged KV cache: the split-partial kernel
-// and the log-sum-exp merge kernel, written for gfx950 (CDNA4, wave64).
+// translation units that instantiate it per head dimension, query blocks per
+// wave, page class and K/V format (they are compiled with their own
+// register-allocation options).  The log-sum-exp merge kernel is in
+// attention.hip.  Written for gfx950 (CDNA4, wave64).
 //
 // What is computed (issue "Metal: paged-KV prefill is 4.43x slower than
 // contiguous KV at 32K"; PR "perf: scale prefill attention splits with GPU
@@ -16,10 +15,12 @@
 // history and block-table row over one page pool: each workgroup then first
 // finds its sequence (see AttnArgs) and otherwise runs unchanged.
 //
-// Workgroup = 4 waves = 128 query vectors of one KV head.  A query vector is
-// one (row, head) pair of the head group, flattened row-major, so the G heads
-// of a row share a causal limit and every K/V byte staged in LDS serves
-// 128 queries.  Per 64-key tile:
+// Workgroup = 4 waves = 128 query vectors of one KV head (256 with two query
+// blocks per wave, QB = 2).  A query vector is one (row, head) pair of the
+// head group, flattened row-major, so the G heads of a row share a causal
+// limit and every K/V byte staged in LDS serves 128 (256) queries.  K/V pages
+// hold 16-bit values, or 8-bit quants with per-32-value scales (Q8) that are
+// widened to fp16 in LDS.  Per 64-key tile:
 //   * K and V rows stream from memory straight into LDS with 16-byte
 //     buffer_load ... lds (no VGPR staging), double-buffered: K of the next
 //     tile and V of this one load while this tile's QK and the previous
