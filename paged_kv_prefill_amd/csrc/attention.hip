@@ -1,6 +1,7 @@
 // The log-sum-exp merge kernel and the dispatch of both kernels by head
 // dimension and element type.
 #include "attn_kernel.h"
+#include "plan.h"
 
 namespace ppa {
 namespace {

@@ -90,10 +90,6 @@ struct AppendQ8Args {
   int32_t log2_ps;
 };
 
-// Thread groups per (row, head) pair in the merge kernel: 4 for 16 splits or
-// more, else 1 (the planner sizes the merge grid with the same rule).
-constexpr int merge_groups_for(int n_splits) { return n_splits >= 16 ? 4 : 1; }
-
 // dtype: 0 = fp16, 1 = bf16.  Returns hipSuccess or the launch error.
 hipError_t launch_attention(const AttnArgs& a, int head_dim, int dtype, bool paged, int grid,
                             hipStream_t stream);

@@ -100,7 +100,7 @@ static int plan_launch(const Shape& s, int64_t ctx, int64_t rule_tiles, int64_t 
     // the merge kernel: groups of head_dim / 4 threads per pair (4 groups for
     // 16 splits or more, else 1); with several sequences one row of blocks per
     // sequence
-    const int threads_per_pair = s.head_dim / 4 * (n_eff >= 16 ? 4 : 1);
+    const int threads_per_pair = s.head_dim / 4 * merge_groups_for(int(n_eff));
     const int pairs_per_block = kThreads / threads_per_pair;
     out->merge_grid = int32_t((grid_rows * s.n_q_heads + pairs_per_block - 1) / pairs_per_block * n_seqs);
     if (n_splits_req > 0 && out->workspace_bytes > max_ws_bytes) return PPA_ERR_WORKSPACE;

@@ -23,6 +23,11 @@ constexpr int kWgPerCu = 1;      // resident attention workgroups per CU (LDS/VG
 constexpr int kMaxSplits = 128;
 constexpr int kChunkRowsForCap = 2048;  // the cap: tile slots of a full 2048-row chunk
 
+// Thread groups per (row, head) pair in the merge kernel: 4 for kMergeFourGroups
+// splits or more, else 1 (the planner sizes the merge grid by it).
+constexpr int kMergeFourGroups = 16;
+constexpr int merge_groups_for(int n_splits) { return n_splits >= kMergeFourGroups ? 4 : 1; }
+
 struct Shape {
   int64_t history;
   int32_t rows, n_q_heads, n_kv_heads, head_dim, page_size, dtype;
