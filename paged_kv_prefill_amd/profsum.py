@@ -5,6 +5,8 @@ counter passes scaled by a copy of known size).
   python -m paged_kv_prefill_amd.profsum stats <kernel_stats.csv> <out.txt> "<command>"
   python -m paged_kv_prefill_amd.profsum traffic <fetch.csv> <write.csv> <out.json> <kernel substring> \
       <copy bytes> "<fetch command>" "<write command>"
+  python -m paged_kv_prefill_amd.profsum counters <counters.csv> <out.txt> <kernel substring> \
+      <exact flops per launch> <wave-tiles per launch> <launch us from the kernel trace> "<command>"
 """
 
 import csv
@@ -82,10 +84,71 @@ def traffic(fetch_csv, write_csv, out_json, kernel_sub, copy_bytes, fetch_cmd, w
     print(json.dumps(rec, indent=1))
 
 
+def _per_kernel_counters(path):
+    """{kernel: {counter: [value per dispatch]}}"""
+    out = {}
+    for r in csv.DictReader(open(path)):
+        out.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+# MI355X: 256 compute units of 4 SIMDs, 2.4 GHz peak engine clock
+SIMDS = 1024
+CLOCK_GHZ = 2.4
+
+
+def counters(csv_path, out_path, kernel_sub, exact_flops, tiles, launch_us, command):
+    """MFMA utilisation of one kernel from an SQ/GRBM counter pass: the MFMA
+    operations the hardware counted (MOPS counters count 512 flops each)
+    against the exact attention flops, the matrix-core busy cycles per SIMD
+    against the launch's duration at the peak clock, and instructions per
+    (wave, 64-key tile)."""
+    per = _per_kernel_counters(csv_path)
+    names = [n for n in per if kernel_sub in short(n, 1 << 30)]
+    if len(names) != 1:
+        raise SystemExit(f"kernel match for {kernel_sub!r}: {names}")
+    c = {k: sum(v) / len(v) for k, v in per[names[0]].items()}
+    n = len(next(iter(per[names[0]].values())))
+    mops = c.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0) + c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
+    counted = mops * 512.0
+    busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+    gui = c.get("GRBM_GUI_ACTIVE", 0.0)
+    lines = [f"# rocprofv3 counter pass: MFMA utilisation of the attention kernel",
+             f"# command: {command}", f"# kernel source hash: {kernel_source_hash()}",
+             f"# kernel: {short(names[0], 200)}", f"# dispatches averaged: {n}", ""]
+    for k in sorted(c):
+        lines.append(f"{k:34s} {c[k]:18.0f}")
+    lines.append("")
+    lines.append(f"exact attention flops per launch   {exact_flops:18.0f}")
+    lines.append(f"MFMA flops counted (MOPS x 512)    {counted:18.0f}  ({counted / exact_flops:.3f} x exact)")
+    per_simd = busy / SIMDS
+    lines.append(f"MFMA busy cycles per SIMD          {per_simd:18.0f}  ({busy / max(c.get('SQ_INSTS_MFMA', 1), 1):.1f} per MFMA)")
+    lines.append(f"launch duration (kernel trace)     {launch_us:18.1f} us = {launch_us * 1e3 * CLOCK_GHZ:.0f} cycles at "
+                 f"{CLOCK_GHZ} GHz")
+    lines.append(f"MFMA utilisation                   {100.0 * per_simd / (launch_us * 1e3 * CLOCK_GHZ):18.1f} %")
+    if gui:
+        # summed over the 8 XCDs and read over the counter window, which is
+        # longer than the kernel: context only
+        lines.append(f"GRBM_GUI_ACTIVE / 8 XCDs           {gui / 8:18.0f}  (counter window, not the launch)")
+    if tiles:
+        lines.append(f"(wave, 64-key tile) pairs per launch {tiles:16.0f}")
+        for k in ("SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_SALU"):
+            if k in c:
+                lines.append(f"{k + ' per (wave, 64-key tile)':44s} {c[k] / tiles:8.1f}")
+        if "SQ_WAVE_CYCLES" in c:
+            lines.append(f"{'SQ_WAVE_CYCLES per (wave, 64-key tile)':44s} {c['SQ_WAVE_CYCLES'] / tiles:8.1f}")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         stats(sys.argv[2], sys.argv[3], sys.argv[4])
     elif sys.argv[1] == "traffic":
         traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], int(sys.argv[6]), sys.argv[7], sys.argv[8])
+    elif sys.argv[1] == "counters":
+        counters(sys.argv[2], sys.argv[3], sys.argv[4], float(sys.argv[5]), float(sys.argv[6]), float(sys.argv[7]),
+                 sys.argv[8])
     else:
         raise SystemExit(__doc__)
