@@ -202,13 +202,18 @@ enum class Addr { Contig, PageBig, Page16, Page8, PageLane };
 
 // The softmax weights are exp2(s c - m_ref) with a fixed reference m_ref per
 // query vector instead of a running max, so the output accumulators are never
-// rescaled inside the key loop.  The reference is the max of the first tile
-// that has a visible key; later weights may exceed 1 by up to 2^15, which
-// fp16 (and bf16) P and fp32 O and l hold.  If any query vector of the
-// workgroup sees a larger score (its running max passes m_ref + 15 in the
-// log2 domain), the split is computed again with the exact max as reference.
-// Either way the result is the same softmax; only rounding differs.
+// rescaled inside the key loop.  The reference is the max of the split's first
+// tile (a query vector that sees any key of the split sees its first key).
+// Later weights may exceed 1; fp16 or bf16 P and fp32 O and l hold them as long
+// as none overflows.  An fp16 weight past the format's range rounds to
+// infinity and makes the lane's sum l infinite; a sum past kSumLimit bounds
+// the weights of the other types.  The first pass checks only that, once, at
+// its end.  If any lane of the workgroup fails, a second pass tracks the
+// running max of every tile, and if some query vector's max passes m_ref + 15
+// (log2 domain) a third pass takes the exact max as reference.  Either way the
+// result is the same softmax; only rounding differs.
 constexpr float kRefMarginLog2 = 15.0f;
+constexpr float kSumLimit = 0x1p64f;
 
 // Q8: K and V pages hold 8-bit quants with an fp16 scale per 32 values along
 // d (see the q8 loader below); the tiles are widened to fp16 in LDS and the
@@ -581,10 +586,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   const int v_cc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   const int vofs1 = v_r * 128 + ((v_cc ^ lds_g(v_r)) << 4) + (lane & 1) * 8;
   const int vofs2 = 1024 + v_r * 128 + ((v_cc ^ lds_g(v_r + 8)) << 4) + (lane & 1) * 8;
-  auto pv_softmax = [&](const uint8_t* vt, auto&& step_hook) __attribute__((always_inline)) {
+  auto pv_softmax = [&](const uint8_t* vt, auto track, auto&& step_hook) __attribute__((always_inline)) {
+    constexpr bool TRACK = decltype(track)::value;
     constexpr int NPV = 4 * DB;
     constexpr int VPF = D >= 256 ? 2 : 3;
-    constexpr int MAX_STEPS = NPV >= 16 ? 4 : 2;  // steps that carry the max reduction
+    // steps that carry the max reduction (none when the tile's max is not needed)
+    constexpr int MAX_STEPS = TRACK ? (NPV >= 16 ? 4 : 2) : 0;
     i16x4 vlo[NPV], vhi[NPV];
     auto load = [&](int i) __attribute__((always_inline)) {
       const int kstep = i / DB, db = i % DB;
@@ -593,21 +600,21 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
       vhi[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vt + (vofs2 ^ ((db & 1) << 6)) + imm));
     };
     // VALU work: max over the lane's 32 QB scores (MAX_STEPS steps, each within
-    // one query block), then their weights.  Element e is score e % 32 of
-    // block e / 32 (kstep-major, 8 per pb entry).
+    // one query block) if tracked, then their weights.  Element e is score
+    // e % 32 of block e / 32 (kstep-major, 8 per pb entry).
     constexpr int ET = 32 * QB;
-    constexpr int PER = ET / MAX_STEPS;
+    constexpr int PER = TRACK ? ET / MAX_STEPS : 32;
     static_assert(32 % PER == 0, "a max step stays within one query block");
     auto elem = [&](int e) __attribute__((always_inline)) -> float { return sc[e >> 5][(e >> 4) & 1][e & 15]; };
-    float part[MAX_STEPS];
+    float part[MAX_STEPS > 0 ? MAX_STEPS : 1];
     float base[QB], rs[QB], p32[ET];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      base[qb] = 0.f;
+      base[qb] = (TRACK || m_ref[qb] == kNegInf) ? 0.f : m_ref[qb];
       rs[qb] = 0.f;
     }
     auto valu = [&](int i) __attribute__((always_inline)) {
-      if (i < MAX_STEPS) {
+      if (TRACK && i < MAX_STEPS) {
         float mx = elem(i * PER);
 #pragma unroll
         for (int e = 1; e < PER; ++e) mx = fmaxf(mx, elem(i * PER + e));
@@ -749,7 +756,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
       __builtin_amdgcn_sched_barrier(0);   // keep the two phases apart
     }
     // PV(it-1) with the previous weights, fused with this tile's softmax.
-    pv_softmax(ODD ? vbuf0 : vbuf1, [&](int i) {
+    pv_softmax(ODD ? vbuf0 : vbuf1, masked, [&](int i) {
       if constexpr (Q8) {
         constexpr int EVERY = 4 * DB / NQ;
         if (i % EVERY == 0)
@@ -786,9 +793,21 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
       ++it;
     }
   };
-
+  // One pass over the split's tiles.  The masked body also takes each tile's
+  // max; the fast body does not.  Tile 0 always runs in the masked body: a
+  // query vector that sees any key of the split sees its first key, so tile 0
+  // sets every reference.  With track_all (the second pass, after the first
+  // one overflowed) every tile runs in the masked body.
+  auto run_pass = [&](bool track_all) __attribute__((always_inline)) {
+    int it = 0;
+    if (!track_all) {
+      run(it, n_tiles > 0 ? 1 : 0, std::true_type{});
+      run(it, n_fast, std::false_type{});
+    }
+    run(it, n_tiles, std::true_type{});
+  };
   __shared__ int wg_redo[kWaves];
-  for (int pass = 0; pass < 2; ++pass) {
+  for (int pass = 0; pass < 3; ++pass) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
@@ -814,28 +833,30 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       }
     }
-    int it = 0;
-    run(it, n_fast, std::false_type{});
-    run(it, n_tiles, std::true_type{});
+    run_pass(pass == 1);
     if (n_tiles > 0) {
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       __syncthreads();
       if ((n_tiles - 1) & 1) pv_last(vbuf1);
       else pv_last(vbuf0);
     }
-    if (pass == 1) break;
-    // Did any query vector of the workgroup outgrow its reference?
+    if (pass == 2) break;
+    // Pass 0: did a weight overflow (an infinite fp16 weight, or a sum past
+    // kSumLimit)?  Pass 1: did a running max outgrow its reference?
     bool outgrown = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) outgrown |= m_true[qb] > m_ref[qb] + kRefMarginLog2;
+    for (int qb = 0; qb < QB; ++qb)
+      outgrown |= pass == 0 ? !(l[qb] <= kSumLimit) : m_true[qb] > m_ref[qb] + kRefMarginLog2;
     const bool redo = __ballot(outgrown) != 0;
     if (lane == 0) wg_redo[wave] = redo;
     __syncthreads();
     const bool any = wg_redo[0] | wg_redo[1] | wg_redo[2] | wg_redo[3];
     __syncthreads();
     if (!any) break;
+    if (pass == 1) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) m_ref[qb] = m_true[qb];  // the exact max: every weight is at most 1 now
+      for (int qb = 0; qb < QB; ++qb) m_ref[qb] = m_true[qb];  // the exact max: every weight is at most 1 now
+    }
   }
 
   // Epilogue: combine the two lanes' sums; lane holds d = 32 db + 8 q + 4 h + 0..3.
