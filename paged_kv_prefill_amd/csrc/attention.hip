@@ -12,9 +12,11 @@ namespace {
 // decode step or a short append on a long history: four times the loads in
 // flight per pair instead of one thread walking every split), GR = 1 below
 // (many pairs, few splits: no cross-group exchange).
-// Each thread keeps 8 splits' loads in flight.  The weights are
-// exp2(lse_s - M) with M the pair's max lse; within a group the splits are
-// summed in index order, then the groups in index order: the order is fixed,
+// One pass: each thread keeps 8 splits' loads in flight and a running
+// reference M (the largest lse it has read); a batch's weights are
+// exp2(lse_s - M) after the sums so far are scaled to the batch's M.  Groups
+// then scale their sums to the pair's largest lse and add in index order.
+// Within a group the splits are summed in index order: the order is fixed,
 // so results are reproducible.  Splits that start past the row's last key
 // hold nothing for it and are not read.
 template <int D, class E, int GR>
@@ -22,10 +24,8 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   constexpr int TPP = D / 4;                      // threads per (pair, group)
   constexpr int TPAIR = TPP * GR;                 // threads per pair
   constexpr int PPB = 256 / TPAIR;                // pairs per block
-  constexpr int WPP = TPAIR >= 64 ? TPAIR / 64 : 1;  // waves per pair
-  __shared__ float mx_part[PPB][WPP];
-  __shared__ f32x4 acc_part[PPB][GR][TPP];
-  __shared__ float w_part[PPB][GR];
+  __shared__ f32x4 acc_part[GR > 1 ? PPB : 1][GR][TPP];
+  __shared__ float w_part[GR > 1 ? PPB : 1][GR], m_part[GR > 1 ? PPB : 1][GR];
 
   // The sequence (grid y with several sequences): its first row in the
   // workspace and output, its rows and history.
@@ -52,18 +52,6 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   if (nv > a.n_splits) nv = a.n_splits;
   const float* lse = a.ws_lse + pair;
 
-  // The pair's max lse: strided over its threads, then across lanes and waves.
-  float mx = kNegInf;
-  for (int s = tp; s < nv; s += TPAIR) mx = fmaxf(mx, lse[(int64_t)s * pairs]);
-  constexpr int WIDTH = TPAIR < 64 ? TPAIR : 64;
-#pragma unroll
-  for (int o = WIDTH / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, WIDTH));
-  if (tp % WIDTH == 0) mx_part[pl][tp / WIDTH] = mx;
-  __syncthreads();
-  mx = mx_part[pl][0];
-#pragma unroll
-  for (int w = 1; w < WPP; ++w) mx = fmaxf(mx, mx_part[pl][w]);
-
   // This group's splits [sb, se).
   const int per = (nv + GR - 1) / GR;
   const int sb = min(grp * per, nv);
@@ -71,35 +59,56 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const float* op = a.ws_o + pair * D + 4 * t;
   const int64_t ostride = (int64_t)pairs * D;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
+  float wsum = 0.f, m = kNegInf;
   for (int s0 = sb; s0 < se; s0 += 8) {
     float l8[8];
     f32x4 v8[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int s = min(s0 + j, se - 1);
-      l8[j] = lse[(int64_t)s * pairs];
-      v8[j] = *(const f32x4*)(op + s * ostride);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
+      l8[j] = kNegInf;
+      v8[j] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (s0 + j < se) {
-        const float w = exp2f(l8[j] - mx);
-        acc += w * v8[j];
-        wsum += w;
+        l8[j] = lse[(int64_t)(s0 + j) * pairs];
+        v8[j] = *(const f32x4*)(op + (int64_t)(s0 + j) * ostride);
       }
     }
-  }
-  acc_part[pl][grp][t] = acc;
-  if (t == 0) w_part[pl][grp] = wsum;
-  __syncthreads();
-  if (grp != 0 || !valid) return;
-  acc = acc_part[pl][0][t];
-  wsum = w_part[pl][0];
+    float mb = m;
 #pragma unroll
-  for (int g = 1; g < GR; ++g) {
-    acc += acc_part[pl][g][t];
-    wsum += w_part[pl][g];
+    for (int j = 0; j < 8; ++j) mb = fmaxf(mb, l8[j]);
+    if (mb == kNegInf) continue;                  // nothing with weight yet
+    const float scale = exp2f(m - mb);            // 0 while nothing has been added
+    acc *= scale;
+    wsum *= scale;
+    m = mb;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float w = exp2f(l8[j] - m);          // 0 for the padding entries
+      acc += w * v8[j];
+      wsum += w;
+    }
+  }
+  if constexpr (GR > 1) {
+    acc_part[pl][grp][t] = acc;
+    if (t == 0) {
+      w_part[pl][grp] = wsum;
+      m_part[pl][grp] = m;
+    }
+    __syncthreads();
+    if (grp != 0 || !valid) return;
+    float mx = m_part[pl][0];
+#pragma unroll
+    for (int g = 1; g < GR; ++g) mx = fmaxf(mx, m_part[pl][g]);
+    acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    wsum = 0.f;
+#pragma unroll
+    for (int g = 0; g < GR; ++g) {
+      const float mg = m_part[pl][g];
+      const float sg = mg == kNegInf ? 0.f : exp2f(mg - mx);  // an empty group adds nothing
+      acc += sg * acc_part[pl][g][t];
+      wsum += sg * w_part[pl][g];
+    }
+  } else {
+    if (!valid) return;
   }
   const float inv = 1.f / wsum;
   const uint32_t lo = E::bits(acc[0] * inv) | ((uint32_t)E::bits(acc[1] * inv) << 16);
