@@ -79,3 +79,31 @@ def test_decode_step_with_many_splits(long_case, n_splits):
     torch.cuda.synchronize()
     assert _gpu.bits_equal(out, out_c)
     _gpu.assert_close(_gpu.host_out(out)[[0]], _oracle_rows(qkv, H, [0]), f"{case.name} R=1 S={plan['n_splits']}")
+
+
+
+def test_decode_and_append_on_a_4m_token_history():
+    """A decode step and a 16-row append after 4,194,304 tokens (2^22; d 64,
+    8/1 heads, fp16): key positions far past the long workloads', the
+    planner's 128 splits; paged = contiguous bit for bit and every row
+    against the oracle."""
+    import torch
+    H, R = 1 << 22, 16
+    case = synth.make_case("h4m_d64_f16", H, R, 8, 1, 64, 16, "f16", seed=23)
+    d = _gpu.dev_case(case)
+    outs = []
+    for rows in (1, R):
+        plan = pkg.paged_prefill_plan(H, rows, 8, 1, 64, 16)
+        print(f"case h4m R={rows}: planner splits {plan['n_splits']}", flush=True)
+        q = d["q"][:rows].contiguous()
+        out = pkg.paged_prefill_attention(q, d["k_pages"], d["v_pages"], d["block_table"], H)
+        out_c = pkg.contiguous_prefill_attention(q, d["k"], d["v"], H)
+        torch.cuda.synchronize()
+        assert _gpu.bits_equal(out, out_c), f"R={rows}: paged and contiguous differ bitwise"
+        outs.append(_gpu.host_out(out))
+    del d
+    torch.cuda.empty_cache()
+    qkv = tuple(_gpu.decode(case, a) for a in (case.q, case.k_contig, case.v_contig))
+    ref = _oracle_rows(qkv, H, np.arange(R))
+    _gpu.assert_close(outs[0], ref[:1], "H=4M R=1")
+    _gpu.assert_close(outs[1], ref, "H=4M R=16")
