@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}   # MI355X dense fp16/bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+NOMINAL_CLOCK_GHZ = 2.4   # the engine clock the published peaks assume
 CHUNKS = ("sweep_32768", "piece_64k", "long_128k")
 ROOFLINE_CHUNK = "sweep_32768"   # one attention launch per call (one split, no merge)
 
@@ -68,6 +69,19 @@ def load_traffic(kernel_hash):
     if rec.get("kernel_source_hash") != kernel_hash:
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def load_clock(kernel_hash):
+    """The engine clock the roofline kernel ran at (an upper bound from the
+    committed MFMA counter pass), or None if the kernel changed since."""
+    path = os.path.join(ROOT, "profiles", "attn_d256_f16_paged_32k_mfma_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_hash:
+        return None
+    return rec.get("clock_ghz_upper_bound")
 
 
 def cpu_baseline(case):
@@ -460,6 +474,12 @@ def main():
                     "frac": round(achieved / PEAK_TFLOPS["f16"], 4), "traffic": traffic,
                     "kernel": "attn_partial_kernel<256, F16, paged> (32K-history 2048-row chunk, one launch)",
                     "launch_ms_mean": round(float(ms.mean()), 4), "kernel_source_hash": khash}
+        clock = load_clock(khash)
+        if clock:
+            # the same peak scaled to the clock the counters saw (at most that clock)
+            peak_clk = PEAK_TFLOPS["f16"] * clock / NOMINAL_CLOCK_GHZ
+            roofline.update({"clock_ghz_counters": round(clock, 3), "peak_at_that_clock": round(peak_clk, 1),
+                             "frac_at_that_clock": round(achieved / peak_clk, 4)})
 
     line = {
         "metric": "paged prefill-attn TFLOP/s + ms per 2048-row chunk at 32K-128K history",

@@ -109,6 +109,12 @@ def counters(csv_path, out_path, kernel_sub, exact_flops, tiles, launch_us, comm
         raise SystemExit(f"kernel match for {kernel_sub!r}: {names}")
     c = {k: sum(v) / len(v) for k, v in per[names[0]].items()}
     n = len(next(iter(per[names[0]].values())))
+    # the counter pass's own dispatch durations (ns), for the clock estimate
+    durs = {}
+    for r in csv.DictReader(open(csv_path)):
+        if r["Kernel_Name"] == names[0]:
+            durs[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    pass_ns = sum(durs.values()) / len(durs)
     mops = c.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0) + c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
     counted = mops * 512.0
     busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
@@ -126,10 +132,16 @@ def counters(csv_path, out_path, kernel_sub, exact_flops, tiles, launch_us, comm
     lines.append(f"launch duration (kernel trace)     {launch_us:18.1f} us = {launch_us * 1e3 * CLOCK_GHZ:.0f} cycles at "
                  f"{CLOCK_GHZ} GHz")
     lines.append(f"MFMA utilisation                   {100.0 * per_simd / (launch_us * 1e3 * CLOCK_GHZ):18.1f} %")
+    clock = None
     if gui:
-        # summed over the 8 XCDs and read over the counter window, which is
-        # longer than the kernel: context only
-        lines.append(f"GRBM_GUI_ACTIVE / 8 XCDs           {gui / 8:18.0f}  (counter window, not the launch)")
+        # GRBM_GUI_ACTIVE counts engine cycles, summed over the 8 XCDs, over a
+        # counter window a few microseconds longer than the dispatch: per XCD
+        # over the dispatch's duration it bounds the clock the kernel ran at
+        # from above (about 1% high for a 1 ms launch).
+        clock = gui / 8 / pass_ns
+        lines.append(f"GRBM_GUI_ACTIVE / 8 XCDs           {gui / 8:18.0f}  over {pass_ns / 1e3:.1f} us "
+                     f"(counter-pass dispatch): clock <= {clock:.2f} GHz")
+        lines.append(f"MFMA utilisation at that clock     {100.0 * busy / SIMDS / (pass_ns * clock):18.1f} %")
     if tiles:
         lines.append(f"(wave, 64-key tile) pairs per launch {tiles:16.0f}")
         for k in ("SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_SALU"):
@@ -140,6 +152,13 @@ def counters(csv_path, out_path, kernel_sub, exact_flops, tiles, launch_us, comm
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+    rec = {"kernel": short(names[0], 200), "kernel_source_hash": kernel_source_hash(), "command": command,
+           "mfma_flops_counted": counted, "exact_flops": exact_flops,
+           "mfma_busy_cycles_per_simd": per_simd, "counter_pass_dispatch_us": pass_ns / 1e3,
+           "clock_ghz_upper_bound": clock}
+    with open(os.path.splitext(out_path)[0] + ".json", "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
 
 
 if __name__ == "__main__":
