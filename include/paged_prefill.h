@@ -17,8 +17,8 @@
  *   with the softmax taken over j = 0 .. H+i and g = h / (Hq/Hkv).  The
  *   history is cut into splits, each split writes a partial output and its
  *   log-sum-exp, and a merge kernel combines them (the PR's split-KV prefill
- *   attention and its reduce).  Inputs are fp16 or bf16; scores, the running
- *   max m, the running sum l and the output accumulator are fp32; out is
+ *   attention and its reduce).  Inputs are fp16 or bf16; scores, the softmax
+ *   reference m, the sum l and the output accumulator are fp32; out is
  *   rounded to the input type, to nearest even.
  *
  * Layouts (row-major, element = 2 bytes):
