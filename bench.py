@@ -264,8 +264,9 @@ def extra_measurements(chunks, paged, contig, pkg, synth, to_dev, stream, reps=1
 
 def q8_measurements(chunks, paged, pkg, synth, stream, reps):
     """Each chunk over 8-bit pages of the same shapes (random quants and
-    scales), interleaved with the 16-bit paged chunk; and a one-row decode step
-    on each history, K/V bytes (quants + scales) against HBM peak."""
+    scales), interleaved with the 16-bit paged chunk; a one-row decode step on
+    each history, K/V bytes (quants + scales) against HBM peak; and the
+    quantizing append of the chunk's rows."""
     import numpy as np
     import torch
     dev = stream.device
@@ -293,11 +294,22 @@ def q8_measurements(chunks, paged, pkg, synth, stream, reps):
             fd()
         md = timed(fd, 2 * reps, stream)[0]
         kvb = (cs.history + 1) * cs.n_kv_heads * (cs.head_dim + cs.head_dim // 16) * 2
+        # The quantizing append of the chunk's own rows (its K and V are taken
+        # from the 16-bit chunk's values at those positions): 16-bit rows read,
+        # quants and scales written.
+        ctx = cs.history + cs.rows
+        kn, vn = c["k"][cs.history:ctx].contiguous(), c["v"][cs.history:ctx].contiguous()
+        fa = lambda: pkg.paged_kv_append_q8(kn, vn, kq, ks, vq, vs, bt, cs.history, stream=stream)
+        fa()
+        ma = timed(fa, 2 * reps, stream)[0]
+        ab = 2 * cs.rows * cs.n_kv_heads * (2 * cs.head_dim + cs.head_dim + cs.head_dim // 16)
         res[c["name"]] = {"ms_median": round(m8, 4), "tflops": round(c["flops"] / (m8 * 1e-3) / 1e12, 1),
                           "over_16bit_pages": round(m8 / m16, 3),
                           "decode_1row_ms_median": round(md, 5),
                           "decode_kv_gbs": round(kvb / (md * 1e-3) / 1e9, 1),
-                          "decode_hbm_frac": round(kvb / (md * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+                          "decode_hbm_frac": round(kvb / (md * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                          "append_q8_chunk_ms_median": round(ma, 5),
+                          "append_q8_gbs": round(ab / (ma * 1e-3) / 1e9, 1)}
         del kq, vq, ks, vs, bt, o, qc
         torch.cuda.empty_cache()
     return res
