@@ -696,6 +696,14 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   // vmcnt(LPW) lgkmcnt(0): before the tile loop's barriers.
   constexpr int kWaitVmcntLPW = 0x0070 | (LPW & 15) | ((LPW >> 4) << 14);
   static_assert(LPW < 64, "vmcnt holds 6 bits");
+  // At head dimensions up to 128 (16-bit pages) both loads of a body, K(it+1)
+  // and V(it), go out during its QK phase, one per MFMA step, and the top
+  // barrier of the next body covers both: one barrier per tile.  At d 256
+  // V(it) loads during the PV phase instead, with a second barrier before PV
+  // (the QK phase there is held by its operand reads; moving the V loads into
+  // it gained 1% on a 2048-row chunk and lost 2% on 128-row pieces, and the
+  // VGPR-form build of that code crashes the compiler).
+  constexpr bool ONE_BARRIER = !Q8 && D <= 128;
   auto body = [&](int it, auto masked, auto parity) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
     constexpr bool ODD = decltype(parity)::value;  // it is odd
@@ -703,9 +711,11 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // This wave's loads in flight, oldest first: K(it) (issued during the QK
     // of it-1), V(it-1) (during the PV phase of it-1), LPW each.  Wait for
     // K(it) only; after the barrier K(it) is in LDS and the buffers of K(it-1)
-    // and V(it-2) are free (every wave is done with body it-1).  Q8: nothing
-    // is in flight; the previous body widened K(it) and V(it-1) in LDS.
-    __builtin_amdgcn_s_waitcnt(Q8 ? kWaitVmcnt0 & ~0x0F00 : kWaitVmcntLPW);
+    // and V(it-2) are free (every wave is done with body it-1).  With one
+    // barrier per tile both were issued during the QK of it-1: wait for both.
+    // Q8: nothing is in flight; the previous body widened K(it) and V(it-1)
+    // in LDS.
+    __builtin_amdgcn_s_waitcnt((Q8 || ONE_BARRIER) ? kWaitVmcnt0 & ~0x0F00 : kWaitVmcntLPW);
     lds_barrier();
     // The loads of K(it+1) and V(it) are spread over the MFMA steps (one per
     // few MFMAs) rather than issued in a burst, which would stall the waves on
@@ -728,6 +738,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         if (ks % EVERY == 0)
           issue_q8(it + 1, pk, kb, false, ODD ? kbuf0 : kbuf1, ks / EVERY, std::bool_constant<!MASKED>{});
         if (ks == 1) ksc = load_scales(it + 1, pk, false);
+      } else if constexpr (ONE_BARRIER) {
+        static_assert(KS == 2 * LPW, "one load per QK step");
+        if (ks % 2 == 0)
+          issue_one(it + 1, pk, kb, false, ODD ? kbuf0 : kbuf1, ks / 2, std::bool_constant<!MASKED>{});
+        else
+          issue_one(it, pv, vb, true, ODD ? vbuf1 : vbuf0, ks / 2, std::bool_constant<!MASKED>{});
       } else {
         constexpr int EVERY = KS / LPW;
         if (ks % EVERY == 0)
@@ -748,8 +764,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
       }
     }
     // Now in flight: V(it-1), then K(it+1).  Wait for V(it-1), which the PV
-    // below reads, so that its load latency hides behind the QK phase.
-    if constexpr (!Q8) {
+    // below reads, so that its load latency hides behind the QK phase.  (With
+    // one barrier per tile V(it-1) was waited for at the top.)
+    if constexpr (!Q8 && !ONE_BARRIER) {
       __builtin_amdgcn_s_waitcnt(kWaitVmcntLPW);
       lds_barrier();
     } else {
@@ -762,7 +779,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         if (i % EVERY == 0)
           issue_q8(it, pv, vb, true, ODD ? vbuf1 : vbuf0, i / EVERY, std::bool_constant<!MASKED>{});
         if (i == 1) vsc = load_scales(it, pv, true);
-      } else {
+      } else if constexpr (!ONE_BARRIER) {
         constexpr int EVERY = 4 * DB / LPW;
         if (i % EVERY == 0)
           issue_one(it, pv, vb, true, ODD ? vbuf1 : vbuf0, i / EVERY, std::bool_constant<!MASKED>{});
