@@ -38,7 +38,10 @@
  * blocks in hipMalloc) and released by paged_prefill_release_workspaces().
  *
  * Execution: asynchronous, ordered on `stream` (0 = the null stream).  `out`
- * is valid once the stream has synchronised.  Results are deterministic for a
+ * is valid once the stream has synchronised.  Once the stream's workspace is
+ * large enough for a call (after a first call of that size on that stream),
+ * the call enqueues kernel launches only and can be captured in a HIP graph
+ * (PPA_VALIDATE=1 adds host copies, which capture does not allow).  Results are deterministic for a
  * given plan: no atomics; partials merge in a fixed order; identity, permuted
  * and scattered block tables give bit-identical outputs.
  *
