@@ -121,12 +121,31 @@ def _need_cuda(*tensors):
             raise ValueError("tensors must be contiguous")
 
 
+def _check_kinds(q, kv, out, int32=(), int64=()):
+    """Element types and output shape the C ABI cannot see: K/V and out in
+    q's type, out shaped like q, index arrays int32 / int64."""
+    import torch
+    _dtype_code(q)
+    for t in kv:
+        if t.dtype != q.dtype:
+            raise TypeError(f"K/V dtype {t.dtype} differs from q's {q.dtype}")
+    if out is not None and (out.dtype != q.dtype or tuple(out.shape) != tuple(q.shape)):
+        raise ValueError("out must have q's dtype and shape")
+    for t in int32:
+        if t.dtype != torch.int32:
+            raise TypeError("block tables and row offsets are int32")
+    for t in int64:
+        if t.dtype != torch.int64:
+            raise TypeError("history lengths are int64")
+
+
 def paged_prefill_attention(q, k_pages, v_pages, block_table, history_len, n_splits=0, out=None,
                             piece_rows=0, stream=None):
     """out[R][Hq][d] = causal attention of q[R][Hq][d] (rows at positions
     history_len .. history_len+R-1) over the paged cache k_pages/v_pages
     [pool][page_size][Hkv][d] addressed by block_table (int32).  piece_rows
     > 0 runs the chunk in pieces of that many rows."""
+    _check_kinds(q, (k_pages, v_pages), out, int32=(block_table,))
     _need_cuda(q, k_pages, v_pages, block_table, out)
     rows, n_q_heads, head_dim = q.shape
     _, page_size, n_kv_heads, kd = k_pages.shape
@@ -150,9 +169,13 @@ def paged_prefill_attention(q, k_pages, v_pages, block_table, history_len, n_spl
 
 def contiguous_prefill_attention(q, k, v, history_len, n_splits=0, out=None, piece_rows=0, stream=None):
     """The same over contiguous k/v [>= H+R][Hkv][d]."""
+    _check_kinds(q, (k, v), out)
     _need_cuda(q, k, v, out)
     rows, n_q_heads, head_dim = q.shape
     n_kv_heads = k.shape[1]
+    if k.dim() != 3 or k.shape[2] != head_dim or tuple(v.shape) != tuple(k.shape) \
+            or k.shape[0] < int(history_len) + rows:
+        raise ValueError("k and v must be [>= history_len + rows][Hkv][d] with q's d")
     if out is None:
         out = q.new_empty(q.shape)
     args = (int(history_len), int(rows))
@@ -177,6 +200,7 @@ def paged_prefill_attention_varlen(q, k_pages, v_pages, block_tables, cu_rows, h
     max_rows and max_context (host ints) bound every sequence's rows and
     history + rows."""
     import torch
+    _check_kinds(q, (k_pages, v_pages), out, int32=(block_tables, cu_rows), int64=(history_lens,))
     _need_cuda(q, k_pages, v_pages, block_tables, cu_rows, history_lens, out)
     if block_tables.dim() != 2 or block_tables.dtype != torch.int32 or cu_rows.dtype != torch.int32 \
             or history_lens.dtype != torch.int64:
@@ -215,6 +239,7 @@ def paged_prefill_attention_q8(q, k_quant, k_scale, v_quant, v_scale, block_tabl
     k_scale/v_scale fp16 [pool][page_size][Hkv][d/32] (value = scale * quant per
     block of 32 along d).  q and out fp16 or bf16 [R][Hq][d]."""
     import torch
+    _check_kinds(q, (), out, int32=(block_table,))
     _need_cuda(q, k_quant, k_scale, v_quant, v_scale, block_table, out)
     rows, n_q_heads, head_dim = q.shape
     _, page_size, n_kv_heads, kd = k_quant.shape
@@ -236,6 +261,7 @@ def paged_kv_append_q8(k_new, v_new, k_quant, k_scale, v_quant, v_scale, block_t
     """Quantize k_new/v_new [R][Hkv][d] (fp16 or bf16) into their slots of the
     8-bit pools, in place."""
     import torch
+    _check_kinds(k_new, (v_new,), None, int32=(block_table,))
     _need_cuda(k_new, v_new, k_quant, k_scale, v_quant, v_scale, block_table)
     rows, n_kv_heads, head_dim = k_new.shape
     _, page_size, pkv, pd = k_quant.shape
@@ -256,6 +282,7 @@ def paged_kv_append(k_new, v_new, k_pages, v_pages, block_table, history_len, st
     """Write k_new/v_new [R][Hkv][d] (tokens at positions history_len ..
     history_len+R-1) into their slots of k_pages/v_pages
     [pool][page_size][Hkv][d] through block_table (int32), in place."""
+    _check_kinds(k_new, (v_new, k_pages, v_pages), None, int32=(block_table,))
     _need_cuda(k_new, v_new, k_pages, v_pages, block_table)
     rows, n_kv_heads, head_dim = k_new.shape
     _, page_size, pkv, pd = k_pages.shape

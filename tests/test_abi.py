@@ -249,3 +249,32 @@ def test_append_q8_argument_errors_return_before_any_device_work(kw, code):
 
 def test_empty_q8_append_is_a_no_op():
     assert _call_append_q8(R=0, kn=0, vn=0, kq=0, ks=0, vq=0, vs=0, bt=0) == 0
+
+
+def test_binding_rejects_mixed_types_and_shapes_before_any_call():
+    """Element types and shapes the C ABI cannot see are checked in the
+    binding, on the host, before the library is called."""
+    import torch
+    import paged_kv_prefill_amd as pkg
+    q = torch.zeros(4, 8, 64, dtype=torch.float16)
+    kp = torch.zeros(3, 16, 2, 64, dtype=torch.float16)
+    bt = torch.zeros(3, dtype=torch.int32)
+    with pytest.raises(TypeError):
+        pkg.paged_prefill_attention(q, kp.to(torch.bfloat16), kp, bt, 10)
+    with pytest.raises(TypeError):
+        pkg.paged_prefill_attention(q, kp, kp, bt.to(torch.int64), 10)
+    with pytest.raises(ValueError):
+        pkg.paged_prefill_attention(q, kp, kp, bt, 10, out=torch.zeros(4, 8, 32, dtype=torch.float16))
+    with pytest.raises(ValueError):
+        pkg.paged_prefill_attention(q, kp, kp, bt, 10, out=q.to(torch.bfloat16))
+    with pytest.raises(TypeError):
+        pkg.paged_prefill_attention(q.float(), kp.float(), kp.float(), bt, 10)
+    with pytest.raises(TypeError):
+        pkg.contiguous_prefill_attention(q, torch.zeros(20, 2, 64, dtype=torch.bfloat16),
+                                         torch.zeros(20, 2, 64, dtype=torch.bfloat16), 10)
+    with pytest.raises(TypeError):
+        pkg.paged_kv_append(torch.zeros(2, 2, 64, dtype=torch.float16), torch.zeros(2, 2, 64, dtype=torch.float16),
+                            kp.to(torch.bfloat16), kp.to(torch.bfloat16), bt, 10)
+    with pytest.raises(TypeError):
+        pkg.paged_prefill_attention_varlen(q, kp, kp, bt.view(1, 3), torch.tensor([0, 4], dtype=torch.int32),
+                                           torch.tensor([10], dtype=torch.int32), 4, 14)
