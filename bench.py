@@ -91,11 +91,21 @@ def cpu_baseline(cases, budget_s=15.0):
     reported in TFLOP/s of exact causal FLOPs."""
     import numpy as np
     import oracle
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        if info:
+            blas = f"{info[0].get('internal_api')} {info[0].get('version')}"
     except Exception:
         threads = os.cpu_count()
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), cpu_model)
+    except OSError:
+        pass
     total_flops, total_s, parts = 0.0, 0.0, []
     for case in cases:
         left = budget_s - total_s
@@ -124,7 +134,7 @@ def cpu_baseline(cases, budget_s=15.0):
     return {"value": total_flops / total_s / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": ", ".join(parts) + f" (rows evenly spaced), {total_s:.1f} s, numpy float64 with BLAS on "
                       f"{threads} threads",
-            "seconds": total_s}
+            "seconds": total_s, "cpu_model": cpu_model, "blas": blas}
 
 
 def kv_bytes(case):
