@@ -213,6 +213,32 @@ def extra_measurements(chunks, paged, contig, pkg, synth, to_dev, stream, reps=1
                                                                                   oc.view(torch.int16)))}
         del q, kp, vp, bt, k, v, o, oc
     out["history_sweep_2048_rows"] = sweep
+    # Page-size sweep on the 32K chunk: the same K/V laid out in pages of 1 to
+    # 256 tokens (a random page order), paged against contiguous, interleaved.
+    c = next((c for c in chunks if c["name"] == "sweep_32768"), None)
+    if c is not None:
+        cs = c["case"]
+        ctx = cs.history + cs.rows
+        gen = torch.Generator(device="cpu").manual_seed(61)
+        pss = {}
+        for ps in (1, 4, 8, 16, 32, 64, 256):
+            n_pages = ctx // ps
+            perm = torch.randperm(n_pages, generator=gen).to(stream.device)
+            kp = torch.empty((n_pages, ps, cs.n_kv_heads, cs.head_dim), dtype=c["k"].dtype, device=stream.device)
+            vp = torch.empty_like(kp)
+            kp[perm] = c["k"][:ctx].view(n_pages, ps, cs.n_kv_heads, cs.head_dim)
+            vp[perm] = c["v"][:ctx].view(n_pages, ps, cs.n_kv_heads, cs.head_dim)
+            bt = perm.to(torch.int32)
+            o = torch.empty_like(c["q"])
+            fp = lambda: pkg.paged_prefill_attention(c["q"], kp, vp, bt, cs.history, out=o, stream=stream)
+            fc = lambda: contig(c)
+            for _ in range(3):
+                fp()
+                fc()
+            mp, mc = timed_pair(fp, fc, reps, stream)
+            pss[str(ps)] = {"ms_median": round(mp, 4), "paged_over_contiguous": round(mp / mc, 4)}
+            del kp, vp, bt, o, perm
+        out["page_size_sweep_32k"] = pss
     # KV append of each chunk's own K/V rows into its pages (idempotent here):
     # bytes = K and V rows read once and written once
     app = {}
