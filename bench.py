@@ -422,8 +422,8 @@ def varlen_measurements(pkg, synth, stream, reps):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the design note on sharding covers how it would split)", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(the work would split by KV head or by history range; see the design notes)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
