@@ -602,6 +602,45 @@ def pin_q8_exact_multiples_and_saturation(orc):
     assert list(q[0, :3]) == [127, -127, 0]
 
 
+def _binary16_value(bits):
+    """The value of an IEEE 754 binary16 bit pattern from its fields: sign
+    bit 15, biased exponent bits 14..10 (bias 15), fraction bits 9..0;
+    exponent 0 is a subnormal (fraction * 2^-24), exponent 31 is infinity
+    (fraction 0) or NaN."""
+    sign = -1.0 if bits >> 15 else 1.0
+    exp = (bits >> 10) & 0x1F
+    frac = bits & 0x3FF
+    if exp == 0x1F:
+        return sign * math.inf if frac == 0 else math.nan
+    if exp == 0:
+        return sign * math.ldexp(frac, -24)
+    return sign * math.ldexp(1024 + frac, exp - 25)
+
+
+def pin_q8_decode_scales(orc):
+    """Scale bit patterns decode to the binary16 values their fields define:
+    known patterns (the golden block's 0x2008 = 129/16384, 1, the largest
+    finite 65504, the smallest subnormal, signed zero, infinity, NaN) and
+    random patterns over the whole 16-bit range, each against the value
+    computed from its sign, exponent and fraction fields."""
+    known = {0x2008: 129 / 16384, 0x3C00: 1.0, 0x7BFF: 65504.0, 0x0001: 2.0 ** -24, 0x0400: 2.0 ** -14,
+             0x8000: -0.0, 0xC000: -2.0, 0x7C00: math.inf, 0xFC00: -math.inf}
+    raw = np.array(list(known), dtype=np.uint16)
+    got = np.asarray(orc.decode_scales(raw)).astype(np.float64)
+    want = np.array(list(known.values()))
+    assert np.array_equal(got, want), got
+    assert np.array_equal(np.signbit(got), np.signbit(want))
+    for nan_bits in (0xFFFF, 0x7E00, 0x7C01):
+        assert math.isnan(float(np.asarray(orc.decode_scales(np.array([nan_bits], dtype=np.uint16)))[0]))
+    rng = np.random.default_rng(45)
+    raw = rng.integers(0, 1 << 16, size=2048).astype(np.uint16)
+    got = np.asarray(orc.decode_scales(raw)).astype(np.float64)
+    want = np.array([_binary16_value(int(b)) for b in raw])
+    finite = ~np.isnan(want)
+    assert np.array_equal(np.isnan(got), ~finite)
+    assert np.array_equal(got[finite], want[finite])
+
+
 def _q8_pool(rng, history, rows, hkv, d, ps, extra_pool=2):
     ctx = history + rows
     n_pages = -(-ctx // ps)
@@ -663,5 +702,5 @@ def pin_q8_append(orc):
         assert all(np.array_equal(a, b) for a, b in zip(out, two))
 
 
-QUANT_PINS = [pin_q8_golden_block, pin_q8_round_trip, pin_q8_exact_multiples_and_saturation, pin_q8_attention,
+QUANT_PINS = [pin_q8_golden_block, pin_q8_decode_scales, pin_q8_round_trip, pin_q8_exact_multiples_and_saturation, pin_q8_attention,
               pin_q8_append]

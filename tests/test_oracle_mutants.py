@@ -111,6 +111,12 @@ QUANT_MUTANTS = [
      "gather_pages(k_scale, block_table, ctx, page_size)"),
     ("append one position late", "pos = history_len + i", "pos = history_len + i + 1"),
     ("append of V quantized from K", "vq, vs = quantize_q8(v_new)", "vq, vs = quantize_q8(k_new)"),
+    ("scales decoded as bfloat16", "return np.asarray(raw, dtype=np.uint16).view(np.float16)",
+     "return (np.asarray(raw, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)"),
+    ("scales decoded as integers", "return np.asarray(raw, dtype=np.uint16).view(np.float16)",
+     "return np.asarray(raw, dtype=np.uint16).astype(np.float64)"),
+    ("scale sign dropped", "return np.asarray(raw, dtype=np.uint16).view(np.float16)",
+     "return np.abs(np.asarray(raw, dtype=np.uint16).view(np.float16))"),
 ]
 
 
