@@ -57,6 +57,7 @@ _SIGNATURES = {
     "paged_prefill_piece_rows": (_I32, [_I64, _I32, _I64]),
     "paged_prefill_check_block_table": (_I32, [_VP, _I64, _I64]),
     "paged_prefill_release_workspaces": (_I32, []),
+    "paged_prefill_workspace_bytes": (_I64, [_VP]),
     "paged_prefill_strerror": (ctypes.c_char_p, [_I32]),
     "paged_prefill_version": (_I32, []),
     "paged_kv_append": (_I32, [_VP, _VP, _VP, _VP, _VP, _I64, _I32, _I32, _I32, _I32, _I32, _VP]),
@@ -139,6 +140,17 @@ def _check_kinds(q, kv, out, int32=(), int64=()):
             raise TypeError("history lengths are int64")
 
 
+def _check_table(block_table, history_len, rows, page_size):
+    """The block table must name a page for every position 0 .. H+R-1: the
+    kernels read ceil((H + R) / page_size) entries and cannot see its length."""
+    need = -(-(int(history_len) + int(rows)) // int(page_size))
+    if int(history_len) < 0 or int(rows) < 0:
+        return
+    if block_table.numel() < need:
+        raise ValueError(f"block_table has {block_table.numel()} entries; history_len + rows = "
+                         f"{int(history_len) + int(rows)} tokens need {need} pages of {int(page_size)}")
+
+
 def paged_prefill_attention(q, k_pages, v_pages, block_table, history_len, n_splits=0, out=None,
                             piece_rows=0, stream=None):
     """out[R][Hq][d] = causal attention of q[R][Hq][d] (rows at positions
@@ -146,9 +158,10 @@ def paged_prefill_attention(q, k_pages, v_pages, block_table, history_len, n_spl
     [pool][page_size][Hkv][d] addressed by block_table (int32).  piece_rows
     > 0 runs the chunk in pieces of that many rows."""
     _check_kinds(q, (k_pages, v_pages), out, int32=(block_table,))
-    _need_cuda(q, k_pages, v_pages, block_table, out)
     rows, n_q_heads, head_dim = q.shape
     _, page_size, n_kv_heads, kd = k_pages.shape
+    _check_table(block_table, history_len, rows, page_size)
+    _need_cuda(q, k_pages, v_pages, block_table, out)
     if kd != head_dim or tuple(v_pages.shape) != tuple(k_pages.shape):
         raise ValueError("k_pages/v_pages shape mismatch")
     if out is None:
@@ -240,9 +253,10 @@ def paged_prefill_attention_q8(q, k_quant, k_scale, v_quant, v_scale, block_tabl
     block of 32 along d).  q and out fp16 or bf16 [R][Hq][d]."""
     import torch
     _check_kinds(q, (), out, int32=(block_table,))
-    _need_cuda(q, k_quant, k_scale, v_quant, v_scale, block_table, out)
     rows, n_q_heads, head_dim = q.shape
     _, page_size, n_kv_heads, kd = k_quant.shape
+    _check_table(block_table, history_len, rows, page_size)
+    _need_cuda(q, k_quant, k_scale, v_quant, v_scale, block_table, out)
     if kd != head_dim or tuple(v_quant.shape) != tuple(k_quant.shape) or k_quant.dtype != torch.int8 \
             or v_quant.dtype != torch.int8 or tuple(k_scale.shape) != (k_quant.shape[0], page_size, n_kv_heads, kd // 32) \
             or tuple(v_scale.shape) != tuple(k_scale.shape) or k_scale.element_size() != 2 or v_scale.element_size() != 2:
@@ -262,9 +276,10 @@ def paged_kv_append_q8(k_new, v_new, k_quant, k_scale, v_quant, v_scale, block_t
     8-bit pools, in place."""
     import torch
     _check_kinds(k_new, (v_new,), None, int32=(block_table,))
-    _need_cuda(k_new, v_new, k_quant, k_scale, v_quant, v_scale, block_table)
     rows, n_kv_heads, head_dim = k_new.shape
     _, page_size, pkv, pd = k_quant.shape
+    _check_table(block_table, history_len, rows, page_size)
+    _need_cuda(k_new, v_new, k_quant, k_scale, v_quant, v_scale, block_table)
     if (pkv, pd) != (n_kv_heads, head_dim) or tuple(v_new.shape) != tuple(k_new.shape) \
             or k_quant.dtype != torch.int8 or v_quant.dtype != torch.int8 or tuple(v_quant.shape) != tuple(k_quant.shape) \
             or tuple(k_scale.shape) != (k_quant.shape[0], page_size, n_kv_heads, head_dim // 32) \
@@ -283,9 +298,10 @@ def paged_kv_append(k_new, v_new, k_pages, v_pages, block_table, history_len, st
     history_len+R-1) into their slots of k_pages/v_pages
     [pool][page_size][Hkv][d] through block_table (int32), in place."""
     _check_kinds(k_new, (v_new, k_pages, v_pages), None, int32=(block_table,))
-    _need_cuda(k_new, v_new, k_pages, v_pages, block_table)
     rows, n_kv_heads, head_dim = k_new.shape
     _, page_size, pkv, pd = k_pages.shape
+    _check_table(block_table, history_len, rows, page_size)
+    _need_cuda(k_new, v_new, k_pages, v_pages, block_table)
     if (pkv, pd) != (n_kv_heads, head_dim) or tuple(v_pages.shape) != tuple(k_pages.shape) \
             or tuple(v_new.shape) != tuple(k_new.shape) or k_new.dtype != k_pages.dtype:
         raise ValueError("k_new/v_new/k_pages/v_pages shapes or dtypes do not match")
@@ -325,3 +341,14 @@ def paged_prefill_check_block_table(block_table_host, n_pool_pages):
 
 def paged_prefill_release_workspaces():
     _check(lib().paged_prefill_release_workspaces(), "paged_prefill_release_workspaces")
+
+
+def paged_prefill_workspace_bytes(stream=None, device=None):
+    """Bytes of the split workspace the library holds for `stream` (the
+    current stream by default)."""
+    import torch
+    dev = device if device is not None else torch.cuda.current_device()
+    rc = lib().paged_prefill_workspace_bytes(_stream_handle(stream, dev))
+    if rc < 0:
+        raise PagedPrefillError(rc, "paged_prefill_workspace_bytes")
+    return int(rc)

@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = pkg.lib()
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     for name in names:
         assert hasattr(lib, name), name
     assert lib.paged_prefill_version() == 10000
@@ -278,3 +278,31 @@ def test_binding_rejects_mixed_types_and_shapes_before_any_call():
     with pytest.raises(TypeError):
         pkg.paged_prefill_attention_varlen(q, kp, kp, bt.view(1, 3), torch.tensor([0, 4], dtype=torch.int32),
                                            torch.tensor([10], dtype=torch.int32), 4, 14)
+
+
+def test_binding_rejects_short_block_tables_before_any_call():
+    """A block table with fewer than ceil((H + R) / page_size) entries is
+    rejected in the binding (the kernels would read past it), on the host,
+    for the attention, the 8-bit attention and both appends."""
+    import torch
+    import paged_kv_prefill_amd as pkg
+    q = torch.zeros(4, 8, 64, dtype=torch.float16)          # R = 4
+    kp = torch.zeros(6, 16, 2, 64, dtype=torch.float16)     # pages of 16
+    short = torch.zeros(1, dtype=torch.int32)               # H + R = 20 tokens need 2 pages
+    with pytest.raises(ValueError, match="need 2 pages"):
+        pkg.paged_prefill_attention(q, kp, kp, short, 16)
+    with pytest.raises(ValueError, match="need 2 pages"):
+        pkg.paged_prefill_attention(q, kp, kp, short, 16, piece_rows=2)
+    kq = torch.zeros(6, 16, 2, 64, dtype=torch.int8)
+    ks = torch.zeros(6, 16, 2, 2, dtype=torch.float16)
+    with pytest.raises(ValueError, match="need 2 pages"):
+        pkg.paged_prefill_attention_q8(q, kq, ks, kq, ks, short, 16)
+    kn = torch.zeros(4, 2, 64, dtype=torch.float16)
+    with pytest.raises(ValueError, match="need 2 pages"):
+        pkg.paged_kv_append(kn, kn, kp, kp.clone(), short, 16)
+    with pytest.raises(ValueError, match="need 2 pages"):
+        pkg.paged_kv_append_q8(kn, kn, kq, ks, kq.clone(), ks.clone(), short, 16)
+    # a table just long enough passes this check (and stops at the next one: CPU tensors)
+    ok = torch.zeros(2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="on the GPU"):
+        pkg.paged_prefill_attention(q, kp, kp, ok, 16)
