@@ -35,15 +35,24 @@
  * valid until `stream` has executed the enqueued work; the library keeps no
  * pointer after a call returns.  The library owns one grow-only split
  * workspace per (device, stream), allocated on first need (that first call
- * blocks in hipMalloc) and released by paged_prefill_release_workspaces().
+ * blocks in hipMalloc).  When a larger call arrives a larger buffer is
+ * allocated and the smaller one is kept, not freed, so that work already
+ * enqueued and HIP graphs captured earlier keep valid memory; all of them
+ * are freed by paged_prefill_release_workspaces() only.
  *
  * Execution: asynchronous, ordered on `stream` (0 = the null stream).  `out`
  * is valid once the stream has synchronised.  Once the stream's workspace is
  * large enough for a call (after a first call of that size on that stream),
  * the call enqueues kernel launches only and can be captured in a HIP graph
- * (PPA_VALIDATE=1 adds host copies, which capture does not allow).  Results are deterministic for a
- * given plan: no atomics; partials merge in a fixed order; identity, permuted
- * and scattered block tables give bit-identical outputs.
+ * (PPA_VALIDATE=1 adds host copies, which capture does not allow).  A
+ * captured graph stays valid through later calls of any size on that stream
+ * (their growth retires the buffer it uses without freeing it) until
+ * paged_prefill_release_workspaces() is called.  Replaying it runs its
+ * kernels on the workspace it captured: do not replay it while other work
+ * that uses the same workspace runs on another stream.  Results are
+ * deterministic for a given plan: no atomics; partials merge in a fixed
+ * order; identity, permuted and scattered block tables give bit-identical
+ * outputs.
  *
  * Errors: 0 on success, a negative PPA_ERR_* code otherwise.  On any argument
  * error nothing is enqueued.  Slots past ctx in the last page may hold any
@@ -52,8 +61,12 @@
  * paged_prefill_check_block_table() on a host copy, or set PPA_VALIDATE=1 to
  * make every paged call copy the table to the host and check it first (slow).
  *
- * Thread safety: concurrent calls on different streams are safe; calls on the
- * same stream are ordered by the stream.
+ * Thread safety: concurrent calls on different streams are safe.  Host
+ * threads may also call concurrently on one stream: a call holds that
+ * stream's workspace from planning until its last kernel is enqueued, so the
+ * calls' kernels reach the stream one whole call after another (which call
+ * comes first is not defined).  paged_prefill_release_workspaces() must not
+ * run concurrently with any other call.
  */
 #ifndef PAGED_PREFILL_H
 #define PAGED_PREFILL_H
@@ -288,8 +301,20 @@ int paged_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v
                     int32_t n_kv_heads, int32_t head_dim, int32_t page_size, int32_t dtype,
                     ppa_stream_t stream);
 
-/* Frees every split workspace; call only when no stream still uses one. */
+/*
+ * Frees every split workspace, including the smaller ones kept after growth.
+ * Call only when no stream still runs, and no captured graph will replay,
+ * work that uses one, and not concurrently with any other call.
+ */
 int paged_prefill_release_workspaces(void);
+
+/*
+ * Host-only: bytes of the split workspace the library currently holds for
+ * `stream` on the current device (0 if none), or a negative PPA_ERR_HIP.
+ * A call with a split plan needs plan.workspace_bytes; below that it
+ * allocates (so it cannot run under stream capture).
+ */
+int64_t paged_prefill_workspace_bytes(ppa_stream_t stream);
 
 /* Static text for a status code. */
 const char* paged_prefill_strerror(int code);

@@ -16,6 +16,7 @@ dimension; PPA_MFMA_VGPR_FORM=0 selects the AGPR form for comparison.
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -42,6 +43,7 @@ KERNEL_SOURCES = (
     ("attention_q8_d256.hip", os.environ.get("PPA_MFMA_VGPR_FORM_Q8", "0")),
     ("kv_append.hip", "0"),
 )
+HOST_SOURCES = ("api.cpp", "plan.cpp")
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
@@ -57,19 +59,28 @@ def _run(cmd, verbose):
         print(err, file=sys.stderr)
 
 
-def build(verbose=False, resource_usage=False):
+def build(verbose=False, resource_usage=False, jobs=None):
+    """Compile every translation unit (in parallel, `jobs` at a time; default
+    MAX_JOBS or the CPU count, at most 16) and link the library."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    objs = []
     extra = ["-Rpass-analysis=kernel-resource-usage"] if resource_usage else []
+    steps = []
     for src, vgpr_form in KERNEL_SOURCES:
         kern_obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
-        _run([HIPCC, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, "-mllvm", "-amdgpu-mfma-vgpr-form=" + vgpr_form,
-              *extra, "-c", os.path.join(CSRC, src), "-o", kern_obj], verbose or resource_usage)
-        objs.append(kern_obj)
-    for src in ("api.cpp", "plan.cpp"):
+        steps.append(([HIPCC, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, "-mllvm",
+                       "-amdgpu-mfma-vgpr-form=" + vgpr_form, *extra, "-c", os.path.join(CSRC, src), "-o", kern_obj],
+                      kern_obj))
+    for src in HOST_SOURCES:
         obj = os.path.join(BUILD_DIR, src.replace(".cpp", ".o"))
-        _run([HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
-        objs.append(obj)
+        steps.append(([HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj], obj))
+    if jobs is None:
+        jobs = int(os.environ.get("MAX_JOBS", "0") or 0) or (os.cpu_count() or 1)
+    jobs = max(1, min(16, jobs))
+    with ThreadPoolExecutor(max_workers=jobs) as pool:
+        futures = [pool.submit(_run, cmd, verbose or resource_usage) for cmd, _ in steps]
+        for f in futures:
+            f.result()
+    objs = [obj for _, obj in steps]
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)

@@ -15,43 +15,38 @@
 #include "kernels.h"
 #include "paged_prefill.h"
 #include "plan.h"
+#include "workspace.h"
 
 namespace ppa {
 namespace {
 
-struct Workspace {
-  void* ptr = nullptr;
-  int64_t bytes = 0;
+// hipMalloc / hipFree for the workspace registry.
+struct HipAlloc {
+  void* alloc(int64_t bytes) {
+    void* p = nullptr;
+    if (hipMalloc(&p, size_t(bytes)) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    return p;
+  }
+  bool free(void* p) { return hipFree(p) == hipSuccess; }
 };
 
-std::mutex g_ws_mutex;
-std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+using Registry = WorkspaceRegistry<std::pair<int, hipStream_t>, HipAlloc>;
 
-// Grow-only workspace per (device, stream).  The first use of a size blocks
-// in hipMalloc; later calls of the same or smaller size reuse it.
-int get_workspace(hipStream_t stream, int64_t bytes, void** out) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return PPA_ERR_HIP;
-  std::lock_guard<std::mutex> lock(g_ws_mutex);
-  Workspace& ws = g_ws[{dev, stream}];
-  if (ws.bytes < bytes) {
-    if (ws.ptr) {
-      // The old buffer may still be in use by work queued on this stream.
-      if (hipStreamSynchronize(stream) != hipSuccess) return PPA_ERR_HIP;
-      (void)hipFree(ws.ptr);
-      ws.ptr = nullptr;
-      ws.bytes = 0;
-    }
-    if (hipMalloc(&ws.ptr, size_t(bytes)) != hipSuccess) {
-      (void)hipGetLastError();
-      ws.ptr = nullptr;
-      return PPA_ERR_WORKSPACE;
-    }
-    ws.bytes = bytes;
-  }
-  *out = ws.ptr;
-  return PPA_OK;
+Registry& registry() {
+  static Registry r;
+  return r;
 }
+
+// Where a call's split workspace comes from: the (device, stream) registry
+// (grow-only, held for the whole call), or a fixed device buffer the caller
+// passes in (no allocation; calls larger than it are rejected).
+struct WsSource {
+  void* fixed = nullptr;
+  int64_t fixed_bytes = 0;
+};
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -83,7 +78,8 @@ struct Q8Scales {
 
 int run(const void* q, const void* k, const void* v, const int32_t* bt, bool paged,
         int64_t history, int32_t rows, int32_t hq, int32_t hkv, int32_t d, int32_t ps,
-        int32_t n_splits, void* out, int32_t dtype, hipStream_t stream, const Q8Scales* q8 = nullptr) {
+        int32_t n_splits, void* out, int32_t dtype, hipStream_t stream, const Q8Scales* q8 = nullptr,
+        const WsSource& wsrc = WsSource()) {
   Shape shape{history, rows, hq, hkv, d, ps, dtype};
   shape.q8 = q8 ? 1 : 0;
   int rc = check_shape(shape);
@@ -105,15 +101,25 @@ int run(const void* q, const void* k, const void* v, const int32_t* bt, bool pag
   if (rc != PPA_OK) return rc;
   if (plan.workspace_bytes > max_workspace_bytes()) return PPA_ERR_WORKSPACE;
 
-  if (paged && env_validate()) {
+  if (wsrc.fixed && plan.workspace_bytes > wsrc.fixed_bytes) return PPA_ERR_WORKSPACE;
+
+  if (paged && !wsrc.fixed && env_validate()) {
     rc = validate_block_table(bt, (history + rows + ps - 1) / ps, stream);
     if (rc != PPA_OK) return rc;
   }
 
+  // The stream's workspace stays held (lease) until both kernels are enqueued.
   void* ws = nullptr;
+  Registry::Lease lease;
   if (plan.n_splits > 1) {
-    rc = get_workspace(stream, plan.workspace_bytes, &ws);
-    if (rc != PPA_OK) return rc;
+    if (wsrc.fixed) {
+      ws = wsrc.fixed;
+    } else {
+      int dev = 0;
+      if (hipGetDevice(&dev) != hipSuccess) return PPA_ERR_HIP;
+      if (!registry().acquire({dev, stream}, plan.workspace_bytes, &lease)) return PPA_ERR_WORKSPACE;
+      ws = lease.ptr();
+    }
   }
   const int64_t pairs = int64_t(rows) * hq;
   const int64_t o_bytes = (int64_t(plan.n_splits) * pairs * d * 4 + 255) / 256 * 256;
@@ -227,9 +233,12 @@ int run_varlen(const void* q, const void* k, const void* v, const int32_t* bt, i
     if (rc != PPA_OK) return rc;
   }
   void* ws = nullptr;
+  Registry::Lease lease;
   if (plan.n_splits > 1) {
-    rc = get_workspace(stream, plan.workspace_bytes, &ws);
-    if (rc != PPA_OK) return rc;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return PPA_ERR_HIP;
+    if (!registry().acquire({dev, stream}, plan.workspace_bytes, &lease)) return PPA_ERR_WORKSPACE;
+    ws = lease.ptr();
   }
   const int64_t pairs = int64_t(total_rows) * hq;
   const int64_t o_bytes = (int64_t(plan.n_splits) * pairs * d * 4 + 255) / 256 * 256;
@@ -286,18 +295,18 @@ int run_varlen(const void* q, const void* k, const void* v, const int32_t* bt, i
 int run_pieces(const void* q, const void* k, const void* v, const int32_t* bt, bool paged,
                int64_t history, int32_t rows, int32_t piece_rows, int32_t hq, int32_t hkv,
                int32_t d, int32_t ps, int32_t n_splits, void* out, int32_t dtype,
-               hipStream_t stream, const Q8Scales* q8 = nullptr) {
+               hipStream_t stream, const Q8Scales* q8 = nullptr, const WsSource& wsrc = WsSource()) {
   if (piece_rows < 0) return PPA_ERR_BAD_SHAPE;
   Shape shape{history, rows, hq, hkv, d, ps, dtype};
   int rc = check_shape(shape);
   if (rc != PPA_OK) return rc;
   if (piece_rows == 0 || piece_rows >= rows)
-    return run(q, k, v, bt, paged, history, rows, hq, hkv, d, ps, n_splits, out, dtype, stream, q8);
+    return run(q, k, v, bt, paged, history, rows, hq, hkv, d, ps, n_splits, out, dtype, stream, q8, wsrc);
   const int64_t row_bytes = int64_t(hq) * d * 2;
   for (int32_t r0 = 0; r0 < rows; r0 += piece_rows) {
     const int32_t n = rows - r0 < piece_rows ? rows - r0 : piece_rows;
     rc = run(static_cast<const char*>(q) + r0 * row_bytes, k, v, bt, paged, history + r0, n, hq,
-             hkv, d, ps, n_splits, static_cast<char*>(out) + r0 * row_bytes, dtype, stream, q8);
+             hkv, d, ps, n_splits, static_cast<char*>(out) + r0 * row_bytes, dtype, stream, q8, wsrc);
     if (rc != PPA_OK) return rc;
   }
   return PPA_OK;
@@ -452,13 +461,13 @@ int paged_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v
 }
 
 int paged_prefill_release_workspaces(void) {
-  std::lock_guard<std::mutex> lock(ppa::g_ws_mutex);
-  int rc = PPA_OK;
-  for (auto& kv : ppa::g_ws) {
-    if (kv.second.ptr && hipFree(kv.second.ptr) != hipSuccess) rc = PPA_ERR_HIP;
-  }
-  ppa::g_ws.clear();
-  return rc;
+  return ppa::registry().release_all() ? PPA_OK : PPA_ERR_HIP;
+}
+
+int64_t paged_prefill_workspace_bytes(ppa_stream_t stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PPA_ERR_HIP;
+  return ppa::registry().capacity({dev, reinterpret_cast<hipStream_t>(stream)});
 }
 
 }  // extern "C"

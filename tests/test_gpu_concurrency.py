@@ -72,3 +72,44 @@ def test_two_threads_on_two_streams():
         assert len(got) == 6 * len(refs)
         for j, out in enumerate(got):
             assert _gpu.bits_equal(out, refs[j % len(refs)]), f"thread {key} call {j}"
+
+
+def test_two_threads_on_one_stream():
+    """Two host threads calling on the same stream at once: a call holds the
+    stream's workspace until its merge kernel is enqueued, so one call's
+    partials are never overwritten by the other thread's attention kernel
+    before its merge reads them, also while the workspace grows."""
+    import torch
+    print("case concurrency: two threads, one stream, 4 shapes x 6 rounds each", flush=True)
+    ca, cb = _cases(SEQ_A, 300), _cases(SEQ_B, 400)
+    ref_a = [_call(c, d, s, None) for c, d, s in ca]
+    ref_b = [_call(c, d, s, None) for c, d, s in cb]
+    torch.cuda.synchronize()
+    shared = torch.cuda.Stream()                 # default priority
+    start = threading.Barrier(2)
+    results = {"a": [], "b": []}
+    errors = []
+
+    def worker(key, cases):
+        try:
+            start.wait()
+            with torch.cuda.stream(shared):
+                for _ in range(6):
+                    for c, d, s in cases:
+                        results[key].append(_call(c, d, s, shared))
+        except Exception as e:  # reported below, in the main thread
+            errors.append(e)
+
+    ta = threading.Thread(target=worker, args=("a", ca))
+    tb = threading.Thread(target=worker, args=("b", cb))
+    ta.start()
+    tb.start()
+    ta.join()
+    tb.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for key, refs in (("a", ref_a), ("b", ref_b)):
+        got = results[key]
+        assert len(got) == 6 * len(refs)
+        for j, out in enumerate(got):
+            assert _gpu.bits_equal(out, refs[j % len(refs)]), f"thread {key} call {j}"

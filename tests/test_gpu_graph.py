@@ -52,3 +52,53 @@ def test_captured_piece_loop_replays_match_eager_calls():
         torch.cuda.synchronize()
         assert _gpu.bits_equal(got, eager), f"replay {rep}"
         print(f"  replay {rep}: equal to the eager call", flush=True)
+
+
+def test_replay_after_the_stream_workspace_grew():
+    """A graph captured with a split call keeps working after later, larger
+    calls on the same stream have grown its workspace (the smaller buffer is
+    retired, not freed): each replay equals the eager call bit for bit."""
+    import torch
+    case = synth.make_case("graph_grow", 2048, 128, 16, 2, 256, 16, "f16", seed=33)
+    big = synth.make_case("graph_big", 4096, 512, 16, 2, 256, 16, "f16", seed=34)
+    print("case graph_grow: H=2048 R=128 16/2 d256 f16 S=4 captured; H=4096 R=512 S=8 between replays",
+          flush=True)
+    d = _gpu.dev_case(case, contiguous=False)
+    db = _gpu.dev_case(big, contiguous=False)
+    s = torch.cuda.Stream()                      # default priority
+    out = torch.empty_like(d["q"])
+    out_big = torch.empty_like(db["q"])
+
+    def call(stream):
+        pkg.paged_prefill_attention(d["q"], d["k_pages"], d["v_pages"], d["block_table"], case.history,
+                                    n_splits=4, out=out, stream=stream)
+
+    def call_big(stream, splits):
+        pkg.paged_prefill_attention(db["q"], db["k_pages"], db["v_pages"], db["block_table"], big.history,
+                                    n_splits=splits, out=out_big, stream=stream)
+
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call(s)
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call(s)
+    torch.cuda.synchronize()
+    eager = pkg.paged_prefill_attention(d["q"], d["k_pages"], d["v_pages"], d["block_table"], case.history,
+                                        n_splits=4)
+    torch.cuda.synchronize()
+    before = pkg.paged_prefill_workspace_bytes(stream=s)
+    for rep, splits in enumerate((8, 16)):
+        with torch.cuda.stream(s):
+            call_big(s, splits)                  # grows the capture stream's workspace
+        s.synchronize()
+        grown = pkg.paged_prefill_workspace_bytes(stream=s)
+        assert grown > before, (before, grown)
+        before = grown
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert _gpu.bits_equal(out, eager), f"replay after growth {rep}"
+        print(f"  replay after growth to {grown} bytes: equal to the eager call", flush=True)
