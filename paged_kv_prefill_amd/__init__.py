@@ -71,11 +71,23 @@ _SIGNATURES = {
 
 
 def lib():
-    """The loaded library (raises if it is not built)."""
+    """The loaded library (raises if it is not built).
+
+    torch is imported first: its wheel carries its own HIP runtime
+    (torch/lib/libamdhip64.so, soname libamdhip64.so.7).  Loaded after the
+    library, whose dependency resolves to the system runtime, torch's copy
+    would be a second HIP runtime in the process, and the streams and device
+    memory torch hands the library would belong to the other one (launches on
+    them fail).  Loaded before it, the library's dependency resolves to
+    torch's runtime by soname: one runtime."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is not built: run `python -c 'import __graft_entry__ as g; g.build()'`")
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         handle = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in _SIGNATURES.items():
             fn = getattr(handle, name)

@@ -68,7 +68,8 @@ def build(verbose=False, resource_usage=False, jobs=None):
     for src, vgpr_form in KERNEL_SOURCES:
         kern_obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
         steps.append(([HIPCC, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, "-mllvm",
-                       "-amdgpu-mfma-vgpr-form=" + vgpr_form, *extra, "-c", os.path.join(CSRC, src), "-o", kern_obj],
+                       "-amdgpu-mfma-vgpr-form=" + vgpr_form, f"-DPPA_MFMA_AGPR_FORM={1 - int(vgpr_form)}",
+                       *extra, "-c", os.path.join(CSRC, src), "-o", kern_obj],
                       kern_obj))
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD_DIR, src.replace(".cpp", ".o"))

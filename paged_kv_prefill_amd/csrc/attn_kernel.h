@@ -36,8 +36,9 @@
 //     keys, so a row max needs only one cross-lane exchange
 //     (v_permlane32_swap) with the lane holding the other 32 keys.
 //   * Softmax weights exp2(s c - m_ref) in fp32 (scale * log2 e folded into
-//     one FMA before v_exp_f32) against a fixed per-row reference, so the
-//     output accumulators are never rescaled (see kRefMarginLog2 below).
+//     one FMA before v_exp_f32) against a per-row integer reference that only
+//     moves when a weight would overflow (see kSumLimit below), so the output
+//     accumulators are rescaled only then, by an exact power of two.
 //   * O^T += V^T P^T on the same MFMA: V^T is read with ds_read_b64_tr_b16,
 //     which transposes 16-bit elements across lanes, so V stays row-major in
 //     LDS; P's registers are already the B operand's layout.
@@ -190,6 +191,32 @@ __device__ __forceinline__ float sum_with_partner(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);  // same order on both lanes
 }
 
+// acc *= alpha for an output accumulator tile.  Translation units built with
+// MFMA results in AGPRs (PPA_MFMA_AGPR_FORM) keep the accumulators there:
+// VALU instructions cannot read AGPRs, and plain C++ would move the whole
+// tile through VGPRs and make the allocator spill, so each element is read,
+// scaled and written back in place.  The nops before the first read cover
+// the wait an MFMA result needs before an accumulator read (at most 18 wait
+// states), those after each write the wait before an MFMA reads it.
+__device__ __forceinline__ void scale_acc(f32x16& acc, float alpha) {
+#if defined(PPA_MFMA_AGPR_FORM) && PPA_MFMA_AGPR_FORM
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float x = acc[r], t;
+    if (r == 0)
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\tv_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %2, %1\n\t"
+                   "v_accvgpr_write_b32 %0, %1\n\ts_nop 4"
+                   : "+a"(x), "=&v"(t) : "v"(alpha));
+    else
+      asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %2, %1\n\tv_accvgpr_write_b32 %0, %1\n\ts_nop 4"
+                   : "+a"(x), "=&v"(t) : "v"(alpha));
+    acc[r] = x;
+  }
+#else
+  acc *= alpha;
+#endif
+}
+
 // How K/V rows are addressed.  Contig: [ctx][Hkv][d].  Paged: pages of
 // `page_size` tokens, each [page_size][Hkv][d].  PageBig: pages of 64 tokens or
 // more, so a 64-key tile lies in one page.  Page16: pages of 16 or 32 tokens,
@@ -200,19 +227,21 @@ __device__ __forceinline__ float sum_with_partner(float x) {
 // tile to tile.  PageLane: smaller pages; every row looks up its own page.
 enum class Addr { Contig, PageBig, Page16, Page8, PageLane };
 
-// The softmax weights are exp2(s c - m_ref) with a fixed reference m_ref per
-// query vector instead of a running max, so the output accumulators are never
-// rescaled inside the key loop.  The reference is the max of the split's first
-// tile (a query vector that sees any key of the split sees its first key).
-// Later weights may exceed 1; fp16 or bf16 P and fp32 O and l hold them as long
-// as none overflows.  An fp16 weight past the format's range rounds to
-// infinity and makes the lane's sum l infinite; a sum past kSumLimit bounds
-// the weights of the other types.  The first pass checks only that, once, at
-// its end.  If any lane of the workgroup fails, a second pass tracks the
-// running max of every tile, and if some query vector's max passes m_ref + 15
-// (log2 domain) a third pass takes the exact max as reference.  Either way the
-// result is the same softmax; only rounding differs.
-constexpr float kRefMarginLog2 = 15.0f;
+// The softmax weights are exp2(s c - m_ref) against a reference m_ref per
+// query vector that is an integer (log2 domain) and moves only when it must,
+// instead of the running max of every tile, so the output accumulators are
+// not rescaled on every tile and most tiles compute no max at all.  The first
+// reference is the ceiling of the max of the split's first tile (a query
+// vector that sees any key of the split sees its first key).  Later weights
+// may exceed 1; fp16 or bf16 P and fp32 O and l hold them as long as none
+// overflows.  After each tile the row sums are checked: an fp16 weight past
+// the format's range rounds to infinity and makes the sum infinite, and a sum
+// past kSumLimit bounds the weights of bf16.  Where a query vector fails, its
+// wave takes the tile's max, raises the reference to its ceiling, scales O and
+// l by 2^(old - new) (exact: both are integers) and recomputes the tile's
+// weights.  Because every reference is an integer, a weight's fp16/bf16
+// rounding does not depend on which reference (which split) it was computed
+// against: exp2(x - n) is 2^-n exp2(x) in both formats' normal range.
 constexpr float kSumLimit = 0x1p64f;
 
 // Q8: K and V pages hold 8-bit quants with an fp16 scale per 32 values along
@@ -327,11 +356,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
   f32x16 o[QB][DB];
-  float m_ref[QB], m_true[QB], l[QB];  // per query block:
+  float m_ref[QB], l[QB];  // per query block:
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    m_ref[qb] = kNegInf;   // softmax reference, scaled log2 domain
-    m_true[qb] = kNegInf;  // running max of the scaled scores
+    m_ref[qb] = kNegInf;   // softmax reference, scaled log2 domain, an integer once set
     l[qb] = 0.f;           // this lane's share of the softmax sum
   }
   const float c = a.scale_log2;
@@ -580,6 +608,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   // the interleave.  The two halves are independent: PV reads pb, softmax
   // writes pb_new.
   vec8 pb[QB][4], pb_new[QB][4];
+  float rs[QB];   // this lane's sum of the tile's rounded weights (pb_new)
   // lds_off(16 kstep + vr (+ 8), 4 db + cc) + within = (vofs1 (vofs2) ^ (db % 2) 64)
   // + (db / 2) 8192 + kstep 2048, vr = 4 h + (lane % 16) / 4, cc = 2 ((lane / 16) % 2) + (lane % 4) / 2
   const int v_r = 4 * h + ((lane & 15) >> 2);
@@ -607,7 +636,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     static_assert(32 % PER == 0, "a max step stays within one query block");
     auto elem = [&](int e) __attribute__((always_inline)) -> float { return sc[e >> 5][(e >> 4) & 1][e & 15]; };
     float part[MAX_STEPS > 0 ? MAX_STEPS : 1];
-    float base[QB], rs[QB], p32[ET];
+    float base[QB], p32[ET];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       base[qb] = (TRACK || m_ref[qb] == kNegInf) ? 0.f : m_ref[qb];
@@ -626,9 +655,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             float m = part[qb * SPB];
 #pragma unroll
             for (int j = 1; j < SPB; ++j) m = fmaxf(m, part[qb * SPB + j]);
-            const float mxs = max_with_partner(m) * c;
-            m_true[qb] = fmaxf(m_true[qb], mxs);
-            if (m_ref[qb] == kNegInf) m_ref[qb] = mxs;  // first tile with a visible key (O and l are still 0)
+            // the split's first tile (O and l are still 0): the first reference
+            m_ref[qb] = ceilf(max_with_partner(m) * c);
             base[qb] = m_ref[qb] == kNegInf ? 0.f : m_ref[qb];
           }
         }
@@ -659,6 +687,46 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
       valu(i);
       step_hook(i);
       __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // After a tile's weights: where a query vector's sum overflowed (see
+  // kSumLimit), its wave raises the reference to the ceiling of the tile's
+  // max, scales O and l (tiles up to the previous one) by the exact power of
+  // two 2^(old - new) and recomputes this tile's weights.  Then this tile's
+  // weights become the next PV's operand.
+  auto commit_tile = [&]() __attribute__((always_inline)) {
+    bool over = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) over |= !(l[qb] + rs[qb] <= kSumLimit);
+    if (__builtin_expect(__ballot(over) != 0, 0)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = sc[qb][0][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[qb][kb][r]);
+        const float m_new = fmaxf(m_ref[qb], ceilf(max_with_partner(mx) * c));
+        if (m_new != kNegInf && m_new != m_ref[qb]) {
+          const float alpha = __builtin_amdgcn_exp2f(m_ref[qb] - m_new);   // 2^-k, 0 if m_ref was -inf
+          l[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) scale_acc(o[qb][db], alpha);
+          m_ref[qb] = m_new;
+        }
+        const float base = m_ref[qb] == kNegInf ? 0.f : m_ref[qb];
+        float p32[32];
+        rs[qb] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+          p32[e] = __builtin_amdgcn_exp2f(fmaf(sc[qb][e >> 4][e & 15], c, -base));
+          if ((e & 7) == 7) {
+            pb_new[qb][e >> 3] = M::from_f32(p32 + (e & ~7));
+            rs[qb] = M::sum8(pb_new[qb][e >> 3], rs[qb]);
+          }
+        }
+      }
     }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -704,7 +772,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   // it gained 1% on a 2048-row chunk and lost 2% on 128-row pieces, and the
   // VGPR-form build of that code crashes the compiler).
   constexpr bool ONE_BARRIER = !Q8 && D <= 128;
-  auto body = [&](int it, auto masked, auto parity) __attribute__((always_inline)) {
+  auto body = [&](int it, auto masked, auto track, auto parity) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
     constexpr bool ODD = decltype(parity)::value;  // it is odd
     const int t0 = k0 + it * kTK;
@@ -773,7 +841,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
       __builtin_amdgcn_sched_barrier(0);   // keep the two phases apart
     }
     // PV(it-1) with the previous weights, fused with this tile's softmax.
-    pv_softmax(ODD ? vbuf0 : vbuf1, masked, [&](int i) {
+    pv_softmax(ODD ? vbuf0 : vbuf1, track, [&](int i) {
       if constexpr (Q8) {
         constexpr int EVERY = 4 * DB / NQ;
         if (i % EVERY == 0)
@@ -785,6 +853,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
           issue_one(it, pv, vb, true, ODD ? vbuf1 : vbuf0, i / EVERY, std::bool_constant<!MASKED>{});
       }
     });
+    commit_tile();
     if constexpr (Q8) {
       // Widen K(it+1) and V(it): their buffers' last readers (QK(it-1) and
       // PV(it-2)) finished before this body's barrier.
@@ -797,83 +866,54 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   // Tiles in even/odd pairs so that each body has its buffers fixed at compile
   // time and the output accumulators flow through one chain of code.
   auto run = [&](int& it, int end, auto masked) __attribute__((always_inline)) {
+    const std::false_type no_track{};
     if (it < end && (it & 1)) {
-      body(it, masked, std::true_type{});
+      body(it, masked, no_track, std::true_type{});
       ++it;
     }
     for (; it + 1 < end; it += 2) {
-      body(it, masked, std::false_type{});
-      body(it + 1, masked, std::true_type{});
+      body(it, masked, no_track, std::false_type{});
+      body(it + 1, masked, no_track, std::true_type{});
     }
     if (it < end) {
-      body(it, masked, std::false_type{});
+      body(it, masked, no_track, std::false_type{});
       ++it;
     }
   };
-  // One pass over the split's tiles.  The masked body also takes each tile's
-  // max; the fast body does not.  Tile 0 always runs in the masked body: a
-  // query vector that sees any key of the split sees its first key, so tile 0
-  // sets every reference.  With track_all (the second pass, after the first
-  // one overflowed) every tile runs in the masked body.
-  auto run_pass = [&](bool track_all) __attribute__((always_inline)) {
-    int it = 0;
-    if (!track_all) {
-      run(it, n_tiles > 0 ? 1 : 0, std::true_type{});
-      run(it, n_fast, std::false_type{});
-    }
-    run(it, n_tiles, std::true_type{});
-  };
-  __shared__ int wg_redo[kWaves];
-  for (int pass = 0; pass < 3; ++pass) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[qb][db] = f32x16{};
+    for (int db = 0; db < DB; ++db) o[qb][db] = f32x16{};
 #pragma unroll
-      for (int kstep = 0; kstep < 4; ++kstep) pb[qb][kstep] = vec8{};
-      l[qb] = 0.f;
-    }
-    for (int i = tid; i < Gm::TILE_BYTES / 16; i += 256) *LDS_PTR(u32x4, vbuf1 + i * 16) = u32x4{0u, 0u, 0u, 0u};
-    if (n_tiles > 0) {
-      pg0 = pages(0);
-      if constexpr (Q8) {
+    for (int kstep = 0; kstep < 4; ++kstep) pb[qb][kstep] = vec8{};
+  }
+  for (int i = tid; i < Gm::TILE_BYTES / 16; i += 256) *LDS_PTR(u32x4, vbuf1 + i * 16) = u32x4{0u, 0u, 0u, 0u};
+  if (n_tiles > 0) {
+    pg0 = pages(0);
+    if constexpr (Q8) {
 #pragma unroll
-        for (int i = 0; i < NQ; ++i) issue_q8(0, pg0, TileBases{}, false, kbuf0, i, std::false_type{});
-        const uint32_t s0 = load_scales(0, pg0, false);
-        pg1 = pages(1);
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        convert_q8(kbuf0, s0);
-      } else {
-        issue(0, pg0, false, kbuf0);
-        pg1 = pages(1);
-        // K(0) is the only load in flight: the first body's vmcnt(LPW) would not wait for it.
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      }
-    }
-    run_pass(pass == 1);
-    if (n_tiles > 0) {
+      for (int i = 0; i < NQ; ++i) issue_q8(0, pg0, TileBases{}, false, kbuf0, i, std::false_type{});
+      const uint32_t s0 = load_scales(0, pg0, false);
+      pg1 = pages(1);
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      __syncthreads();
-      if ((n_tiles - 1) & 1) pv_last(vbuf1);
-      else pv_last(vbuf0);
+      convert_q8(kbuf0, s0);
+    } else {
+      issue(0, pg0, false, kbuf0);
+      pg1 = pages(1);
+      // K(0) is the only load in flight: the first body's vmcnt(LPW) would not wait for it.
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     }
-    if (pass == 2) break;
-    // Pass 0: did a weight overflow (an infinite fp16 weight, or a sum past
-    // kSumLimit)?  Pass 1: did a running max outgrow its reference?
-    bool outgrown = false;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-      outgrown |= pass == 0 ? !(l[qb] <= kSumLimit) : m_true[qb] > m_ref[qb] + kRefMarginLog2;
-    const bool redo = __ballot(outgrown) != 0;
-    if (lane == 0) wg_redo[wave] = redo;
+    // Tile 0 runs in the masked body and takes its max (the first reference);
+    // then the fast body (no mask, no clamp) while both its tile and the one
+    // it loads lie below the first row's last key; then the masked body.
+    body(0, std::true_type{}, std::true_type{}, std::false_type{});
+    int it = 1;
+    run(it, n_fast, std::false_type{});
+    run(it, n_tiles, std::true_type{});
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    const bool any = wg_redo[0] | wg_redo[1] | wg_redo[2] | wg_redo[3];
-    __syncthreads();
-    if (!any) break;
-    if (pass == 1) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) m_ref[qb] = m_true[qb];  // the exact max: every weight is at most 1 now
-    }
+    if ((n_tiles - 1) & 1) pv_last(vbuf1);
+    else pv_last(vbuf0);
   }
 
   // Epilogue: combine the two lanes' sums; lane holds d = 32 db + 8 q + 4 h + 0..3.
