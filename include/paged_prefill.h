@@ -225,6 +225,29 @@ int paged_kv_append_q8(const void* k_new, const void* v_new, void* k_quant, void
                        int32_t rows, int32_t n_kv_heads, int32_t head_dim, int32_t page_size,
                        int32_t dtype, ppa_stream_t stream);
 
+/*
+ * paged_prefill_attention_pieces for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation, plan, kernels and bits, but the
+ * split workspace is a fixed 64 MiB device array inside the library (one per
+ * GPU, held until the process ends) instead of the per-stream workspace, and
+ * the call never allocates or frees device memory.  A call whose plan needs
+ * more than 64 MiB of workspace (plan.workspace_bytes, per piece) returns
+ * PPA_ERR_WORKSPACE before enqueuing anything; planner-chosen plans need at
+ * most 2048 * Hq * (d + 1) * 4 bytes, which fits for Hq * d <= 8128.
+ * Every call on one GPU shares that GPU's array and leaves its last
+ * partials there: calls that overlap on one GPU (several streams, or several
+ * threads) race on it and must be serialized by the caller.  PPA_VALIDATE is
+ * not applied here.  The first call on a device looks the array's address up
+ * (hipGetSymbolAddress) and must not be under stream capture.
+ */
+int paged_prefill_attention_pieces_noalloc(const void* q, const void* k_pages, const void* v_pages,
+                                           const int32_t* block_table, int64_t history_len,
+                                           int32_t chunk_rows, int32_t piece_rows, int32_t n_q_heads,
+                                           int32_t n_kv_heads, int32_t head_dim, int32_t page_size,
+                                           int32_t n_splits, void* out, int32_t dtype,
+                                           ppa_stream_t stream);
+
 /* Contiguous-KV counterpart of paged_prefill_attention_pieces. */
 int contiguous_prefill_attention_pieces(const void* q, const void* k, const void* v,
                                         int64_t history_len, int32_t chunk_rows,

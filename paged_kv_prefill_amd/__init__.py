@@ -51,6 +51,8 @@ _SIGNATURES = {
     "paged_prefill_attention": (_I32, [_VP, _VP, _VP, _VP, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _I32, _VP]),
     "contiguous_prefill_attention": (_I32, [_VP, _VP, _VP, _I64, _I32, _I32, _I32, _I32, _I32, _VP, _I32, _VP]),
     "paged_prefill_attention_pieces": (_I32, [_VP, _VP, _VP, _VP, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _I32, _VP]),
+    "paged_prefill_attention_pieces_noalloc": (_I32, [_VP, _VP, _VP, _VP, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                      _VP, _I32, _VP]),
     "contiguous_prefill_attention_pieces": (_I32, [_VP, _VP, _VP, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _I32, _VP]),
     "paged_prefill_plan": (_I32, [_I64, _I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(Plan)]),
     "paged_prefill_split_rule": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
@@ -364,3 +366,26 @@ def paged_prefill_workspace_bytes(stream=None, device=None):
     if rc < 0:
         raise PagedPrefillError(rc, "paged_prefill_workspace_bytes")
     return int(rc)
+
+
+def paged_prefill_attention_noalloc(q, k_pages, v_pages, block_table, history_len, n_splits=0, out=None,
+                                    piece_rows=0, stream=None):
+    """paged_prefill_attention (pieces form) with the split workspace in the
+    library's fixed device array: no device allocation by the library (out
+    must be given to avoid torch's).  Overlapping calls on one GPU race on
+    that array."""
+    _check_kinds(q, (k_pages, v_pages), out, int32=(block_table,))
+    rows, n_q_heads, head_dim = q.shape
+    _, page_size, n_kv_heads, kd = k_pages.shape
+    _check_table(block_table, history_len, rows, page_size)
+    _need_cuda(q, k_pages, v_pages, block_table, out)
+    if kd != head_dim or tuple(v_pages.shape) != tuple(k_pages.shape):
+        raise ValueError("k_pages/v_pages shape mismatch")
+    if out is None:
+        out = q.new_empty(q.shape)
+    rc = lib().paged_prefill_attention_pieces_noalloc(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), int(history_len), int(rows), int(piece_rows),
+        int(n_q_heads), int(n_kv_heads), int(head_dim), int(page_size), int(n_splits), _ptr(out), _dtype_code(q),
+        _stream_handle(stream, q.device))
+    _check(rc, "paged_prefill_attention_pieces_noalloc")
+    return out

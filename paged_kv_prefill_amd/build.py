@@ -42,6 +42,7 @@ KERNEL_SOURCES = (
     ("attention_q8_d64_d128.hip", os.environ.get("PPA_MFMA_VGPR_FORM_Q8", "0")),
     ("attention_q8_d256.hip", os.environ.get("PPA_MFMA_VGPR_FORM_Q8", "0")),
     ("kv_append.hip", "0"),
+    ("noalloc.hip", "0"),
 )
 HOST_SOURCES = ("api.cpp", "plan.cpp")
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}"]

@@ -41,11 +41,10 @@ Registry& registry() {
 }
 
 // Where a call's split workspace comes from: the (device, stream) registry
-// (grow-only, held for the whole call), or a fixed device buffer the caller
-// passes in (no allocation; calls larger than it are rejected).
+// (grow-only, held for the whole call), or the library's fixed device array
+// (no allocation; calls that need more than it holds are rejected).
 struct WsSource {
-  void* fixed = nullptr;
-  int64_t fixed_bytes = 0;
+  bool fixed_array = false;
 };
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -101,9 +100,9 @@ int run(const void* q, const void* k, const void* v, const int32_t* bt, bool pag
   if (rc != PPA_OK) return rc;
   if (plan.workspace_bytes > max_workspace_bytes()) return PPA_ERR_WORKSPACE;
 
-  if (wsrc.fixed && plan.workspace_bytes > wsrc.fixed_bytes) return PPA_ERR_WORKSPACE;
+  if (wsrc.fixed_array && plan.workspace_bytes > kStaticScratchBytes) return PPA_ERR_WORKSPACE;
 
-  if (paged && !wsrc.fixed && env_validate()) {
+  if (paged && !wsrc.fixed_array && env_validate()) {
     rc = validate_block_table(bt, (history + rows + ps - 1) / ps, stream);
     if (rc != PPA_OK) return rc;
   }
@@ -112,8 +111,9 @@ int run(const void* q, const void* k, const void* v, const int32_t* bt, bool pag
   void* ws = nullptr;
   Registry::Lease lease;
   if (plan.n_splits > 1) {
-    if (wsrc.fixed) {
-      ws = wsrc.fixed;
+    if (wsrc.fixed_array) {
+      rc = static_scratch(&ws);
+      if (rc != PPA_OK) return rc;
     } else {
       int dev = 0;
       if (hipGetDevice(&dev) != hipSuccess) return PPA_ERR_HIP;
@@ -468,6 +468,19 @@ int64_t paged_prefill_workspace_bytes(ppa_stream_t stream) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return PPA_ERR_HIP;
   return ppa::registry().capacity({dev, reinterpret_cast<hipStream_t>(stream)});
+}
+
+int paged_prefill_attention_pieces_noalloc(const void* q, const void* k_pages, const void* v_pages,
+                                           const int32_t* block_table, int64_t history_len,
+                                           int32_t chunk_rows, int32_t piece_rows, int32_t n_q_heads,
+                                           int32_t n_kv_heads, int32_t head_dim, int32_t page_size,
+                                           int32_t n_splits, void* out, int32_t dtype,
+                                           ppa_stream_t stream) {
+  ppa::WsSource src;
+  src.fixed_array = true;
+  return ppa::run_pieces(q, k_pages, v_pages, block_table, true, history_len, chunk_rows, piece_rows,
+                         n_q_heads, n_kv_heads, head_dim, page_size, n_splits, out, dtype,
+                         reinterpret_cast<hipStream_t>(stream), nullptr, src);
 }
 
 }  // extern "C"

@@ -110,4 +110,10 @@ hipError_t launch_attention_d64_d128_qb1(const AttnArgs& a, int head_dim, int dt
 hipError_t launch_attention_q8_d64_d128(const AttnArgs& a, int head_dim, int dtype, int grid, hipStream_t stream);
 hipError_t launch_attention_q8_d256(const AttnArgs& a, int dtype, int grid, hipStream_t stream);
 
+// Size of the fixed scratch array (noalloc.hip), one per device.
+constexpr int64_t kStaticScratchBytes = int64_t(64) << 20;   // 64 MiB
+// The current device's fixed scratch array: its device address (looked up
+// once per device).  PPA_OK or PPA_ERR_HIP.
+int static_scratch(void** ptr);
+
 }  // namespace ppa
