@@ -137,6 +137,19 @@ def cpu_baseline(cases, budget_s=15.0):
             "seconds": total_s, "cpu_model": cpu_model, "blas": blas}
 
 
+def stated_flops(case):
+    """FLOPs in the convention 4 * rows * ctx * head_dim * n_q_heads with ctx =
+    history + rows of each call (the chunk's pieces summed): counts the masked
+    upper triangle of each call's own rows, 3% more than the exact count at
+    32K, 0.8% at 128K."""
+    p = case.piece_rows or case.rows
+    total = 0
+    for r0 in range(0, case.rows, p):
+        r = min(p, case.rows - r0)
+        total += 4 * r * (case.history + r0 + r) * case.head_dim * case.n_q_heads
+    return total
+
+
 def kv_bytes(case):
     """Algorithmic K+V bytes of one chunk: every key read once."""
     return (case.history + case.rows) * case.n_kv_heads * case.head_dim * 2 * 2
@@ -180,18 +193,29 @@ def timed_pair(fa, fb, reps, stream):
             float(np.median([e[2].elapsed_time(e[3]) for e in evs])))
 
 
+def timed_round_robin(fns, reps, stream):
+    """Median ms of each of several calls, timed in rounds (every call once
+    per round, in turn) so that clock drift over the run hits all alike."""
+    import numpy as np
+    import torch
+    for f in fns.values():
+        f()
+    evs = {k: [] for k in fns}
+    for _ in range(reps):
+        for k, f in fns.items():
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            f()
+            b.record(stream)
+            evs[k].append((a, b))
+    torch.cuda.synchronize()
+    return {k: round(float(np.median([a.elapsed_time(b) for a, b in v])), 4) for k, v in evs.items()}
+
+
 def extra_measurements(chunks, paged, contig, pkg, synth, to_dev, stream, reps=10):
     """Cold-cache medians, the short-history sweep and the split sweep."""
     import torch
     out = {}
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=stream.device)   # 512 MB
-
-    def flush():
-        scratch.fill_(1)
-
-    out["cold_cache_ms_median"] = {c["name"]: round(timed(lambda: paged(c), reps, stream, flush)[0], 4)
-                                   for c in chunks}
-    del scratch
     sweep = {}
     for h in (1024, 2048, 4096, 8192, 16384):
         case = synth.config_case(f"sweep_{h}")
@@ -213,6 +237,26 @@ def extra_measurements(chunks, paged, contig, pkg, synth, to_dev, stream, reps=1
                                                                                   oc.view(torch.int16)))}
         del q, kp, vp, bt, k, v, o, oc
     out["history_sweep_2048_rows"] = sweep
+    # The Qwen-like chunk (8K history, 512 rows, values x 0.5), paged against contiguous.
+    case = synth.config_case("qwen_like")
+    q, kp, vp = to_dev(case.q, torch.float16), to_dev(case.k_pages, torch.float16), to_dev(case.v_pages, torch.float16)
+    bt = torch.from_numpy(case.block_table).to(stream.device)
+    k, v = to_dev(case.k_contig, torch.float16), to_dev(case.v_contig, torch.float16)
+    o, oc = torch.empty_like(q), torch.empty_like(q)
+    fp = lambda: pkg.paged_prefill_attention(q, kp, vp, bt, case.history, out=o, stream=stream)
+    fc = lambda: pkg.contiguous_prefill_attention(q, k, v, case.history, out=oc, stream=stream)
+    for _ in range(3):
+        fp()
+        fc()
+    mp, mc = timed_pair(fp, fc, 2 * reps, stream)
+    fl = synth.exact_flops(case.history, case.rows, case.n_q_heads, case.head_dim)
+    out["qwen_like_8k_512_rows"] = {"ms_median": round(mp, 4), "tflops": round(fl / (mp * 1e-3) / 1e12, 1),
+                                    "contiguous_ms_median": round(mc, 4), "paged_over_contiguous": round(mp / mc, 4),
+                                    "splits": pkg.paged_prefill_plan(case.history, case.rows, 16, 2, 256)["n_splits"],
+                                    "bitwise_equal_to_contiguous": bool(torch.equal(o.view(torch.int16),
+                                                                                    oc.view(torch.int16)))}
+    del q, kp, vp, bt, k, v, o, oc
+    out["peaked_scores"] = peaked_measurements(chunks, paged, pkg, stream, reps)
     # Page-size sweep on the 32K chunk: the same K/V laid out in pages of 1 to
     # 256 tokens (a random page order), paged against contiguous, interleaved.
     c = next((c for c in chunks if c["name"] == "sweep_32768"), None)
@@ -268,15 +312,33 @@ def extra_measurements(chunks, paged, contig, pkg, synth, to_dev, stream, reps=1
     c = next((c for c in chunks if c["name"] == "sweep_32768"), None)
     if c is not None:
         cs = c["case"]
-        res = {}
-        for s in (1, 2, 4, 8, 16, 32):
-            f = lambda: pkg.paged_prefill_attention(c["q"], c["kp"], c["vp"], c["bt"], cs.history, n_splits=s,
-                                                    out=c["out"], stream=stream)
-            f()
-            res[str(s)] = round(timed(f, reps, stream)[0], 4)
+        res = timed_round_robin(
+            {str(sreq): (lambda sreq=sreq: pkg.paged_prefill_attention(c["q"], c["kp"], c["vp"], c["bt"], cs.history,
+                                                                       n_splits=sreq, out=c["out"], stream=stream))
+             for sreq in (1, 2, 4, 8, 16, 32)}, reps, stream)
         out["split_sweep_32k_ms_median"] = res
         out["split_sweep_planner_splits"] = pkg.paged_prefill_plan(cs.history, cs.rows, cs.n_q_heads,
                                                                    cs.n_kv_heads, cs.head_dim)["n_splits"]
+    # The PR's comparison (1 split against the planner) at its piece shapes:
+    # the whole 64K chunk in 256-row pieces and the 128K chunk in 128-row
+    # pieces, every piece at the same requested split count; "planner" is each
+    # piece's own planned count.
+    for name, counts in (("piece_64k", (1, 2, 4, 8, 16, 32)), ("long_128k", (1, 4, 8, 16, 32, 64))):
+        c = next((c for c in chunks if c["name"] == name), None)
+        if c is None:
+            continue
+        cs = c["case"]
+        res = timed_round_robin(
+            {("planner" if sreq == 0 else str(sreq)):
+             (lambda sreq=sreq: pkg.paged_prefill_attention(c["q"], c["kp"], c["vp"], c["bt"], cs.history,
+                                                            n_splits=sreq, out=c["out"], piece_rows=cs.piece_rows,
+                                                            stream=stream))
+             for sreq in counts + (0,)}, reps, stream)
+        best = min(v for k, v in res.items() if k != "planner")
+        out[f"split_sweep_{name}_ms_median"] = res
+        out[f"split_sweep_{name}_planner_splits"] = pkg.paged_prefill_plan(
+            cs.history, cs.piece_rows, cs.n_q_heads, cs.n_kv_heads, cs.head_dim)["n_splits"]
+        out[f"split_sweep_{name}_planner_over_best"] = round(res["planner"] / best, 4)
     # Short appends and decode steps: the first R rows of each chunk as one
     # call on the same history (planner splits).  KV-bound at small R, so
     # reported as K/V bytes per second against HBM peak, with the paged /
@@ -307,6 +369,46 @@ def extra_measurements(chunks, paged, contig, pkg, synth, to_dev, stream, reps=1
     out["varlen"] = varlen_measurements(pkg, synth, stream, reps)
     out["q8_pages"] = q8_measurements(chunks, paged, pkg, synth, stream, reps)
     return out
+
+
+def peaked_measurements(chunks, paged, pkg, stream, reps):
+    """The 32K fp16 and 128K bf16 chunks with peaked scores: q scaled by 4
+    (scores with sigma about 4 instead of 1) and component 0 of every query
+    raised by 8, and eight keys spread over the last quarter of the history
+    with component 0 set to 56, so that for most rows one late key scores
+    12-20 nats (or more) above the split's first tile.  Where a weight would
+    overflow, the wave raises its softmax reference and rescales its
+    accumulators; the time is reported against the same chunk with N(0,1)
+    inputs (calls interleaved)."""
+    import torch
+    res = {}
+    for name in ("sweep_32768", "long_128k"):
+        c = next((c for c in chunks if c["name"] == name), None)
+        if c is None:
+            continue
+        cs = c["case"]
+        q2 = (c["q"].float() * 4.0)
+        q2[:, :, 0] += 8.0
+        q2 = q2.to(c["q"].dtype)
+        kp2 = c["kp"].clone()
+        keys = [cs.history - 1 - (cs.history // 4) * j // 8 for j in range(8)]
+        bt = c["bt"].cpu().numpy()
+        for key in keys:
+            kp2[int(bt[key // cs.page_size]), key % cs.page_size, :, 0] = 56.0
+        o2 = torch.empty_like(c["q"])
+        fpk = lambda: pkg.paged_prefill_attention(q2, kp2, c["vp"], c["bt"], cs.history, out=o2,
+                                                  piece_rows=cs.piece_rows, stream=stream)
+        fn = lambda: paged(c)
+        for _ in range(3):
+            fpk()
+            fn()
+        mp, mn = timed_pair(fpk, fn, reps, stream)
+        res[name] = {"ms_median": round(mp, 4), "normal_inputs_ms_median": round(mn, 4),
+                     "over_normal_inputs": round(mp / mn, 4),
+                     "finite": bool(torch.isfinite(o2.float()).all())}
+        del q2, kp2, o2
+        torch.cuda.empty_cache()
+    return res
 
 
 def q8_measurements(chunks, paged, pkg, synth, stream, reps):
@@ -493,13 +595,26 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
 
+    # The same calls with a cold cache: a 512 MB scratch write (more than the
+    # 256 MB Infinity Cache plus the 8 x 4 MB L2) before each call, outside
+    # its events, so the call reads its K/V from HBM.
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = {c["name"]: timed(lambda: paged(c), max(5, min(n, 10)), stream, lambda: scratch.fill_(1))
+            for c in chunks}
+    del scratch
+    torch.cuda.synchronize()
+
     per_chunk = {}
     for c in chunks:
         ms = np.array([a.elapsed_time(b) for a, b in ev[c["name"]]])
         paged_ms_total += ms.sum()
+        cm = cold[c["name"]]
         rec = {"ms_median": float(np.median(ms)), "ms_p10": float(np.percentile(ms, 10)),
                "ms_p90": float(np.percentile(ms, 90)),
+               "cold_ms_median": cm[0], "cold_ms_p10": cm[1], "cold_ms_p90": cm[2],
                "tflops": c["flops"] / (np.median(ms) * 1e-3) / 1e12,
+               "tflops_cold": c["flops"] / (cm[0] * 1e-3) / 1e12,
+               "tflops_4_rows_ctx_convention": stated_flops(c["case"]) / (np.median(ms) * 1e-3) / 1e12,
                "kv_stream_gbs": kv_bytes(c["case"]) / (np.median(ms) * 1e-3) / 1e9,
                "history": c["case"].history, "piece_rows": c["case"].piece_rows or c["case"].rows,
                "heads": f"{c['case'].n_q_heads}/{c['case'].n_kv_heads}", "head_dim": c["case"].head_dim,
@@ -518,6 +633,7 @@ def main():
     total_flops = sum(c["flops"] for c in chunks)
     step_ms = paged_ms_total / n
     value = total_flops / (step_ms * 1e-3) / 1e12
+    value_cold = total_flops / (sum(cold[c["name"]][0] for c in chunks) * 1e-3) / 1e12
 
     roofline = None
     rc = next((c for c in chunks if c["name"] == ROOFLINE_CHUNK), None)
@@ -549,7 +665,13 @@ def main():
                                "64K (32/4, d128, bf16, 8x256-row pieces) and 128K history (16/2, d256, "
                                "bf16, 16x128-row pieces, pages scattered in a 65536-page pool); paged KV, "
                                "16-token pages in random order",
-                   "chunks": per_chunk, "wall_s": round(wall, 3)},
+                   "chunks": per_chunk, "wall_s": round(wall, 3),
+                   "value_timing": "warm: the K timed steps back to back (each chunk's K/V may still sit in the "
+                                   "256 MB Infinity Cache from the previous step); value_cold and each chunk's "
+                                   "cold_ms_median time the same calls after a 512 MB scratch write",
+                   "value_cold": round(value_cold, 2),
+                   "flop_convention": "exact causal: 4 d Hq (R H + R (R + 1) / 2) per call; "
+                                      "tflops_4_rows_ctx_convention uses 4 R (H + R) d Hq per call"},
         "roofline": roofline,
     }
 

@@ -24,11 +24,18 @@ def short(name, width=100):
 
 
 def kernel_source_hash():
+    """Hash of everything that decides the device code: every HIP translation
+    unit and header under csrc/ and the build's per-file compile options
+    (register form, flags).  Counter records in profiles/ carry it and are
+    used only while it matches."""
+    from paged_kv_prefill_amd import build as _build
     h = hashlib.sha256()
-    # the attention kernels' sources (the counters in profiles/ are theirs)
-    for f in ("attn_kernel.h", "attention.hip", "attention_d64_d128.hip", "attention_d256.hip", "kernels.h"):
-        with open(os.path.join(ROOT, "paged_kv_prefill_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    csrc = os.path.join(ROOT, "paged_kv_prefill_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    h.update(repr((_build.KERNEL_SOURCES, _build.DEVICE_FLAGS, _build.COMMON[:2], _build.ARCH)).encode())
     return h.hexdigest()[:16]
 
 

@@ -230,16 +230,18 @@ def test_split_variance_at_the_pr_shape():
     torch.cuda.empty_cache()
 
 
-def _plant_outlier(case, key, value):
-    """Shift component 0 of every query by +2 and set K[key, :, 0] = value, so
-    key `key` scores about 2 value / sqrt(d) for every row."""
+def _plant_outlier(case, key, value, shift_q=True):
+    """Shift component 0 of every query by +2 (unless shift_q is false: done
+    already) and set K[key, :, 0] = value, so key `key` scores about
+    2 value / sqrt(d) for every row."""
     from paged_kv_prefill_amd.synth import ENCODERS
     import oracle
     dec = oracle.decode_f16 if case.dtype == "f16" else oracle.decode_bf16
     enc = ENCODERS[case.dtype]
-    q = dec(case.q).astype(np.float32)
-    q[:, :, 0] += 2.0
-    case.q = enc(q)
+    if shift_q:
+        q = dec(case.q).astype(np.float32)
+        q[:, :, 0] += 2.0
+        case.q = enc(q)
     k = dec(case.k_contig).astype(np.float32)
     k[key, :, 0] = value
     case.k_contig = enc(k)
@@ -248,22 +250,30 @@ def _plant_outlier(case, key, value):
     return case
 
 
-OUTLIERS = [("late", 80.0), ("first_tile", 80.0), ("late", 40.0), ("late", 64.0), ("late", 72.0)]
+# (where, K[key, 0]): with q[., 0] + 2 the key scores about 2 value / sqrt(128)
+# above the rest, i.e. 0.255 value log2 units: 40 -> 10 (weights stay below
+# fp16's range), 64 -> 16.3 and 72 -> 18.4 (some rows overflow fp16), 80 -> 20.4
+# (every row overflows fp16), 300 -> 76.5 (past the 2^64 bound on bf16 sums).
+OUTLIERS = [("late", 80.0), ("first_tile", 80.0), ("late", 40.0), ("late", 64.0), ("late", 72.0),
+            ("late", 300.0), ("first_tile", 300.0), ("two_late", 300.0)]
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("where,value", OUTLIERS, ids=[f"{w}-{int(v)}" for w, v in OUTLIERS])
 def test_score_outlier_reference(dtype, where, value):
     """A late key whose score exceeds the first tile's max: by a few units
-    (log2) the weights stay finite and no pass is repeated; past fp16's range
-    (value 80, and for some rows 72) the workgroup repeats the split, first
-    tracking every tile's max, then with the exact max as reference.  An
-    outlier in the first tile only raises the reference.  Every case matches
-    the oracle."""
+    (log2) the weights stay finite and nothing is rescaled; past fp16's range
+    (value 80, and for some rows 72), or past the bound on bf16 sums (300),
+    the wave raises its reference at that tile and rescales O and l.  An
+    outlier in the first tile only raises the first reference; two late
+    outliers in different tiles (the second larger) rescale twice.  Every
+    case matches the oracle."""
     import torch
     case = synth.make_case("outlier", 3000, 64, 8, 2, 128, 16, dtype, seed=21)
-    key = 2900 if where == "late" else 5
+    key = 5 if where == "first_tile" else 2900
     case = _plant_outlier(case, key, value)
+    if where == "two_late":
+        case = _plant_outlier(case, 1700, value * 0.5, shift_q=False)   # the first of the two, in an earlier tile
     print(f"case outlier {where} {dtype}: key {key} K[.,0]={value}, q[.,0]+=2", flush=True)
     d = _gpu.dev_case(case)
     ref = _gpu.oracle_out(case)
