@@ -45,6 +45,8 @@ Registry& registry() {
 // (no allocation; calls that need more than it holds are rejected).
 struct WsSource {
   bool fixed_array = false;
+  void* ws = nullptr;       // a buffer the caller holds (its capacity below), or null
+  int64_t ws_bytes = 0;
 };
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -75,10 +77,12 @@ struct Q8Scales {
   const void* v;
 };
 
+// kv16: k and v are contiguous fp16 (8-bit pages dequantized beforehand)
+// whatever dtype says about q and out.
 int run(const void* q, const void* k, const void* v, const int32_t* bt, bool paged,
         int64_t history, int32_t rows, int32_t hq, int32_t hkv, int32_t d, int32_t ps,
         int32_t n_splits, void* out, int32_t dtype, hipStream_t stream, const Q8Scales* q8 = nullptr,
-        const WsSource& wsrc = WsSource()) {
+        const WsSource& wsrc = WsSource(), bool kv16 = false) {
   Shape shape{history, rows, hq, hkv, d, ps, dtype};
   shape.q8 = q8 ? 1 : 0;
   int rc = check_shape(shape);
@@ -101,6 +105,7 @@ int run(const void* q, const void* k, const void* v, const int32_t* bt, bool pag
   if (plan.workspace_bytes > max_workspace_bytes()) return PPA_ERR_WORKSPACE;
 
   if (wsrc.fixed_array && plan.workspace_bytes > kStaticScratchBytes) return PPA_ERR_WORKSPACE;
+  if (wsrc.ws && plan.workspace_bytes > wsrc.ws_bytes) return PPA_ERR_WORKSPACE;
 
   if (paged && !wsrc.fixed_array && env_validate()) {
     rc = validate_block_table(bt, (history + rows + ps - 1) / ps, stream);
@@ -111,7 +116,9 @@ int run(const void* q, const void* k, const void* v, const int32_t* bt, bool pag
   void* ws = nullptr;
   Registry::Lease lease;
   if (plan.n_splits > 1) {
-    if (wsrc.fixed_array) {
+    if (wsrc.ws) {
+      ws = wsrc.ws;
+    } else if (wsrc.fixed_array) {
       rc = static_scratch(&ws);
       if (rc != PPA_OK) return rc;
     } else {
@@ -153,8 +160,9 @@ int run(const void* q, const void* k, const void* v, const int32_t* bt, bool pag
   a.v_scale = q8 ? static_cast<const uint16_t*>(q8->v) : nullptr;
   a.query_blocks = plan.m_tile / 128;
 
-  const hipError_t le = q8 ? launch_attention_q8(a, d, dtype, plan.grid, stream)
-                           : launch_attention(a, d, dtype, paged, plan.grid, stream);
+  const hipError_t le = q8     ? launch_attention_q8(a, d, dtype, plan.grid, stream)
+                       : kv16 ? launch_attention_kv16(a, d, dtype, plan.grid, stream)
+                              : launch_attention(a, d, dtype, paged, plan.grid, stream);
   if (le != hipSuccess) return PPA_ERR_HIP;
   if (plan.n_splits > 1) {
     MergeArgs m;
@@ -292,14 +300,95 @@ int run_varlen(const void* q, const void* k, const void* v, const int32_t* bt, i
   return PPA_OK;
 }
 
+// 8-bit pages read by several m tiles per KV head: dequantize the chunk's
+// context once into contiguous fp16 K/V (kv_dequant_q8_kernel) and run the
+// 16-bit kernels over it, instead of widening every tile in every workgroup
+// that reads it (about 30 VALU instructions per 16 values, serialized with a
+// wave's MFMAs).  The fp16 values are the ones the in-tile widening computes.
+// Returns PPA_OK, an error, or kNoDequant when the in-tile path should run
+// (one m tile per KV head: each tile is then widened once anyway; or a buffer
+// beyond the workspace cap).
+constexpr int kNoDequant = 1;
+constexpr int kDequantMinTiles = 4;   // m tiles per KV head over the whole chunk
+
+int run_q8_dequant(const void* q, const void* kq, const void* vq, const int32_t* bt, int64_t history,
+                   int32_t rows, int32_t piece_rows, int32_t hq, int32_t hkv, int32_t d, int32_t ps,
+                   int32_t n_splits, void* out, int32_t dtype, hipStream_t stream, const Q8Scales& q8) {
+  const int64_t qv = int64_t(rows) * (hq / hkv);
+  const int32_t mt = m_tile_for(d, false, qv);
+  if ((qv + mt - 1) / mt < kDequantMinTiles) return kNoDequant;
+  const int32_t p = (piece_rows <= 0 || piece_rows >= rows) ? rows : piece_rows;
+  // the pieces' split workspaces (16-bit plans), one after another on the stream
+  int64_t split_ws = 0;
+  for (int32_t r0 = 0; r0 < rows; r0 += p) {
+    const int32_t n = rows - r0 < p ? rows - r0 : p;
+    const Shape ps16{history + r0, n, hq, hkv, d, ps, dtype};
+    ppa_plan plan;
+    const int rc = make_plan(ps16, n_splits, max_workspace_bytes(), &plan);
+    if (rc != PPA_OK) return rc;
+    if (plan.workspace_bytes > split_ws) split_ws = plan.workspace_bytes;
+  }
+  const int64_t ctx = history + rows;
+  const int64_t tensor_bytes = (ctx * hkv * d * 2 + 255) / 256 * 256;
+  const int64_t total = 2 * tensor_bytes + split_ws;
+  if (total > max_workspace_bytes()) return kNoDequant;
+  if (!q || !kq || !vq || !out || !bt || !q8.k || !q8.v) return PPA_ERR_NULL_PTR;
+  const int64_t qbytes = int64_t(rows) * hq * d * 2;
+  const char* qc = static_cast<const char*>(q);
+  const char* oc = static_cast<const char*>(out);
+  if (oc < qc + qbytes && qc < oc + qbytes) return PPA_ERR_ALIAS;
+  if (env_validate()) {
+    const int rc = validate_block_table(bt, (ctx + ps - 1) / ps, stream);
+    if (rc != PPA_OK) return rc;
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PPA_ERR_HIP;
+  Registry::Lease lease;   // held until the last piece's kernels are enqueued
+  if (!registry().acquire({dev, stream}, total, &lease)) return PPA_ERR_WORKSPACE;
+  char* base = static_cast<char*>(lease.ptr());
+  DequantQ8Args da;
+  da.k_quant = static_cast<const int8_t*>(kq);
+  da.v_quant = static_cast<const int8_t*>(vq);
+  da.k_scale = static_cast<const uint16_t*>(q8.k);
+  da.v_scale = static_cast<const uint16_t*>(q8.v);
+  da.bt = bt;
+  da.k_out = reinterpret_cast<uint16_t*>(base);
+  da.v_out = reinterpret_cast<uint16_t*>(base + tensor_bytes);
+  da.ctx = int32_t(ctx);
+  da.n_kv_heads = hkv;
+  da.head_dim = d;
+  da.log2_ps = log2_exact(ps);
+  if (launch_kv_dequant_q8(da, stream) != hipSuccess) return PPA_ERR_HIP;
+  WsSource src;
+  src.ws = split_ws > 0 ? base + 2 * tensor_bytes : nullptr;
+  src.ws_bytes = split_ws;
+  const int64_t row_bytes = int64_t(hq) * d * 2;
+  for (int32_t r0 = 0; r0 < rows; r0 += p) {
+    const int32_t n = rows - r0 < p ? rows - r0 : p;
+    const int rc = run(static_cast<const char*>(q) + r0 * row_bytes, da.k_out, da.v_out, nullptr, false,
+                       history + r0, n, hq, hkv, d, ps, n_splits, static_cast<char*>(out) + r0 * row_bytes,
+                       dtype, stream, nullptr, src, true);
+    if (rc != PPA_OK) return rc;
+  }
+  return PPA_OK;
+}
+
 int run_pieces(const void* q, const void* k, const void* v, const int32_t* bt, bool paged,
                int64_t history, int32_t rows, int32_t piece_rows, int32_t hq, int32_t hkv,
                int32_t d, int32_t ps, int32_t n_splits, void* out, int32_t dtype,
                hipStream_t stream, const Q8Scales* q8 = nullptr, const WsSource& wsrc = WsSource()) {
   if (piece_rows < 0) return PPA_ERR_BAD_SHAPE;
   Shape shape{history, rows, hq, hkv, d, ps, dtype};
+  shape.q8 = q8 ? 1 : 0;
   int rc = check_shape(shape);
   if (rc != PPA_OK) return rc;
+  if (q8 && rows > 0 && ps >= 16 && n_splits >= 0 && !wsrc.fixed_array) {
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(q8->k) ||
+        !aligned16(q8->v))
+      return PPA_ERR_ALIGNMENT;
+    rc = run_q8_dequant(q, k, v, bt, history, rows, piece_rows, hq, hkv, d, ps, n_splits, out, dtype, stream, *q8);
+    if (rc != kNoDequant) return rc;
+  }
   if (piece_rows == 0 || piece_rows >= rows)
     return run(q, k, v, bt, paged, history, rows, hq, hkv, d, ps, n_splits, out, dtype, stream, q8, wsrc);
   const int64_t row_bytes = int64_t(hq) * d * 2;

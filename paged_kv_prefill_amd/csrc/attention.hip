@@ -151,6 +151,13 @@ hipError_t launch_attention_q8(const AttnArgs& a, int head_dim, int dtype, int g
   return launch_attention_q8_d64_d128(a, head_dim, dtype, grid, stream);
 }
 
+hipError_t launch_attention_kv16(const AttnArgs& a, int head_dim, int dtype, int grid, hipStream_t stream) {
+  // fp16 q: the ordinary fp16 kernel over contiguous K/V
+  if (dtype == 0) return launch_attention(a, head_dim, dtype, false, grid, stream);
+  if (head_dim == 256) return launch_attention_kv16_d256(a, grid, stream);
+  return launch_attention_kv16_d64_d128(a, head_dim, grid, stream);
+}
+
 hipError_t launch_merge(const MergeArgs& a, int head_dim, int dtype, int grid, int grid_y, hipStream_t stream) {
   return dtype == 1 ? launch_merge_d<BF16>(a, head_dim, grid, grid_y, stream)
                     : launch_merge_d<F16>(a, head_dim, grid, grid_y, stream);

@@ -11,4 +11,9 @@ hipError_t launch_attention_d256(const AttnArgs& a, int dtype, bool paged, int g
                     : launch_attn_p_large<256, F16>(a, paged, grid, stream);
 }
 
+// bf16 q and out over contiguous fp16 K/V (dequantized 8-bit pages)
+hipError_t launch_attention_kv16_d256(const AttnArgs& a, int grid, hipStream_t stream) {
+  return launch_attn_t<256, BF16, Addr::Contig, false, 1, true>(a, grid, stream);
+}
+
 }  // namespace ppa

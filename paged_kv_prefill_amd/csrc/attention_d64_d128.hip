@@ -16,4 +16,15 @@ hipError_t launch_attention_d64_d128(const AttnArgs& a, int head_dim, int dtype,
   }
 }
 
+// bf16 q and out over contiguous fp16 K/V (dequantized 8-bit pages), two
+// query blocks per wave
+hipError_t launch_attention_kv16_d64_d128(const AttnArgs& a, int head_dim, int grid, hipStream_t stream) {
+  if (a.query_blocks != 2) return launch_attention_kv16_d64_d128_qb1(a, head_dim, grid, stream);
+  switch (head_dim) {
+    case 64: return launch_attn_t<64, BF16, Addr::Contig, false, 2, true>(a, grid, stream);
+    case 128: return launch_attn_t<128, BF16, Addr::Contig, false, 2, true>(a, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace ppa

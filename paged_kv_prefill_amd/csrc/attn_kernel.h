@@ -247,11 +247,15 @@ constexpr float kSumLimit = 0x1p64f;
 // Q8: K and V pages hold 8-bit quants with an fp16 scale per 32 values along
 // d (see the q8 loader below); the tiles are widened to fp16 in LDS and the
 // MFMA, softmax and P arithmetic run in fp16 whatever the type of q and out.
-template <int D, class E, Addr AM, bool Q8 = false, int QB = 1>
+// KV16: K and V are fp16 (8-bit pages dequantized beforehand into a
+// contiguous buffer) while q and out have type E: the same fp16 arithmetic as
+// Q8, over 16-bit tiles.
+template <int D, class E, Addr AM, bool Q8 = false, int QB = 1, bool KV16 = false>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_partial_kernel(AttnArgs a) {
   static_assert(!Q8 || AM == Addr::Page16 || AM == Addr::PageBig, "8-bit pages need pages of 16 tokens or more");
+  static_assert(!KV16 || (!Q8 && AM == Addr::Contig), "fp16 K/V under another q type: contiguous buffers");
   using Gm = Geom<D>;
-  using M = std::conditional_t<Q8, F16, E>;   // element type of the MFMA operands
+  using M = std::conditional_t<Q8 || KV16, F16, E>;   // element type of the MFMA operands
   using vec8 = typename M::vec8;
   constexpr int EB = Q8 ? 1 : 2;              // bytes per K/V element in memory
   constexpr int MT = kWaves * 32 * QB;        // query vectors per workgroup
@@ -951,9 +955,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   }
 }
 
-template <int D, class E, Addr AM, bool Q8 = false, int QB = 1>
+template <int D, class E, Addr AM, bool Q8 = false, int QB = 1, bool KV16 = false>
 hipError_t launch_attn_t(const AttnArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_partial_kernel<D, E, AM, Q8, QB>), dim3(grid), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((attn_partial_kernel<D, E, AM, Q8, QB, KV16>), dim3(grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -90,6 +90,23 @@ struct AppendQ8Args {
   int32_t log2_ps;
 };
 
+// Dequantizing gather: tokens [0, ctx) of one sequence from 8-bit pages
+// (quants [pool][ps][Hkv][D], fp16 scales [pool][ps][Hkv][D / 32]) to
+// contiguous fp16 [ctx][Hkv][D], K and V.
+struct DequantQ8Args {
+  const int8_t* k_quant;
+  const int8_t* v_quant;
+  const uint16_t* k_scale;
+  const uint16_t* v_scale;
+  const int32_t* bt;
+  uint16_t* k_out;
+  uint16_t* v_out;
+  int32_t ctx;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t log2_ps;
+};
+
 // dtype: 0 = fp16, 1 = bf16.  Returns hipSuccess or the launch error.
 hipError_t launch_attention(const AttnArgs& a, int head_dim, int dtype, bool paged, int grid,
                             hipStream_t stream);
@@ -98,6 +115,10 @@ hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_kv_append_q8(const AppendQ8Args& a, int dtype, hipStream_t stream);
 // The attention kernel over 8-bit pages (page_size >= 16).
 hipError_t launch_attention_q8(const AttnArgs& a, int head_dim, int dtype, int grid, hipStream_t stream);
+// The attention kernel over contiguous fp16 K/V with q and out of type dtype
+// (dequantized 8-bit pages).
+hipError_t launch_attention_kv16(const AttnArgs& a, int head_dim, int dtype, int grid, hipStream_t stream);
+hipError_t launch_kv_dequant_q8(const DequantQ8Args& a, hipStream_t stream);
 
 // The per-head-dimension halves of launch_attention and launch_attention_q8
 // (separate translation units).
@@ -109,6 +130,9 @@ hipError_t launch_attention_d64_d128_qb1(const AttnArgs& a, int head_dim, int dt
                                          hipStream_t stream);
 hipError_t launch_attention_q8_d64_d128(const AttnArgs& a, int head_dim, int dtype, int grid, hipStream_t stream);
 hipError_t launch_attention_q8_d256(const AttnArgs& a, int dtype, int grid, hipStream_t stream);
+hipError_t launch_attention_kv16_d256(const AttnArgs& a, int grid, hipStream_t stream);
+hipError_t launch_attention_kv16_d64_d128(const AttnArgs& a, int head_dim, int grid, hipStream_t stream);
+hipError_t launch_attention_kv16_d64_d128_qb1(const AttnArgs& a, int head_dim, int grid, hipStream_t stream);
 
 // Size of the fixed scratch array (noalloc.hip), one per device.
 constexpr int64_t kStaticScratchBytes = int64_t(64) << 20;   // 64 MiB

@@ -94,7 +94,54 @@ __global__ __launch_bounds__(256) void kv_append_q8_kernel(AppendQ8Args a) {
   }
 }
 
+// Dequantizing gather of 8-bit pages into contiguous fp16 K and V: token j
+// of the sequence, KV head h, values 16 c .. 16 c + 15 come from slot j % ps
+// of pool page bt[j / ps]; each value is quant * scale of its 32-value block,
+// rounded once to fp16 (the product of a 7-bit integer and an fp16 scale is
+// exact in fp32), the same value the attention kernel's in-LDS widening
+// computes.  One thread per 16 values; consecutive threads take consecutive
+// 16-byte quant units of a token's rows, so reads and writes coalesce.
+__global__ __launch_bounds__(256) void kv_dequant_q8_kernel(DequantQ8Args a) {
+  const int upr = a.head_dim / 16;                                  // units per token-head row
+  const int64_t per_tensor = int64_t(a.ctx) * a.n_kv_heads * upr;
+  const int64_t ps_mask = (int64_t(1) << a.log2_ps) - 1;
+  for (int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x; t < 2 * per_tensor; t += int64_t(gridDim.x) * 256) {
+    const bool is_v = t >= per_tensor;
+    const int64_t u = is_v ? t - per_tensor : t;
+    const int c = int(u % upr);
+    const int64_t rh = u / upr;                       // token * Hkv + head
+    const int64_t j = rh / a.n_kv_heads;
+    const int head = int(rh % a.n_kv_heads);
+    const int64_t page = a.bt[j >> a.log2_ps];
+    const int64_t src_row = ((page << a.log2_ps) + (j & ps_mask)) * a.n_kv_heads + head;
+    const u32x4 qw = *reinterpret_cast<const u32x4*>((is_v ? a.v_quant : a.k_quant) + src_row * a.head_dim + 16 * c);
+    const uint16_t sb = (is_v ? a.v_scale : a.k_scale)[src_row * (a.head_dim / 32) + c / 2];
+    const float sf = (float)__builtin_bit_cast(_Float16, sb);
+    uint32_t ow[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t w = qw[k >> 1];
+      const int sh = 16 * (k & 1);
+      const float x0 = (float)(int8_t)((w >> sh) & 0xffu) * sf;
+      const float x1 = (float)(int8_t)((w >> (sh + 8)) & 0xffu) * sf;
+      ow[k] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x0) |
+              ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x1) << 16);
+    }
+    u32x4* dst = reinterpret_cast<u32x4*>((is_v ? a.v_out : a.k_out) + rh * a.head_dim + 16 * c);
+    dst[0] = u32x4{ow[0], ow[1], ow[2], ow[3]};
+    dst[1] = u32x4{ow[4], ow[5], ow[6], ow[7]};
+  }
+}
+
 }  // namespace
+
+hipError_t launch_kv_dequant_q8(const DequantQ8Args& a, hipStream_t stream) {
+  const int64_t units = 2 * int64_t(a.ctx) * a.n_kv_heads * (a.head_dim / 16);
+  int64_t grid = (units + 255) / 256;
+  if (grid > 8192) grid = 8192;
+  hipLaunchKernelGGL(kv_dequant_q8_kernel, dim3(uint32_t(grid)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_kv_append_q8(const AppendQ8Args& a, int dtype, hipStream_t stream) {
   const int64_t blocks = 2 * int64_t(a.rows) * a.n_kv_heads * (a.head_dim / 32);

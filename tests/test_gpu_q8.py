@@ -64,6 +64,11 @@ SHAPES = [
     ("ps256_d64", 2100, 40, 12, 4, 64, 256, 2),
     ("one_row_long_d256", 4000, 1, 16, 2, 256, 16, 0),
     ("tail_d128", 2047, 129, 4, 2, 128, 16, 5),
+    # four m tiles per KV head or more: the context is dequantized once into
+    # fp16 and the 16-bit kernels run over it (the others widen in the tile loop)
+    ("many_rows_d128", 500, 300, 8, 2, 128, 16, 0),
+    ("many_rows_d64_S3", 200, 160, 16, 2, 64, 32, 3),
+    ("many_rows_d256_ps64", 900, 70, 16, 2, 256, 64, 0),
 ]
 CASES = [s[:7] + (dt,) + s[7:] for s in SHAPES for dt in ("f16", "bf16")]
 
@@ -131,11 +136,25 @@ def test_append_q8_matches_oracle_bit_for_bit(history, rows, hkv, dim, ps, dtype
         assert np.array_equal(g, w), what
 
 
-@pytest.mark.parametrize("name", ["sweep_32768", "long_128k"])
+def test_q8_pieces_dequantized_once():
+    """A bf16 chunk in 128-row pieces over 8-bit pages with 32/4 heads, d 128:
+    the context is dequantized once for all pieces and every piece runs the
+    two-block 16-bit kernel over it; all rows against the oracle."""
+    import torch
+    case = synth.make_q8_case("q8_pieces", 1000, 512, 32, 4, 128, 16, "bf16", seed=88, piece_rows=128)
+    print("case q8 pieces: H=1000 R=512 in 128-row pieces, 32/4 heads, d 128, bf16", flush=True)
+    d = _dev_q8(case)
+    out = _run(d, case, piece_rows=128)
+    torch.cuda.synchronize()
+    _gpu.assert_close_bf16_bound(_gpu.host_out(out), _oracle(case), _oracle_absw(case), "q8 pieces")
+
+
+@pytest.mark.parametrize("name", ["sweep_32768", "piece_64k", "long_128k"])
 def test_q8_full_size_sampled(name):
-    """The 32K chunk (fp16, one call) and the 128K chunk (bf16, 16 pieces of
-    128 rows, pages scattered over a 65,536-page pool) over 8-bit pages of the
-    same shapes; sampled rows against the oracle."""
+    """The 32K chunk (fp16, one call), the 64K chunk (bf16, 8 pieces of 256
+    rows, d 128) and the 128K chunk (bf16, 16 pieces of 128 rows, pages
+    scattered over a 65,536-page pool) over 8-bit pages of the same shapes;
+    sampled rows against the oracle."""
     import torch
     base = synth.config_case(name)
     case = synth.make_q8_case(name, base.history, base.rows, base.n_q_heads, base.n_kv_heads, base.head_dim,
