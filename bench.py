@@ -193,16 +193,20 @@ def timed_pair(fa, fb, reps, stream):
             float(np.median([e[2].elapsed_time(e[3]) for e in evs])))
 
 
-def timed_round_robin(fns, reps, stream):
+def timed_round_robin(fns, reps, stream, seed=5):
     """Median ms of each of several calls, timed in rounds (every call once
-    per round, in turn) so that clock drift over the run hits all alike."""
+    per round, in a shuffled order) so that clock drift over the run, and the
+    state a longer or shorter call leaves behind, hit all alike."""
     import numpy as np
     import torch
     for f in fns.values():
         f()
     evs = {k: [] for k in fns}
+    rng = np.random.default_rng(seed)
+    keys = list(fns)
     for _ in range(reps):
-        for k, f in fns.items():
+        for idx in rng.permutation(len(keys)):
+            k, f = keys[idx], fns[keys[idx]]
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             f()
@@ -335,10 +339,13 @@ def extra_measurements(chunks, paged, contig, pkg, synth, to_dev, stream, reps=1
                                                             stream=stream))
              for sreq in counts + (0,)}, reps, stream)
         best = min(v for k, v in res.items() if k != "planner")
+        planned = pkg.paged_prefill_plan(cs.history, cs.piece_rows, cs.n_q_heads, cs.n_kv_heads,
+                                         cs.head_dim)["n_splits"]
         out[f"split_sweep_{name}_ms_median"] = res
-        out[f"split_sweep_{name}_planner_splits"] = pkg.paged_prefill_plan(
-            cs.history, cs.piece_rows, cs.n_q_heads, cs.n_kv_heads, cs.head_dim)["n_splits"]
-        out[f"split_sweep_{name}_planner_over_best"] = round(res["planner"] / best, 4)
+        out[f"split_sweep_{name}_planner_splits"] = planned
+        # the planner's own count where the sweep has it (the same plan, timed in the same rounds)
+        mine = res.get(str(planned), res["planner"])
+        out[f"split_sweep_{name}_planner_over_best"] = round(mine / best, 4)
     # Short appends and decode steps: the first R rows of each chunk as one
     # call on the same history (planner splits).  KV-bound at small R, so
     # reported as K/V bytes per second against HBM peak, with the paged /
