@@ -19,7 +19,11 @@ planner, the KV append of each chunk (GB/s against HBM peak), short appends
 in one launch against one call per sequence, and each chunk over 8-bit K/V
 pages.  Prints one JSON line.
 
+With --power SECONDS it also runs each chunk, and an 8192^3 fp16 matmul, back
+to back for SECONDS while sampling board power and engine clocks.
+
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-ab] [--no-extra] [--copy-calibration]
+                  [--power SECONDS]
 """
 
 import argparse
@@ -50,6 +54,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (known bytes) for counter scaling")
     ap.add_argument("--chunks", default=",".join(CHUNKS))
+    ap.add_argument("--power", type=float, default=0.0, metavar="SECONDS",
+                    help="also run each chunk (and an fp16 matmul) back to back for SECONDS each while "
+                         "sampling board power and engine clocks with amd-smi")
     return ap.parse_args()
 
 
@@ -82,6 +89,20 @@ def load_clock(kernel_hash):
     if rec.get("kernel_source_hash") != kernel_hash:
         return None
     return rec.get("clock_ghz_upper_bound")
+
+
+def load_power(kernel_hash):
+    """Sustained board power, engine clock and rate of the roofline chunk and of
+    an fp16 matmul under the same power limit, from the committed summary of a
+    `--power` run, or None if the kernels changed since."""
+    path = os.path.join(ROOT, "profiles", "power_clock_sustained_chunks_and_f16_matmul.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_hash:
+        return None
+    return rec.get("phases")
 
 
 def cpu_baseline(cases, budget_s=15.0):
@@ -135,6 +156,76 @@ def cpu_baseline(cases, budget_s=15.0):
             "sample": ", ".join(parts) + f" (rows evenly spaced), {total_s:.1f} s, numpy float64 with BLAS on "
                       f"{threads} threads",
             "seconds": total_s, "cpu_model": cpu_model, "blas": blas}
+
+
+def power_measurements(chunks, paged, stream, seconds):
+    """Board power and engine clock under sustained load: each chunk called back
+    to back for `seconds`, and an 8192^3 fp16 matmul (torch, i.e. the vendor
+    GEMM library) as the reference of what dense MFMA work reaches under the
+    same board power limit.  A thread samples `amd-smi metric -p -c` (socket
+    power, the eight XCDs' GFX clocks) every ~0.2 s; a phase reports the median
+    power and the mean clock of the samples taken from 1 s after its start to
+    its end, and its own rate."""
+    import re
+    import subprocess
+    import threading
+    import numpy as np
+    import torch
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            t = time.time()
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-g", "0", "-p", "-c"], capture_output=True, text=True,
+                                   timeout=10)
+                pw = re.search(r"SOCKET_POWER: (\d+) W", r.stdout)
+                clk = [int(x) for x in re.findall(r"GFX_\d+:\s+CLK: (\d+) MHz", r.stdout)]
+                if pw and clk:
+                    samples.append((t, int(pw.group(1)), float(np.mean(clk))))
+            except (OSError, subprocess.SubprocessError):
+                return
+            stop.wait(0.2)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    phases = {}
+
+    def phase(name, fn, flops):
+        fn()
+        torch.cuda.synchronize()
+        t0, n = time.time(), 0
+        while time.time() - t0 < seconds:
+            for _ in range(5):
+                fn()
+            torch.cuda.synchronize()
+            n += 5
+        t1 = time.time()
+        phases[name] = (t0, t1, (t1 - t0) / n * 1e3, flops)
+        print(f"# power phase {name}: {n} calls", file=sys.stderr, flush=True)
+
+    time.sleep(2.0)
+    phases["idle"] = (time.time() - 2.0, time.time(), None, None)
+    n_g = 8192
+    a = torch.randn(n_g, n_g, device=stream.device, dtype=torch.float16)
+    b = torch.randn(n_g, n_g, device=stream.device, dtype=torch.float16)
+    cg = torch.empty_like(a)
+    phase("matmul_f16_8192", lambda: torch.matmul(a, b, out=cg), 2.0 * n_g ** 3)
+    del a, b, cg
+    for c in chunks:
+        phase(c["name"], lambda: paged(c), c["flops"])
+    stop.set()
+    th.join(timeout=15)
+    res = {"samples": len(samples)}
+    for name, (t0, t1, ms, flops) in phases.items():
+        sel = [x for x in samples if t0 + (0.0 if name == "idle" else 1.0) <= x[0] <= t1]
+        rec = {"power_w_median": float(np.median([x[1] for x in sel])) if sel else None,
+               "gfx_clock_mhz_mean": round(float(np.mean([x[2] for x in sel])), 1) if sel else None,
+               "n_samples": len(sel)}
+        if ms is not None:
+            rec.update({"ms_per_call": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1)})
+        res[name] = rec
+    return res
 
 
 def stated_flops(case):
@@ -662,6 +753,16 @@ def main():
             peak_clk = PEAK_TFLOPS["f16"] * clock / NOMINAL_CLOCK_GHZ
             roofline.update({"clock_ghz_counters": round(clock, 3), "peak_at_that_clock": round(peak_clk, 1),
                              "frac_at_that_clock": round(achieved / peak_clk, 4)})
+        pw = load_power(khash)
+        if pw and ROOFLINE_CHUNK in pw and "matmul_f16_8192" in pw:
+            # under sustained load the board power limit sets the clock: the
+            # same chip's fp16 matmul rate is the practical ceiling
+            mm, rcp = pw["matmul_f16_8192"], pw[ROOFLINE_CHUNK]
+            roofline.update({"sustained_power_w": rcp["power_w_median"],
+                             "sustained_clock_mhz": rcp["gfx_clock_mhz_mean"],
+                             "matmul_f16_8192_tflops": mm["tflops"], "matmul_power_w": mm["power_w_median"],
+                             "matmul_clock_mhz": mm["gfx_clock_mhz_mean"],
+                             "frac_of_matmul": round(achieved / mm["tflops"], 4)})
 
     line = {
         "metric": "paged prefill-attn TFLOP/s + ms per 2048-row chunk at 32K-128K history",
@@ -681,6 +782,9 @@ def main():
                                       "tflops_4_rows_ctx_convention uses 4 R (H + R) d Hq per call"},
         "roofline": roofline,
     }
+
+    if args.power > 0:
+        line["config"]["power"] = power_measurements(chunks, paged, stream, args.power)
 
     if not args.no_extra:
         print("# extra measurements", file=sys.stderr, flush=True)

@@ -7,6 +7,7 @@ counter passes scaled by a copy of known size).
       <copy bytes> "<fetch command>" "<write command>"
   python -m paged_kv_prefill_amd.profsum counters <counters.csv> <out.txt> <kernel substring> \
       <exact flops per launch> <wave-tiles per launch> <launch us from the kernel trace> "<command>"
+  python -m paged_kv_prefill_amd.profsum power <bench output with --power> <out.txt> "<command>"
 """
 
 import csv
@@ -168,6 +169,39 @@ def counters(csv_path, out_path, kernel_sub, exact_flops, tiles, launch_us, comm
         fh.write("\n")
 
 
+def power(bench_out, out_path, command):
+    """Board power and engine clock under sustained load, from the JSON line of
+    `bench.py --power SECONDS`: per phase (idle, the fp16 matmul reference, each
+    chunk) the median socket power, the mean GFX clock, the rate, and the rate
+    as a fraction of the nominal peak and of the matmul's."""
+    line = None
+    with open(bench_out) as f:
+        for l in f:
+            if l.startswith("{"):
+                line = json.loads(l)
+    pw = line["config"]["power"]
+    ref = pw.get("matmul_f16_8192", {}).get("tflops")
+    lines = ["# board power and engine clock under sustained load (amd-smi metric -p -c, ~0.2 s samples)",
+             f"# command: {command}", f"# kernel source hash: {kernel_source_hash()}",
+             f"# samples: {pw['samples']}", "",
+             f"{'phase':18s} {'power W':>8s} {'GFX MHz':>8s} {'ms/call':>9s} {'TFLOP/s':>8s} "
+             f"{'of 2.5 PF':>9s} {'of matmul':>9s}"]
+    for name, r in pw.items():
+        if not isinstance(r, dict):
+            continue
+        tf = r.get("tflops")
+        lines.append(f"{name:18s} {r['power_w_median'] or 0:8.0f} {r['gfx_clock_mhz_mean'] or 0:8.0f} "
+                     f"{r.get('ms_per_call') or 0:9.4f} {tf or 0:8.1f} "
+                     f"{(tf or 0) / 2500.0:9.3f} {(tf or 0) / ref if ref else 0:9.3f}")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    rec = {"kernel_source_hash": kernel_source_hash(), "command": command, "phases": pw}
+    with open(os.path.splitext(out_path)[0] + ".json", "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         stats(sys.argv[2], sys.argv[3], sys.argv[4])
@@ -176,5 +210,7 @@ if __name__ == "__main__":
     elif sys.argv[1] == "counters":
         counters(sys.argv[2], sys.argv[3], sys.argv[4], float(sys.argv[5]), float(sys.argv[6]), float(sys.argv[7]),
                  sys.argv[8])
+    elif sys.argv[1] == "power":
+        power(sys.argv[2], sys.argv[3], sys.argv[4])
     else:
         raise SystemExit(__doc__)

@@ -97,3 +97,28 @@ def test_counter_summary_figures(tmp_path):
     assert "50.0 %" in text
     # against the launch at 2.4 GHz: 800,000 / 2,400,000
     assert "33.3 %" in text
+
+
+def test_power_summary_and_its_hash(tmp_path, monkeypatch):
+    import bench
+    from paged_kv_prefill_amd import profsum
+    phases = {"samples": 40,
+              "idle": {"power_w_median": 300.0, "gfx_clock_mhz_mean": 2400.0, "n_samples": 8},
+              "matmul_f16_8192": {"power_w_median": 1400.0, "gfx_clock_mhz_mean": 1700.0, "n_samples": 10,
+                                  "ms_per_call": 0.88, "tflops": 1250.0},
+              "sweep_32768": {"power_w_median": 1350.0, "gfx_clock_mhz_mean": 1690.0, "n_samples": 10,
+                              "ms_per_call": 1.07, "tflops": 1000.0}}
+    out = tmp_path / "bench.json"
+    out.write_text("# log line\n" + json.dumps({"config": {"power": phases}}) + "\n")
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    txt = prof / "power_clock_sustained_chunks_and_f16_matmul.txt"
+    profsum.power(str(out), str(txt), "python3 bench.py --power 10")
+    body = txt.read_text()
+    assert "python3 bench.py --power 10" in body
+    row = next(l for l in body.splitlines() if l.startswith("sweep_32768"))
+    assert row.split()[-2:] == ["0.400", "0.800"]   # of 2.5 PF, of the matmul
+    rec = json.loads((prof / "power_clock_sustained_chunks_and_f16_matmul.json").read_text())
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.load_power(rec["kernel_source_hash"])["matmul_f16_8192"]["tflops"] == 1250.0
+    assert bench.load_power("0" * 16) is None
