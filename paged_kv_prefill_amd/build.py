@@ -41,6 +41,8 @@ KERNEL_SOURCES = (
     # leave at head dimension 256 (it spills there); the AGPR form does not spill
     ("attention_q8_d64_d128.hip", os.environ.get("PPA_MFMA_VGPR_FORM_Q8", "0")),
     ("attention_q8_d256.hip", os.environ.get("PPA_MFMA_VGPR_FORM_Q8", "0")),
+    # the narrow (decode) kernel
+    ("decode.hip", os.environ.get("PPA_MFMA_VGPR_FORM_DEC", "1")),
     ("kv_append.hip", "0"),
     ("noalloc.hip", "0"),
 )

@@ -85,6 +85,7 @@ int run(const void* q, const void* k, const void* v, const int32_t* bt, bool pag
         const WsSource& wsrc = WsSource(), bool kv16 = false) {
   Shape shape{history, rows, hq, hkv, d, ps, dtype};
   shape.q8 = q8 ? 1 : 0;
+  shape.allow_narrow = kv16 ? 0 : 1;   // the narrow kernel reads 16-bit K/V of q's type or 8-bit pages
   int rc = check_shape(shape);
   if (rc != PPA_OK) return rc;
   if (n_splits < 0) return PPA_ERR_BAD_SHAPE;
@@ -160,9 +161,11 @@ int run(const void* q, const void* k, const void* v, const int32_t* bt, bool pag
   a.v_scale = q8 ? static_cast<const uint16_t*>(q8->v) : nullptr;
   a.query_blocks = plan.m_tile / 128;
 
-  const hipError_t le = q8     ? launch_attention_q8(a, d, dtype, plan.grid, stream)
-                       : kv16 ? launch_attention_kv16(a, d, dtype, plan.grid, stream)
-                              : launch_attention(a, d, dtype, paged, plan.grid, stream);
+  const bool narrow = plan.m_tile == kNarrowVectors;
+  const hipError_t le = narrow ? launch_attention_decode(a, d, dtype, paged, q8 != nullptr, plan.grid, stream)
+                        : q8   ? launch_attention_q8(a, d, dtype, plan.grid, stream)
+                        : kv16 ? launch_attention_kv16(a, d, dtype, plan.grid, stream)
+                               : launch_attention(a, d, dtype, paged, plan.grid, stream);
   if (le != hipSuccess) return PPA_ERR_HIP;
   if (plan.n_splits > 1) {
     MergeArgs m;

@@ -8,10 +8,11 @@ namespace {
 
 // Log-sum-exp merge of split partials.  A (row, head) pair is served by GR
 // groups of D/4 threads, 4 output elements per thread; group g sums its own
-// contiguous share of the pair's splits.  GR = 4 for 16 splits or more (a
-// decode step or a short append on a long history: four times the loads in
-// flight per pair instead of one thread walking every split), GR = 1 below
-// (many pairs, few splits: no cross-group exchange).
+// contiguous share of the pair's splits.  GR = 16 for 64 splits or more (a
+// decode step: a few pairs, up to thousands of splits; one 8-split batch per
+// group for up to 128 splits), 4 for 16 or more (a short append on a long
+// history), GR = 1 below (many pairs, few splits: no cross-group exchange).
+// A block has max(256, GR D / 4) threads.
 // One pass: each thread keeps 8 splits' loads in flight and a running
 // reference M (the largest lse it has read); a batch's weights are
 // exp2(lse_s - M) after the sums so far are scaled to the batch's M.  Groups
@@ -20,10 +21,11 @@ namespace {
 // so results are reproducible.  Splits that start past the row's last key
 // hold nothing for it and are not read.
 template <int D, class E, int GR>
-__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+__global__ __launch_bounds__(D / 4 * GR > 256 ? D / 4 * GR : 256) void merge_kernel(MergeArgs a) {
   constexpr int TPP = D / 4;                      // threads per (pair, group)
   constexpr int TPAIR = TPP * GR;                 // threads per pair
-  constexpr int PPB = 256 / TPAIR;                // pairs per block
+  constexpr int BLOCK = TPAIR > 256 ? TPAIR : 256;
+  constexpr int PPB = BLOCK / TPAIR;              // pairs per block
   __shared__ f32x4 acc_part[GR > 1 ? PPB : 1][GR][TPP];
   __shared__ float w_part[GR > 1 ? PPB : 1][GR], m_part[GR > 1 ? PPB : 1][GR];
 
@@ -116,23 +118,22 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   *(u32x2*)(a.out + pair * D + 4 * t) = u32x2{lo, hi};
 }
 
+template <int D, class E>
+void launch_merge_gr(const MergeArgs& a, dim3 g, hipStream_t stream) {
+  switch (merge_groups_for(a.n_splits)) {
+    case 16: hipLaunchKernelGGL((merge_kernel<D, E, 16>), g, dim3(merge_block_threads(D, a.n_splits)), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((merge_kernel<D, E, 4>), g, dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL((merge_kernel<D, E, 1>), g, dim3(256), 0, stream, a); break;
+  }
+}
+
 template <class E>
 hipError_t launch_merge_d(const MergeArgs& a, int head_dim, int grid, int grid_y, hipStream_t stream) {
   const dim3 g(grid, grid_y);
-  const bool four = merge_groups_for(a.n_splits) == 4;
   switch (head_dim) {
-    case 64:
-      if (four) hipLaunchKernelGGL((merge_kernel<64, E, 4>), g, dim3(256), 0, stream, a);
-      else hipLaunchKernelGGL((merge_kernel<64, E, 1>), g, dim3(256), 0, stream, a);
-      break;
-    case 128:
-      if (four) hipLaunchKernelGGL((merge_kernel<128, E, 4>), g, dim3(256), 0, stream, a);
-      else hipLaunchKernelGGL((merge_kernel<128, E, 1>), g, dim3(256), 0, stream, a);
-      break;
-    case 256:
-      if (four) hipLaunchKernelGGL((merge_kernel<256, E, 4>), g, dim3(256), 0, stream, a);
-      else hipLaunchKernelGGL((merge_kernel<256, E, 1>), g, dim3(256), 0, stream, a);
-      break;
+    case 64: launch_merge_gr<64, E>(a, g, stream); break;
+    case 128: launch_merge_gr<128, E>(a, g, stream); break;
+    case 256: launch_merge_gr<256, E>(a, g, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -1,0 +1,713 @@
+// Device code of the narrow attention kernel: calls with at most 32 query
+// vectors per KV head (decode steps, appends of a few rows), where the work
+// is streaming K/V from memory and the prefill kernel's 128-vector m tile
+// would leave most of its MFMA rows empty and its workgroup with one tile in
+// flight.  Included by decode.hip; shares the element types and small helpers
+// of attn_kernel.h.
+//
+// What is computed is the same as there (issue "Metal: paged-KV prefill is
+// 4.43x slower than contiguous KV at 32K"; PR "perf: scale prefill attention
+// splits with GPU cores on Apple7/8"): causal attention of the call's rows
+// over the history and themselves, GQA head h reading KV head h / G, the key
+// axis cut into splits whose partials (output normalised by its own softmax
+// sum, plus its log-sum-exp) are merged by the merge kernel.
+//
+// Workgroup = one (split, KV head), 4 waves.  Each wave owns every fourth
+// 32-key tile of the split and streams it on its own: K and V tiles land in
+// the wave's part of NS LDS slots by direct-to-LDS loads, NS tiles ahead of
+// the tile being computed (the loads of tile t + NS are issued as soon as
+// tile t has been read), so a CU keeps up to 4 NS tiles in flight with no
+// barrier in the loop.  All 32 query vectors of the KV head (one per lane
+// and lane + 32) stay in registers as the MFMA B operand; each wave keeps its
+// own softmax reference, sum and output accumulators, and at the end the four
+// waves' results are combined in LDS (references are integers, so the
+// combination scales by exact powers of two) into one partial per workgroup.
+//
+// 8-bit pages (Q8) are widened in registers at operand read time: a K read
+// of 16 quants becomes the A operands of two MFMA steps (quant x scale,
+// rounded once to fp16), and V^T comes from ds_read_b64_tr_b8, which hands
+// each lane one column of 8 rows (8 keys) of bytes, scaled per key.
+#pragma once
+
+#include "attn_kernel.h"
+
+namespace ppa {
+namespace {
+
+constexpr int kDecWaves = 4;
+constexpr int kDecPages = 128;   // block-table entries per split held in registers (two per lane)
+
+// Exchange bits 2 and 3 (8-bit K tiles store key swap23(m) in row m; see below).
+__device__ __forceinline__ constexpr int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+template <int D, bool Q8>
+struct DecGeom {
+  static constexpr int TK = 32;                          // keys per tile
+  static constexpr int KT = Q8 ? TK * D : TK * D * 2;    // bytes of one K (or V) tile
+  static constexpr int NS_FIT = (32 * 1024) / (2 * KT);  // slots in 32 KB per wave
+  static constexpr int NS = NS_FIT < 1 ? 1 : NS_FIT > 4 ? 4 : NS_FIT;
+  static constexpr int SCB = Q8 ? 512 : 0;              // Q8: scale rows of one K (or V) tile, 2 x 256 B
+  static constexpr int WS = KT + SCB;                    // one wave's part of a slot array
+  static constexpr int LKQ = KT / 1024;                  // 1 KB direct-to-LDS loads per K (or V) tile
+  static constexpr int LK = LKQ + (Q8 ? 2 : 0);          // loads of a K (or V) group (Q8: + two of scales)
+  static constexpr int LV = LK;
+  static constexpr int U = D / 16;                       // 16-byte units per 8-bit row
+  static constexpr int RPL = 64 / U;                     // 8-bit rows per 1 KB load
+};
+
+// s_waitcnt vmcnt(N), other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void dec_wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+template <int I, int N, class F>
+__device__ __forceinline__ void dec_static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    dec_static_for<I + 1, N>(f);
+  }
+}
+
+// 16-byte direct-to-LDS load (as load_lds16) that reads nothing when `valid`
+// is false: the buffer then has no records, so every lane is out of range and
+// the hardware skips the memory access.  The tile loop issues the loads of
+// tiles past a wave's last one this way, so every iteration issues the same
+// loads and the load counter waits below are constants.
+__device__ __forceinline__ void dec_load_lds16(const char* base, uint32_t voff, bool valid, void* lds) {
+  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)scalar_ptr(base), (short)0,
+                                                               valid ? 0x7fffffff : 0, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(void, lds), 16, (int)voff, 0, 0, 0);
+}
+
+// The same with 4 bytes per lane (lane L writes lds + 4 L).
+__device__ __forceinline__ void dec_load_lds4(const char* base, uint32_t voff, bool valid, void* lds) {
+  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)scalar_ptr(base), (short)0,
+                                                               valid ? 0x7fffffff : 0, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(void, lds), 4, (int)voff, 0, 0, 0);
+}
+
+// LDS layouts of one wave's tiles (bank-conflict-free for the reads below):
+//  * 16-bit K and V: 32 rows in 1 KB blocks of 8 rows x 8 16-byte chunks,
+//    block (row / 8, chunk / 8) at (chunk / 8) 4 KB + (row / 8) 1 KB, the
+//    chunk swizzled by lds_g(row) as in the prefill kernel.
+//  * 8-bit K: row m (D bytes) holds key swap23(m); its 16-byte unit c sits at
+//    unit c ^ sK(m).  With the swap a lane's softmax weights for one PV step
+//    are 8 consecutive keys (below), so the V reads and V scales are too.
+//  * 8-bit V: row = key; its 32-byte unit u sits at unit u ^ fV(key).  It is
+//    read with ds_read_b64_tr_b16 taking byte pairs as 16-bit elements (see
+//    the PV step).
+template <int D>
+__device__ __forceinline__ constexpr int dec_sk(int m) {
+  constexpr int U = D / 16;
+  constexpr int SH = U == 16 ? 0 : U == 8 ? 1 : 2;
+  return (m >> SH) & (U - 1);
+}
+template <int D>
+__device__ __forceinline__ constexpr int dec_fv(int key) {
+  return D == 256 ? 2 * (key & 3) : D == 128 ? 2 * ((key >> 1) & 1) : 0;
+}
+
+template <int D, class E, bool PAGED, bool Q8>
+__global__ __launch_bounds__(256, 1) void attn_decode_kernel(AttnArgs a) {
+  using Gm = DecGeom<D, Q8>;
+  using M = std::conditional_t<Q8, F16, E>;   // MFMA operand type
+  using vec8 = typename M::vec8;
+  constexpr int TK = Gm::TK, KT = Gm::KT, WS = Gm::WS, NS = Gm::NS, LK = Gm::LK, LV = Gm::LV, LKQ = Gm::LKQ;
+  constexpr int KS = D / 16, DB = D / 32;
+  constexpr int EB = Q8 ? 1 : 2;
+  static_assert(2 * NS * KT >= 128 * D, "the output staging fits the wave's slots");
+  constexpr int SROW = D / 16;   // Q8: bytes of one key's scale row
+  static_assert(LV + (NS - 1) * (LK + LV) < 64 && (NS - 1) * (LK + LV) + LK < 64, "vmcnt range");
+  // One array per slot and K/V, so the compiler can tell a read of one slot
+  // from a direct-to-LDS load into another (it waits for a load only before
+  // reads of the same array).  Unused slots are 16 bytes.
+  __shared__ __attribute__((aligned(1024))) uint8_t ks0[kDecWaves * WS];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs0[kDecWaves * WS];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks1[NS > 1 ? kDecWaves * WS : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs1[NS > 1 ? kDecWaves * WS : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks2[NS > 2 ? kDecWaves * WS : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs2[NS > 2 ? kDecWaves * WS : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks3[NS > 3 ? kDecWaves * WS : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs3[NS > 3 ? kDecWaves * WS : 16];
+  __shared__ float ml_m[kDecWaves][32], ml_l[kDecWaves][32];
+  // Q8: V scales of the wave's current tile, [block][key]
+  __shared__ __attribute__((aligned(16))) uint16_t vst[Q8 ? kDecWaves * DB * 32 : 8];
+
+  auto kslot = [&](auto s) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int S = decltype(s)::value;
+    if constexpr (S == 0) return ks0;
+    else if constexpr (S == 1) return ks1;
+    else if constexpr (S == 2) return ks2;
+    else return ks3;
+  };
+  auto vslot = [&](auto s) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int S = decltype(s)::value;
+    if constexpr (S == 0) return vs0;
+    else if constexpr (S == 1) return vs1;
+    else if constexpr (S == 2) return vs2;
+    else return vs3;
+  };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;
+  const int g = blockIdx.x % a.n_kv_heads;
+  const int s = blockIdx.x / a.n_kv_heads;
+
+  // Query vector f = lane % 32 = (row, head) pair of the head group, row-major.
+  const int G = a.group;
+  const int nqv = a.rows * G;
+  const int qv = lane & 31;
+  const bool qv_valid = qv < nqv;
+  const int row = qv_valid ? qv / G : a.rows - 1;
+  const int head = g * G + (qv_valid ? qv % G : 0);
+  const int lim = (int)a.history + row;   // last key the query vector sees
+
+  const int k0 = s * a.split_tokens;
+  const int kend = min(k0 + a.split_tokens, a.ctx);
+  const int n_tiles = kend > k0 ? (kend - k0 + TK - 1) / TK : 0;
+  const int nt = n_tiles > wave ? (n_tiles - wave + kDecWaves - 1) / kDecWaves : 0;  // tiles wave + 4 t
+  // Tiles whose keys all lie at or below the first row's last key need no mask.
+  const int mask_from = (int)a.history - k0;   // tile-relative first key past row 0's limit, at tile j: - 32 j
+
+  // Q fragments (B operand of QK).  16-bit: step ks holds d = 16 ks + 8 h + 0..7.
+  // Q8: steps 2j and 2j + 1 hold d = 32 j + 16 h + 0..7 and + 8..15 (the d
+  // order of one 16-quant K read).
+  vec8 qf[KS];
+  {
+    const uint16_t* qp = a.q + ((int64_t)row * a.n_q_heads + head) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int d0 = Q8 ? 32 * (ks >> 1) + 16 * h + 8 * (ks & 1) : 16 * ks + 8 * h;
+      const u32x4 raw = qv_valid ? *(const u32x4*)(qp + d0) : u32x4{0u, 0u, 0u, 0u};
+      if constexpr (std::is_same_v<M, E>) {
+        qf[ks] = __builtin_bit_cast(vec8, raw);
+      } else {
+        // bf16 q for the fp16 MFMA: exact for |q| in fp16's normal range
+        const bf16x8 qb = __builtin_bit_cast(bf16x8, raw);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[ks][e] = (_Float16)(float)qb[e];
+      }
+    }
+  }
+
+  // Pool pages of the split: page p0 + l in lane l of pr0, p0 + 64 + l in pr1
+  // (two plain registers: an indexed array would be moved to LDS).
+  const int ps_mask = (1 << a.log2_ps) - 1;
+  const int p0 = PAGED ? (k0 >> a.log2_ps) : 0;
+  int pr0 = 0, pr1 = 0;
+  if constexpr (PAGED) {
+    const int plast = kend > k0 ? ((kend - 1) >> a.log2_ps) : p0;
+    pr0 = a.bt[min(p0 + lane, plast)];
+    pr1 = a.bt[min(p0 + 64 + lane, plast)];
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // Q and pages: nothing else is in flight in the tile loop
+
+  const int hkvd = a.n_kv_heads * D * EB;   // bytes per token (all KV heads)
+  const uint32_t page_bytes = (uint32_t)hkvd << a.log2_ps;
+  const char* kg = (const char*)a.k + g * D * EB;
+  const char* vg = (const char*)a.v + g * D * EB;
+  // Pool token (page ps + place in the page; contiguous: the key) of key
+  // `key` (wave-uniform); K/V bytes are at token hkvd, scales at token srow.
+  auto key_tok = [&](int key) __attribute__((always_inline)) -> int64_t {
+    if constexpr (!PAGED) {
+      return key;
+    } else {
+      const int idx = (key >> a.log2_ps) - p0;
+      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)pr0, idx & 63);
+      const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)pr1, idx & 63);
+      const uint32_t page = idx >= 64 ? hi : lo;
+      return ((int64_t)page << a.log2_ps) + (key & ps_mask);
+    }
+  };
+  // Tokens of a tile's four 8-key groups (the same for K and V).
+  struct TileToks {
+    int64_t tok[4];
+  };
+  auto tile_toks = [&](int t0) __attribute__((always_inline)) -> TileToks {
+    TileToks tt;
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) tt.tok[rg] = (PAGED || rg == 0) ? key_tok(t0 + 8 * rg) : tt.tok[0] + 8 * rg;
+    return tt;
+  };
+
+  // ---- loads ----------------------------------------------------------------
+  const int lrow = lane >> 3;
+  // 16-bit: lane L of block (rg, cg) fetches row 8 rg + L / 8, chunk
+  // 8 cg + ((L % 8) ^ lds_g(row % 16)); rg's parity picks the offset set.
+  const uint32_t v16_even = lrow * hkvd + (((lane & 7) ^ lds_g(lrow)) << 4);
+  const uint32_t v16_odd = lrow * hkvd + (((lane & 7) ^ lds_g(8 + lrow)) << 4);
+  // 8-bit: load i covers rows RPL i .. + RPL - 1; lane L: row RPL i + L / U,
+  // LDS unit w = L % U.
+  constexpr int U = Gm::U, RPL = Gm::RPL;
+  const int qr = lane / U, qw = lane % U;
+  const int ctx_last = kend - 1;
+  // Issue the loads of K (is_v false) or V of this wave's tile starting at key
+  // t0 into dst (the wave's part of a slot array); `to` holds the tile's group
+  // offsets (tile_offs).  A tile that is not `valid` (past the wave's last)
+  // issues the same loads, reading nothing.
+  // Q8: after the quants, two loads of scale rows (one per 16-key block, one
+  // page) land behind them: block b at KT + 256 b, row r (LDS row 16 b + r;
+  // K row 16 b + r holds key 16 b + swap23(r)) at r SROW.
+  const int s_dw = lane % (SROW / 4 > 0 ? SROW / 4 : 1);               // dword of the row
+  const int s_r = min(lane / (SROW / 4 > 0 ? SROW / 4 : 1), 15);       // row within the block
+  const char* ksg = (const char*)a.k_scale + g * SROW;
+  const char* vsg = (const char*)a.v_scale + g * SROW;
+  const int srow_bytes = a.n_kv_heads * SROW;   // scale bytes per token (all KV heads)
+  auto issue = [&](int t0, const TileToks& to, bool is_v, uint8_t* dst, bool valid) __attribute__((always_inline)) {
+    const char* src = is_v ? vg : kg;
+    const int last = ctx_last - t0;           // last valid tile-relative key (< 31: the context's last tile)
+    const bool whole = last >= TK - 1;
+    if constexpr (!Q8) {
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        // rows past the end read the last valid row (same 8-row group, same page)
+        const int r0 = whole ? 8 * rg : __builtin_amdgcn_readfirstlane(min(8 * rg, last & ~7));
+        const char* base = src + (whole ? to.tok[rg] : key_tok(t0 + r0)) * hkvd;
+        uint32_t voff = (rg & 1) ? v16_odd : v16_even;
+        if (!whole) {
+          const int lr = min(lrow, last - r0);
+          voff = lr * hkvd + (((lane & 7) ^ lds_g(((8 * rg) & 15) + lrow)) << 4);
+        }
+#pragma unroll
+        for (int cg = 0; cg < D / 64; ++cg)
+          dec_load_lds16(base + 128 * cg, voff, valid, dst + (cg * 4 + rg) * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < LKQ; ++i) {
+        const int m = RPL * i + qr;
+        const int kofs = is_v ? m : swap23(m);               // this lane's key, tile-relative
+        const int kb = is_v ? RPL * i : swap23(RPL * i);       // the load's first key
+        const int c16 = is_v ? (qw ^ (2 * dec_fv<D>(m))) : (qw ^ dec_sk<D>(m));
+        // the load's rows lie in one 16-key block (one page: pages hold >= 16 keys)
+        const int kbase = whole ? kb : __builtin_amdgcn_readfirstlane(min(kb, last) & ~15);
+        const int key = whole ? kofs : min(kofs, last);
+        // kb is 4-aligned and its 8-key group starts at kb & ~7
+        const char* base = src + (whole ? to.tok[kb >> 3] + (kb & 7) : key_tok(t0 + kbase)) * hkvd;
+        dec_load_lds16(base, (uint32_t)((key - kbase) * hkvd + 16 * c16), valid, dst + i * 1024);
+      }
+      const char* ssrc = is_v ? vsg : ksg;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int kofs = 16 * b + (is_v ? s_r : swap23(s_r));
+        const int kbase = whole ? 16 * b : __builtin_amdgcn_readfirstlane(min(16 * b, last) & ~15);
+        const int key = whole ? kofs : min(kofs, last);
+        // the block's first token (the tile's 8-key group 2 b)
+        const int64_t tok0 = whole ? to.tok[2 * b] : key_tok(t0 + kbase);
+        const char* base = ssrc + tok0 * srow_bytes;
+        dec_load_lds4(base, (uint32_t)((key - kbase) * srow_bytes + 4 * s_dw), valid, dst + KT + 256 * b);
+      }
+    }
+  };
+
+  // ---- state ----------------------------------------------------------------
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  float m_ref = kNegInf, l = 0.f;
+  const float c = a.scale_log2;
+
+  // 16-bit operand read offsets (as in the prefill kernel, 32-row tiles).
+  const int kofs16 = ((lane >> 3) & 3) * 1024 + (lane & 7) * 128 + ((h ^ lds_g(lane & 15)) << 4);
+  const int v_r = 4 * h + ((lane & 15) >> 2);
+  const int v_cc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int vofs1 = v_r * 128 + ((v_cc ^ lds_g(v_r)) << 4) + (lane & 1) * 8;
+  const int vofs2 = 1024 + v_r * 128 + ((v_cc ^ lds_g(v_r + 8)) << 4) + (lane & 1) * 8;
+  // 8-bit V reads (PV step): lane 4 j + c of each 16-lane group names key
+  // 16 kstep + 8 h + j (+ 4) and bytes 8 c .. + 7 of the group's 32-byte
+  // unit 2 p + (lane / 16) % 2, stored at unit ^ fV(key); fV depends only on
+  // key % 4 = j, so per lane it is one value.
+  int tr_row[2], tr_unit[D / 64 > 0 ? D / 64 : 1];
+  {
+    const int trj = (lane & 15) >> 2, trc = lane & 3, gi = (lane >> 4) & 1;
+    const int fv = dec_fv<D>(trj);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) tr_row[ks] = (16 * ks + 8 * h + trj) * D + 8 * trc;
+#pragma unroll
+    for (int p = 0; p < D / 64; ++p) tr_unit[p] = 32 * ((2 * p + gi) ^ fv);
+  }
+
+  // One tile: QK, mask, softmax, PV; loads of tile tw + NS go out as the
+  // slot's K and V are read.  `first` = the wave's first tile.
+  auto tile = [&](int tw, auto slot, bool first) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slot)::value;
+    uint8_t* kt = kslot(slot) + wave * WS;
+    uint8_t* vt = vslot(slot) + wave * WS;
+    const int j = wave + kDecWaves * tw;
+    const int t0 = k0 + TK * j;
+    const bool refill = tw + NS < nt;   // the slot's next tile is one of the wave's
+    const int t0n = t0 + TK * kDecWaves * NS;
+
+    // K(tw) (and its scale rows) has arrived when at most V(tw) and the K/V
+    // groups of the NS - 1 later slots are outstanding.
+    dec_wait_vm<LV + (NS - 1) * (LK + LV)>();
+
+    f32x16 sc = f32x16{};
+    if constexpr (!Q8) {
+      constexpr int QPF = 4;
+      i16x8 kr[KS];
+      auto load = [&](int ks) __attribute__((always_inline)) {
+        kr[ks] = *LDS_PTR(const i16x8, kt + (kofs16 ^ ((ks & 3) << 5)) + (ks >> 2) * 4096);
+      };
+#pragma unroll
+      for (int ks = 0; ks < QPF && ks < KS; ++ks) load(ks);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + QPF < KS) load(ks + QPF);
+        sc = M::mfma(__builtin_bit_cast(vec8, kr[ks]), qf[ks], sc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+      // The K scale row of this lane's LDS row (single vector loads: the
+      // compiler keeps their alias information).
+      uint32_t ksr[SROW / 4];
+      {
+        const int m = lane & 31;
+        const uint8_t* kr_s = kt + KT + 256 * (m >> 4) + (m & 15) * SROW;
+        if constexpr (SROW == 16) {
+          const u32x4 v = *LDS_PTR(const u32x4, kr_s);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ksr[e] = v[e];
+        } else if constexpr (SROW == 8) {
+          const u32x2 v = *LDS_PTR(const u32x2, kr_s);
+          ksr[0] = v[0];
+          ksr[1] = v[1];
+        } else {
+          ksr[0] = *LDS_PTR(const uint32_t, kr_s);
+        }
+      }
+      const int m = lane & 31;
+      const uint8_t* krow = kt + m * D;
+      constexpr int QPF = DB < 3 ? DB : 3;
+      u32x4 kr[DB];
+      auto load = [&](int jj) __attribute__((always_inline)) {
+        kr[jj] = *LDS_PTR(const u32x4, krow + 16 * ((2 * jj + h) ^ dec_sk<D>(m)));
+      };
+#pragma unroll
+      for (int jj = 0; jj < QPF; ++jj) load(jj);
+      const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+#pragma unroll
+      for (int jj = 0; jj < DB; ++jj) {
+        if (jj + QPF < DB) load(jj + QPF);
+        const uint32_t sb = (jj & 1) ? (ksr[jj >> 1] >> 16) : (ksr[jj >> 1] & 0xffffu);
+        const h2 ss = __builtin_bit_cast(h2, sb | (sb << 16));
+        uint32_t w[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          // byte u = quant ^ 0x80 under exponent byte 0x64 is the fp16 1024 + u:
+          // minus 1152 gives the quant exactly, times the scale rounds once
+          const uint32_t x = kr[jj][k] ^ 0x80808080u;
+          const h2 lo = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x, 0x04010400u));
+          const h2 hi = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u));
+          w[2 * k] = __builtin_bit_cast(uint32_t, (lo - bias) * ss);
+          w[2 * k + 1] = __builtin_bit_cast(uint32_t, (hi - bias) * ss);
+        }
+        const u32x4 a0 = {w[0], w[1], w[2], w[3]}, a1 = {w[4], w[5], w[6], w[7]};
+        sc = M::mfma(__builtin_bit_cast(vec8, a0), qf[2 * jj], sc);
+        sc = M::mfma(__builtin_bit_cast(vec8, a1), qf[2 * jj + 1], sc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // This slot's K has been read: its next tile's K group goes out.
+    const TileToks ton = tile_toks(t0n);
+    issue(t0n, ton, false, kt, refill);
+
+    // Element e of sc is S^T row 8 (e / 4) + 4 h + e % 4 (Q8: key swap23 of it).
+    auto key_of = [&](int e) __attribute__((always_inline)) {
+      const int r = 8 * (e >> 2) + 4 * h + (e & 3);
+      return Q8 ? swap23(r) : r;
+    };
+    if (TK * j + TK - 1 > mask_from) {
+      const int rel = lim - t0;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sc[e] = key_of(e) > rel ? kNegInf : sc[e];
+    }
+
+    // Softmax weights against the integer reference (see kSumLimit): the
+    // wave's first tile sets it; a tile whose sum would overflow raises it.
+    if (first) {
+      float mx = sc[0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[e]);
+      m_ref = ceilf(max_with_partner(mx) * c);
+    }
+    vec8 pb[2];
+    float rs = 0.f;
+    auto weights = [&]() __attribute__((always_inline)) {
+      const float base = m_ref == kNegInf ? 0.f : m_ref;
+      float p32[16];
+      rs = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        p32[e] = __builtin_amdgcn_exp2f(fmaf(sc[e], c, -base));
+        if ((e & 7) == 7) {
+          pb[e >> 3] = M::from_f32(p32 + (e & ~7));
+          rs = M::sum8(pb[e >> 3], rs);
+        }
+      }
+    };
+    weights();
+    if (__builtin_expect(__ballot(!(l + rs <= kSumLimit)) != 0, 0)) {
+      float mx = sc[0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[e]);
+      const float m_new = fmaxf(m_ref, ceilf(max_with_partner(mx) * c));
+      if (m_new != kNegInf && m_new != m_ref) {
+        const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);   // 2^-k, 0 if m_ref was -inf
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        m_ref = m_new;
+      }
+      weights();
+    }
+    l += rs;
+
+    // V(tw) has arrived when at most the later slots' groups and the K group
+    // just issued are outstanding.
+    dec_wait_vm<(NS - 1) * (LK + LV) + LK>();
+    if constexpr (Q8) {
+      // The V scale rows of this tile, transposed to [block][key] for the PV
+      // reads (lanes 0-31, one key each).
+      if (h == 0) {
+        const int key = lane & 31;
+        const uint8_t* vr = vt + KT + 256 * (key >> 4) + (key & 15) * SROW;
+        uint32_t w4[SROW / 4];
+        if constexpr (SROW == 16) {
+          const u32x4 v = *LDS_PTR(const u32x4, vr);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w4[e] = v[e];
+        } else if constexpr (SROW == 8) {
+          const u32x2 v = *LDS_PTR(const u32x2, vr);
+          w4[0] = v[0];
+          w4[1] = v[1];
+        } else {
+          w4[0] = *LDS_PTR(const uint32_t, vr);
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const uint32_t w2 = w4[db >> 1];
+          const uint16_t sc16 = (uint16_t)((db & 1) ? (w2 >> 16) : (w2 & 0xffffu));
+          vst[(wave * DB + db) * 32 + key] = sc16;
+        }
+      }
+    }
+
+    // O^T[d][qv] += V^T[d][key] P^T[key][qv], 16 keys per MFMA.
+#pragma unroll
+    for (int kstep = 0; kstep < 2; ++kstep) {
+      if constexpr (!Q8) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          // rows 16 kstep + 4 h + (lane % 16) / 4 and + 8 (the keys of pb[kstep])
+          const int imm = (db >> 1) * 4096 + kstep * 2048;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vt + (vofs1 ^ ((db & 1) << 6)) + imm));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vt + (vofs2 ^ ((db & 1) << 6)) + imm));
+          const vec8 av = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[db] = M::mfma(av, pb[kstep], o[db]);
+        }
+      } else {
+        // 8-bit V, 64 values of d per step p: each 16-lane group reads 4 keys
+        // x 32 bytes with ds_read_b64_tr_b16 (lane 4 j + c names key row j,
+        // bytes 8 c .. + 7), lo for keys 16 kstep + 8 h + 0..3 and hi for
+        // + 4..7; lane L then holds the byte pair (d, d + 1), d = 64 p + 2 (L % 32),
+        // of 8 keys.  Even bytes make the A operand of o[2 p] (row m: d =
+        // 64 p + 2 m), odd bytes that of o[2 p + 1] (d + 1), each widened with
+        // the keys' scales of block d / 32.
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+        const int gi = (lane >> 4) & 1;
+#pragma unroll
+        for (int p = 0; p < D / 64; ++p) {
+          const int u = 2 * p + gi;   // 32-byte unit of the group's window
+          // one offset per read from the slot base (a long chain of address
+          // steps would lose the compiler's alias information)
+          const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              LDS_PTR(i16x4, vt + (tr_row[kstep] + tr_unit[p]))));
+          const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              LDS_PTR(i16x4, vt + (tr_row[kstep] + 4 * D + tr_unit[p]))));
+          // scales of keys 16 kstep + 8 h + 0..7 at block 2 p + gi
+          const u32x4 sv = *LDS_PTR(const u32x4, (uint8_t*)vst + ((wave * DB + u) * 32 + 16 * kstep + 8 * h) * 2);
+          const uint32_t x[4] = {lo[0] ^ 0x80808080u, lo[1] ^ 0x80808080u, hi[0] ^ 0x80808080u, hi[1] ^ 0x80808080u};
+          uint32_t we[4], wo[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            // x[k] = bytes (d, d + 1) of keys 2k and 2k + 1
+            const h2 ev = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x[k], 0x04020400u));
+            const h2 od = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x[k], 0x04030401u));
+            // (the element goes through a plain variable: a bit cast of a
+            // vector element as such reads element 0)
+            const uint32_t sk = sv[k];
+            const h2 sc2 = __builtin_bit_cast(h2, sk);
+            we[k] = __builtin_bit_cast(uint32_t, (ev - bias) * sc2);
+            wo[k] = __builtin_bit_cast(uint32_t, (od - bias) * sc2);
+          }
+          o[2 * p] = M::mfma(__builtin_bit_cast(vec8, u32x4{we[0], we[1], we[2], we[3]}), pb[kstep], o[2 * p]);
+          o[2 * p + 1] = M::mfma(__builtin_bit_cast(vec8, u32x4{wo[0], wo[1], wo[2], wo[3]}), pb[kstep], o[2 * p + 1]);
+        }
+      }
+    }
+    // This slot's V has been read: its next tile's V group goes out.
+    issue(t0n, ton, true, vt, refill);
+  };
+
+  // ---- tile loop ------------------------------------------------------------
+  // Prologue: the first NS tiles' K and V groups, in tile order.
+  auto prologue = [&](auto slot) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slot)::value;
+    const int t0 = k0 + TK * (wave + kDecWaves * SL);
+    const TileToks to = tile_toks(t0);
+    issue(t0, to, false, kslot(slot) + wave * WS, SL < nt);
+    issue(t0, to, true, vslot(slot) + wave * WS, SL < nt);
+  };
+  prologue(std::integral_constant<int, 0>{});
+  if constexpr (NS > 1) prologue(std::integral_constant<int, 1>{});
+  if constexpr (NS > 2) prologue(std::integral_constant<int, 2>{});
+  if constexpr (NS > 3) prologue(std::integral_constant<int, 3>{});
+  // Whole groups of NS tiles, then the remainder with nested conditions: on
+  // every path the slots run in order, so the compiler's own load counting
+  // agrees with the waits above (a path that skips a slot and runs a later
+  // one would make it wait for every load in flight).
+  int t = 0;
+  for (; t + NS <= nt; t += NS) {
+    tile(t, std::integral_constant<int, 0>{}, t == 0);
+    if constexpr (NS > 1) tile(t + 1, std::integral_constant<int, 1>{}, false);
+    if constexpr (NS > 2) tile(t + 2, std::integral_constant<int, 2>{}, false);
+    if constexpr (NS > 3) tile(t + 3, std::integral_constant<int, 3>{}, false);
+  }
+  if constexpr (NS > 1) {
+    if (t < nt) {
+      tile(t, std::integral_constant<int, 0>{}, t == 0);
+      if constexpr (NS > 2) {
+        if (t + 1 < nt) {
+          tile(t + 1, std::integral_constant<int, 1>{}, false);
+          if constexpr (NS > 3)
+            if (t + 2 < nt) tile(t + 2, std::integral_constant<int, 2>{}, false);
+        }
+      }
+    }
+  }
+
+  // ---- combine the four waves ---------------------------------------------
+  // Each wave leaves its reference, sum and unnormalised accumulators; its own
+  // slots (all loads consumed) hold the accumulators as 1 KB blocks
+  // bj = 4 db + jq of [h][qv][4 floats], d = 32 db + 8 jq + 4 h + 0..3.
+  dec_wait_vm<0>();
+  const float l_tot = sum_with_partner(l);
+  if (h == 0) {
+    ml_m[wave][qv] = m_ref;
+    ml_l[wave][qv] = l_tot;
+  }
+  // Blocks of one slot array; with a multiple of 4 the blocks the four waves
+  // of a reading thread group touch in one step lie in one array, known at
+  // compile time (a pointer chosen among the arrays at run time would keep
+  // the compiler from telling the arrays apart in the tile loop).  Otherwise
+  // (8-bit pages at head dimension 64) a separate array holds the staging.
+  constexpr int BPA = KT / 1024;
+  constexpr bool OWN_STAGE = BPA % 4 != 0;
+  __shared__ __attribute__((aligned(1024))) uint8_t ostage[OWN_STAGE ? kDecWaves * 128 * D : 16];
+  auto arr_of = [&](auto ai) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int A = decltype(ai)::value;
+    if constexpr (A == 0) return ks0;
+    else if constexpr (A == 1) return vs0;
+    else if constexpr (A == 2) return ks1;
+    else if constexpr (A == 3) return vs1;
+    else if constexpr (A == 4) return ks2;
+    else if constexpr (A == 5) return vs2;
+    else if constexpr (A == 6) return ks3;
+    else return vs3;
+  };
+  // block bj (compile time) of wave w
+  auto stage = [&](auto bjc, int w) __attribute__((always_inline)) -> float* {
+    constexpr int BJ = decltype(bjc)::value;
+    if constexpr (OWN_STAGE) return (float*)(ostage + (w * 4 * DB + BJ) * 1024);
+    else return (float*)(arr_of(std::integral_constant<int, BJ / BPA>{}) + w * WS + (BJ % BPA) * 1024);
+  };
+  if constexpr (!Q8) {
+    dec_static_for<0, 4 * DB>([&](auto bjc) __attribute__((always_inline)) {
+      constexpr int BJ = decltype(bjc)::value;
+      constexpr int DBI = BJ / 4, JQ = BJ % 4;
+      const f32x4 v4 = {o[DBI][4 * JQ], o[DBI][4 * JQ + 1], o[DBI][4 * JQ + 2], o[DBI][4 * JQ + 3]};
+      *(f32x4*)(stage(bjc, wave) + (h * 32 + qv) * 4) = v4;
+    });
+  } else {
+    // o[2 p + par] row m = 8 j + 4 h + i holds d = 64 p + 16 j + 8 h + 2 i + par:
+    // four consecutive d = 64 p + 16 j + 8 h + 4 f + 0..3 (f = i / 2) go to
+    // block 4 (2 p + j / 2) + 2 (j % 2) + h, half f.
+    dec_static_for<0, D / 8>([&](auto c) __attribute__((always_inline)) {   // (P, J, F): D/64 x 4 x 2
+      constexpr int C = decltype(c)::value;
+      constexpr int P = C / 8, J = (C / 2) % 4, F = C % 2;
+      constexpr int BJ0 = 4 * (2 * P + J / 2) + 2 * (J % 2);
+      const f32x4 v4 = {o[2 * P][4 * J + 2 * F], o[2 * P + 1][4 * J + 2 * F], o[2 * P][4 * J + 2 * F + 1],
+                        o[2 * P + 1][4 * J + 2 * F + 1]};
+      *(f32x4*)(stage(std::integral_constant<int, BJ0>{}, wave) + h * 256 + (F * 32 + qv) * 4) = v4;
+    });
+  }
+  __syncthreads();
+
+  // 256 threads over the 32 x D/4 four-float units: step i takes blocks
+  // bj = 4 i + (thread / 64), unit (h, qv) = thread % 64 of the block.
+  const int64_t pairs = (int64_t)a.rows * a.n_q_heads;
+  const int uq = tid & 31, uh = (tid >> 5) & 1, wq = tid >> 6;
+  float mw[kDecWaves], lw[kDecWaves], mx = kNegInf;
+#pragma unroll
+  for (int w = 0; w < kDecWaves; ++w) {
+    mw[w] = ml_m[w][uq];
+    lw[w] = ml_l[w][uq];
+    mx = fmaxf(mx, mw[w]);
+  }
+  float sw[kDecWaves], lsum = 0.f;
+#pragma unroll
+  for (int w = 0; w < kDecWaves; ++w) {
+    // a wave that saw no key of this query vector adds nothing
+    sw[w] = (mw[w] == kNegInf || !(lw[w] > 0.f)) ? 0.f : __builtin_amdgcn_exp2f(mw[w] - mx);   // exact: integers
+    lsum += sw[w] * lw[w];
+  }
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  const int urow = uq / G, uhead = g * G + uq % G;
+  const int64_t pair = (int64_t)urow * a.n_q_heads + uhead;
+  const bool uvalid = uq < nqv;
+  dec_static_for<0, DB>([&](auto ic) __attribute__((always_inline)) {
+    constexpr int I = decltype(ic)::value;   // blocks 4 I .. 4 I + 3: one per reading wave
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float* src[kDecWaves];
+    if constexpr (OWN_STAGE) {
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) src[w] = (float*)(ostage + (w * 4 * DB + 4 * I + wq) * 1024);
+    } else {
+      constexpr int A = (4 * I) / BPA;         // the four blocks' array (BPA is a multiple of 4)
+      constexpr int B0 = (4 * I) % BPA;
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w)
+        src[w] = (float*)(arr_of(std::integral_constant<int, A>{}) + w * WS + (B0 + wq) * 1024);
+    }
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) acc += sw[w] * *(const f32x4*)(src[w] + (uh * 32 + uq) * 4);
+    if (!uvalid) return;
+    const int bj = 4 * I + wq;
+    const int d = 32 * (bj >> 2) + 8 * (bj & 3) + 4 * uh;
+    if (a.n_splits == 1) {
+      const uint32_t lo = E::bits(acc[0] * inv) | ((uint32_t)E::bits(acc[1] * inv) << 16);
+      const uint32_t hi = E::bits(acc[2] * inv) | ((uint32_t)E::bits(acc[3] * inv) << 16);
+      *(u32x2*)(a.out + pair * D + d) = u32x2{lo, hi};
+    } else {
+      *(f32x4*)(a.ws_o + ((int64_t)s * pairs + pair) * D + d) =
+          f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+    }
+  });
+  if (a.n_splits > 1 && uvalid && wq == 0 && uh == 0)
+    a.ws_lse[(int64_t)s * pairs + pair] = lsum > 0.f ? mx + log2f(lsum) : kNegInf;
+}
+
+template <int D, class E, bool PAGED, bool Q8>
+hipError_t launch_decode_t(const AttnArgs& a, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((attn_decode_kernel<D, E, PAGED, Q8>), dim3(grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace ppa

@@ -119,6 +119,11 @@ hipError_t launch_attention_q8(const AttnArgs& a, int head_dim, int dtype, int g
 // (dequantized 8-bit pages).
 hipError_t launch_attention_kv16(const AttnArgs& a, int head_dim, int dtype, int grid, hipStream_t stream);
 hipError_t launch_kv_dequant_q8(const DequantQ8Args& a, hipStream_t stream);
+// The narrow kernel (at most 32 query vectors per KV head, one sequence;
+// 16-bit pages of >= 8 tokens, 8-bit pages of >= 16, or contiguous K/V):
+// grid = n_splits * Hkv workgroups.
+hipError_t launch_attention_decode(const AttnArgs& a, int head_dim, int dtype, bool paged, bool q8, int grid,
+                                   hipStream_t stream);
 
 // The per-head-dimension halves of launch_attention and launch_attention_q8
 // (separate translation units).

@@ -55,6 +55,23 @@ static int split_rule(int32_t cores, int32_t kv_heads, int32_t tiles, int32_t pe
   return int(splits);
 }
 
+// Split workspace and merge grid of a plan with n_eff splits over ws_rows rows.
+static void plan_workspace(const Shape& s, int64_t n_eff, int64_t ws_rows, int64_t grid_rows, int32_t n_seqs,
+                           ppa_plan* out) {
+  if (n_eff > 1) {
+    const int64_t pairs = ws_rows * s.n_q_heads;
+    const int64_t o_bytes = (n_eff * pairs * s.head_dim * 4 + 255) / 256 * 256;
+    const int64_t lse_bytes = (n_eff * pairs * 4 + 255) / 256 * 256;
+    out->workspace_bytes = o_bytes + lse_bytes;
+    const int threads_per_pair = s.head_dim / 4 * merge_groups_for(int(n_eff));
+    const int pairs_per_block = merge_block_threads(s.head_dim, int(n_eff)) / threads_per_pair;
+    out->merge_grid = int32_t((grid_rows * s.n_q_heads + pairs_per_block - 1) / pairs_per_block * n_seqs);
+  } else {
+    out->workspace_bytes = 0;
+    out->merge_grid = 0;
+  }
+}
+
 // The plan of a launch: split units from the longest context `ctx`, the
 // split rule's m tiles `rule_tiles`, the grid's m tiles from `grid_rows`, the
 // workspace from `ws_rows`, times `n_seqs` sequences.
@@ -90,24 +107,48 @@ static int plan_launch(const Shape& s, int64_t ctx, int64_t rule_tiles, int64_t 
   if (grid >= (int64_t(1) << 31)) return PPA_ERR_TOO_LARGE;
   out->grid = int32_t(grid);
   out->reserved = 0;
-  if (n_eff > 1) {
-    const int64_t pairs = ws_rows * s.n_q_heads;
-    const int64_t o_elems = n_eff * pairs * s.head_dim;
-    if (o_elems >= (int64_t(1) << 31)) return PPA_ERR_TOO_LARGE;
-    const int64_t o_bytes = (o_elems * 4 + 255) / 256 * 256;
-    const int64_t lse_bytes = (n_eff * pairs * 4 + 255) / 256 * 256;
-    out->workspace_bytes = o_bytes + lse_bytes;
-    // the merge kernel: groups of head_dim / 4 threads per pair (4 groups for
-    // 16 splits or more, else 1); with several sequences one row of blocks per
-    // sequence
-    const int threads_per_pair = s.head_dim / 4 * merge_groups_for(int(n_eff));
-    const int pairs_per_block = kThreads / threads_per_pair;
-    out->merge_grid = int32_t((grid_rows * s.n_q_heads + pairs_per_block - 1) / pairs_per_block * n_seqs);
-    if (n_splits_req > 0 && out->workspace_bytes > max_ws_bytes) return PPA_ERR_WORKSPACE;
+  if (n_eff > 1 && n_eff * ws_rows * s.n_q_heads * s.head_dim >= (int64_t(1) << 31)) return PPA_ERR_TOO_LARGE;
+  // the merge kernel: groups of head_dim / 4 threads per pair (4 groups for
+  // 16 splits or more, else 1); with several sequences one row of blocks per
+  // sequence
+  plan_workspace(s, n_eff, ws_rows, grid_rows, n_seqs, out);
+  if (n_eff > 1 && n_splits_req > 0 && out->workspace_bytes > max_ws_bytes) return PPA_ERR_WORKSPACE;
+  return PPA_OK;
+}
+
+// The narrow kernel's plan: splits of whole 32-key tiles (and whole pages),
+// one workgroup per CU over the KV heads unless the splits would get fewer
+// than kNarrowMinKeys keys, at most kNarrowPages pages per split.  Returns 1
+// (not planned) when the call needs more than kNarrowMaxSplits splits.
+static int plan_narrow(const Shape& s, int32_t n_splits_req, int64_t max_ws_bytes, ppa_plan* out) {
+  const int64_t ctx = s.history + s.rows;
+  const int32_t unit = s.page_size > kNarrowTile ? s.page_size : kNarrowTile;
+  const int64_t n_units = (ctx + unit - 1) / unit;
+  int64_t splits;
+  if (n_splits_req <= 0) {
+    splits = (kNumCUs + s.n_kv_heads - 1) / s.n_kv_heads;
+    const int64_t by_keys = (ctx + kNarrowMinKeys - 1) / kNarrowMinKeys;
+    if (splits > by_keys) splits = by_keys;
   } else {
-    out->workspace_bytes = 0;
-    out->merge_grid = 0;
+    splits = n_splits_req;
   }
+  if (splits > n_units) splits = n_units;
+  if (splits < 1) splits = 1;
+  int64_t units_per_split = (n_units + splits - 1) / splits;
+  const int64_t max_units = int64_t(kNarrowPages) * s.page_size / unit;
+  if (units_per_split > max_units) units_per_split = max_units;
+  const int64_t split_tokens = units_per_split * unit;
+  const int64_t n_eff = (ctx + split_tokens - 1) / split_tokens;
+  if (n_eff > kNarrowMaxSplits || n_eff * s.rows * s.n_q_heads * s.head_dim >= (int64_t(1) << 31)) return 1;
+  out->n_splits = int32_t(n_eff < 1 ? 1 : n_eff);
+  out->split_tokens = int32_t(split_tokens);
+  out->m_tile = kNarrowVectors;
+  out->kv_tile = kNarrowTile;
+  out->tiles_m = 1;
+  out->grid = int32_t(s.n_kv_heads * out->n_splits);
+  out->reserved = 0;
+  plan_workspace(s, out->n_splits, s.rows, s.rows, 1, out);
+  if (n_splits_req > 0 && out->workspace_bytes > max_ws_bytes) return PPA_ERR_WORKSPACE;
   return PPA_OK;
 }
 
@@ -119,6 +160,10 @@ static int64_t m_tiles(int64_t rows, int64_t grid_rows, const Shape& s) {
 }
 
 int make_plan(const Shape& s, int32_t n_splits_req, int64_t max_ws_bytes, ppa_plan* out) {
+  if (s.allow_narrow && narrow_call(s.rows, s.n_q_heads / s.n_kv_heads, s.page_size)) {
+    const int rc = plan_narrow(s, n_splits_req, max_ws_bytes, out);
+    if (rc <= 0) return rc;
+  }
   return plan_launch(s, s.history + s.rows, m_tiles(s.rows, s.rows, s), s.rows, s.rows, 1, n_splits_req,
                      max_ws_bytes, out);
 }

@@ -23,22 +23,47 @@ constexpr int kWgPerCu = 1;      // resident attention workgroups per CU (LDS/VG
 constexpr int kMaxSplits = 128;
 constexpr int kChunkRowsForCap = 2048;  // the cap: tile slots of a full 2048-row chunk
 
-// Thread groups per (row, head) pair in the merge kernel: 4 for kMergeFourGroups
-// splits or more, else 1 (the planner sizes the merge grid by it).
+// Thread groups per (row, head) pair in the merge kernel: 16 for
+// kMergeSixteenGroups splits or more (decode steps: a few pairs, many splits),
+// 4 for kMergeFourGroups or more, else 1; a merge block has max(256, threads
+// per pair) threads (the planner sizes the merge grid by these).
 constexpr int kMergeFourGroups = 16;
-constexpr int merge_groups_for(int n_splits) { return n_splits >= kMergeFourGroups ? 4 : 1; }
+constexpr int kMergeSixteenGroups = 64;
+constexpr int merge_groups_for(int n_splits) {
+  return n_splits >= kMergeSixteenGroups ? 16 : n_splits >= kMergeFourGroups ? 4 : 1;
+}
+constexpr int merge_block_threads(int head_dim, int n_splits) {
+  return head_dim / 4 * merge_groups_for(n_splits) > 256 ? head_dim / 4 * merge_groups_for(n_splits) : 256;
+}
+
+// The narrow kernel (decode steps, appends of a few rows): one sequence with
+// at most kNarrowVectors query vectors (rows x Hq/Hkv) per KV head and pages
+// of 8 tokens or more.  A workgroup is one (split, KV head); its four waves
+// stream 32-key tiles and keep the pages of their split (at most
+// kNarrowPages) in registers.  The planner aims at one workgroup per CU with
+// at least kNarrowMinKeys keys per split.
+constexpr int kNarrowVectors = 32;
+constexpr int kNarrowTile = 32;
+constexpr int kNarrowPages = 128;
+constexpr int kNarrowMinKeys = 256;
+constexpr int kNarrowMaxSplits = 4096;
+constexpr bool narrow_call(int64_t rows, int64_t group, int32_t page_size) {
+  return rows * group <= kNarrowVectors && page_size >= 8;
+}
 
 struct Shape {
   int64_t history;
   int32_t rows, n_q_heads, n_kv_heads, head_dim, page_size, dtype;
-  int32_t q8 = 0;  // 8-bit K/V pages (changes the m tile at head_dim 128)
+  int32_t q8 = 0;            // 8-bit K/V pages (changes the m tile at head_dim 128)
+  int32_t allow_narrow = 1;  // 0: plan for the prefill kernel whatever the size
 };
 
 // Shape checks shared by every entry point (no pointers).
 int check_shape(const Shape& s);
 
 // The plan for a call; assumes check_shape passed.  max_ws_bytes bounds an
-// explicitly requested split count.
+// explicitly requested split count.  A narrow call (see narrow_call) gets
+// m_tile = kv_tile = 32 and grid = Hkv * n_splits.
 int make_plan(const Shape& s, int32_t n_splits_req, int64_t max_ws_bytes, ppa_plan* out);
 
 // The plan of a launch over n_seqs sequences: s.rows is the total row

@@ -40,6 +40,15 @@ def test_binding_covers_every_declared_symbol():
         assert name in pkg._SIGNATURES, name
 
 
+def _merge_pairs_per_block(d, n_splits):
+    """The merge kernel serves a (row, head) pair with groups of d/4 threads:
+    16 groups from 64 splits, 4 from 16, else 1; a block has max(256, threads
+    per pair) threads."""
+    groups = 16 if n_splits >= 64 else 4 if n_splits >= 16 else 1
+    per_pair = d // 4 * groups
+    return max(256, per_pair) // per_pair
+
+
 def test_split_rule_reproduces_the_pr_table():
     for cores, kv_heads, piece_rows, tiles, splits in _pins.load_golden("page_split_table.txt"):
         assert pkg.paged_prefill_split_rule(cores, kv_heads, tiles) == splits
@@ -72,24 +81,55 @@ def test_plan_matches_the_workloads():
 def test_plan_invariants(history, rows, hq, hkv, d, ps, req):
     p = pkg.paged_prefill_plan(history, rows, hq, hkv, d, ps, req)
     ctx = history + rows
-    unit = max(64, ps)
-    assert p["split_tokens"] % 64 == 0 and p["split_tokens"] % ps == 0
-    assert 1 <= p["n_splits"] <= 64
+    # calls with at most 32 query vectors per KV head and pages of >= 8 tokens
+    # get the narrow kernel: 32-key tiles, one 32-vector m tile, one workgroup
+    # per (split, KV head)
+    narrow = rows * (hq // hkv) <= 32 and ps >= 8
+    tile = 32 if narrow else 64
+    unit = max(tile, ps)
+    assert p["split_tokens"] % tile == 0 and p["split_tokens"] % ps == 0
+    assert p["kv_tile"] == tile
+    assert 1 <= p["n_splits"] <= (4096 if narrow else 64)
     # the splits cover [0, ctx) and none is empty
     assert (p["n_splits"] - 1) * p["split_tokens"] < ctx <= p["n_splits"] * p["split_tokens"]
-    # two query blocks per wave (256-vector m tiles) at d <= 128 once the call
-    # has more query vectors than one 128-vector tile
-    assert p["m_tile"] == (256 if d <= 128 and rows * (hq // hkv) > 128 else 128)
-    assert p["tiles_m"] == -(-rows * (hq // hkv) // p["m_tile"])
+    if narrow:
+        assert p["m_tile"] == 32 and p["tiles_m"] == 1
+        assert p["split_tokens"] // ps <= 128          # the pages a split keeps in registers
+    else:
+        # two query blocks per wave (256-vector m tiles) at d <= 128 once the
+        # call has more query vectors than one 128-vector tile
+        assert p["m_tile"] == (256 if d <= 128 and rows * (hq // hkv) > 128 else 128)
+        assert p["tiles_m"] == -(-rows * (hq // hkv) // p["m_tile"])
     assert p["grid"] == p["tiles_m"] * hkv * p["n_splits"]
     if req:
         assert p["n_splits"] <= max(1, min(req, -(-ctx // unit)))
     if p["n_splits"] > 1:
         assert p["workspace_bytes"] >= p["n_splits"] * rows * hq * (d + 1) * 4
-        groups = 4 if p["n_splits"] >= 16 else 1
-        assert p["merge_grid"] == -(-rows * hq // (256 // (d // 4 * groups)))
+        assert p["merge_grid"] == -(-rows * hq // _merge_pairs_per_block(d, p["n_splits"]))
     else:
         assert p["workspace_bytes"] == 0 and p["merge_grid"] == 0
+
+
+@pytest.mark.parametrize("history,hq,hkv,d,ps", [
+    (131072, 16, 2, 256, 16), (65536, 32, 4, 128, 16), (32768, 16, 2, 256, 16), (1 << 22, 8, 1, 64, 16),
+    (100000, 8, 1, 128, 8), (5000, 64, 8, 128, 32), (300, 16, 2, 256, 64)])
+def test_narrow_plans(history, hq, hkv, d, ps):
+    """Decode steps and appends of up to 32 query vectors per KV head: about
+    one workgroup per CU (256), no split under 256 keys unless the context is
+    shorter, whole pages and at most 128 of them per split."""
+    g = hq // hkv
+    for rows in sorted({1, max(1, 32 // g)}):
+        p = pkg.paged_prefill_plan(history, rows, hq, hkv, d, ps)
+        ctx = history + rows
+        assert p["m_tile"] == 32 and p["kv_tile"] == 32
+        assert p["split_tokens"] % max(32, ps) == 0 and p["split_tokens"] // ps <= 128
+        assert p["grid"] == hkv * p["n_splits"]
+        if p["split_tokens"] < 128 * ps:   # not bound by the page registers
+            assert p["grid"] <= 256 + hkv
+            assert p["n_splits"] == 1 or p["split_tokens"] >= 256 - max(32, ps)
+    # one vector past 32 per KV head: the prefill kernel
+    p = pkg.paged_prefill_plan(history, 32 // g + 1, hq, hkv, d, ps)
+    assert p["m_tile"] >= 128 and p["kv_tile"] == 64
 
 
 def test_planner_never_exceeds_a_full_chunk_workspace():
@@ -196,8 +236,7 @@ def test_varlen_plan_invariants(n, total, max_rows, max_ctx, hq, hkv, d, ps, req
         assert p["n_splits"] <= max(1, (256 // hkv) // tiles)
     if p["n_splits"] > 1:
         assert p["workspace_bytes"] >= p["n_splits"] * total * hq * (d + 1) * 4
-        groups = 4 if p["n_splits"] >= 16 else 1
-        assert p["merge_grid"] == -(-max_rows * hq // (256 // (d // 4 * groups))) * n
+        assert p["merge_grid"] == -(-max_rows * hq // _merge_pairs_per_block(d, p["n_splits"])) * n
     else:
         assert p["workspace_bytes"] == 0 and p["merge_grid"] == 0
 
