@@ -61,6 +61,18 @@ __device__ __forceinline__ void dec_wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
+// Every LDS read this wave has issued has returned its data (lgkmcnt(0)),
+// with the scheduler kept from moving anything across.  A slot's refill goes
+// out only after this: a direct-to-LDS load does not queue behind the wave's
+// LDS reads, and one with no memory to read (past the context or the wave's
+// last tile) writes its zeros almost at once, so it could overwrite rows a
+// read still in flight has not fetched yet.
+__device__ __forceinline__ void lds_reads_done() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int I, int N, class F>
 __device__ __forceinline__ void dec_static_for(F&& f) {
   if constexpr (I < N) {
@@ -69,21 +81,20 @@ __device__ __forceinline__ void dec_static_for(F&& f) {
   }
 }
 
-// 16-byte direct-to-LDS load (as load_lds16) that reads nothing when `valid`
-// is false: the buffer then has no records, so every lane is out of range and
-// the hardware skips the memory access.  The tile loop issues the loads of
-// tiles past a wave's last one this way, so every iteration issues the same
-// loads and the load counter waits below are constants.
-__device__ __forceinline__ void dec_load_lds16(const char* base, uint32_t voff, bool valid, void* lds) {
-  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)scalar_ptr(base), (short)0,
-                                                               valid ? 0x7fffffff : 0, 0x00020000);
+// 16-byte direct-to-LDS load (as load_lds16) over a buffer of `nrec` bytes
+// from `base`: a lane whose 16 bytes end past nrec reads nothing and its LDS
+// bytes are written with zeros.  The tile loop uses this for rows past the
+// context's end (they arrive as zeros) and for tiles past a wave's last
+// (nrec 0: every lane out of range, no memory access), so every iteration
+// issues the same loads and the load counter waits below are constants.
+__device__ __forceinline__ void dec_load_lds16(const char* base, uint32_t voff, uint32_t nrec, void* lds) {
+  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)scalar_ptr(base), (short)0, (int)nrec, 0x00020000);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(void, lds), 16, (int)voff, 0, 0, 0);
 }
 
 // The same with 4 bytes per lane (lane L writes lds + 4 L).
-__device__ __forceinline__ void dec_load_lds4(const char* base, uint32_t voff, bool valid, void* lds) {
-  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)scalar_ptr(base), (short)0,
-                                                               valid ? 0x7fffffff : 0, 0x00020000);
+__device__ __forceinline__ void dec_load_lds4(const char* base, uint32_t voff, uint32_t nrec, void* lds) {
+  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)scalar_ptr(base), (short)0, (int)nrec, 0x00020000);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(void, lds), 4, (int)voff, 0, 0, 0);
 }
 
@@ -206,31 +217,51 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(AttnArgs a) {
   __builtin_amdgcn_s_waitcnt(0x0F70);   // Q and pages: nothing else is in flight in the tile loop
 
   const int hkvd = a.n_kv_heads * D * EB;   // bytes per token (all KV heads)
-  const uint32_t page_bytes = (uint32_t)hkvd << a.log2_ps;
   const char* kg = (const char*)a.k + g * D * EB;
   const char* vg = (const char*)a.v + g * D * EB;
-  // Pool token (page ps + place in the page; contiguous: the key) of key
-  // `key` (wave-uniform); K/V bytes are at token hkvd, scales at token srow.
-  auto key_tok = [&](int key) __attribute__((always_inline)) -> int64_t {
-    if constexpr (!PAGED) {
-      return key;
-    } else {
-      const int idx = (key >> a.log2_ps) - p0;
-      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)pr0, idx & 63);
-      const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)pr1, idx & 63);
-      const uint32_t page = idx >= 64 ? hi : lo;
-      return ((int64_t)page << a.log2_ps) + (key & ps_mask);
-    }
+  const int ctx_last = kend - 1;
+
+  // ---- addressing -------------------------------------------------------------
+  // A tile's keys come in groups of GK consecutive keys that are consecutive
+  // tokens of one page (16-bit: 8, pages hold at least 8 tokens; 8-bit: 16,
+  // one scale block's rows, pages of at least 16).  Per group the tile keeps
+  // the pool byte offset of its first key's row (all KV heads; the 8-bit
+  // scale rows, 1/16 of the quant bytes per token, sit at 1/16 of it) and the
+  // bytes of its rows that lie in the context: the loads' range, so rows
+  // past the context's end arrive as zeros and a tile past the wave's last
+  // (range 0) reads nothing.  K, V and the scale rows share it.
+  constexpr int GK = Q8 ? 16 : 8, NG = TK / GK;
+  struct TileAddr {
+    int64_t off[NG];
+    uint32_t nb[NG];
   };
-  // Tokens of a tile's four 8-key groups (the same for K and V).
-  struct TileToks {
-    int64_t tok[4];
+  // Pool byte offset of key `key`'s row (wave-uniform): page from the split's
+  // registers (two readlanes), place in the page.
+  auto page_off = [&](int key) __attribute__((always_inline)) -> int64_t {
+    const int idx = (key >> a.log2_ps) - p0;
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)pr0, idx & 63);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)pr1, idx & 63);
+    const uint32_t page = idx >= 64 ? hi : lo;
+    return ((((int64_t)page) << a.log2_ps) + (key & ps_mask)) * hkvd;
   };
-  auto tile_toks = [&](int t0) __attribute__((always_inline)) -> TileToks {
-    TileToks tt;
+  auto tile_addr = [&](int t0, bool valid) __attribute__((always_inline)) -> TileAddr {
+    TileAddr ta;
+    const int last = ctx_last - t0;   // tile-relative last key of the context
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) tt.tok[rg] = (PAGED || rg == 0) ? key_tok(t0 + 8 * rg) : tt.tok[0] + 8 * rg;
-    return tt;
+    for (int gi = 0; gi < NG; ++gi) {
+      const int n = valid ? min(max(last - GK * gi + 1, 0), GK) : 0;
+      ta.nb[gi] = (uint32_t)(n * hkvd);
+      if constexpr (!PAGED) {
+        ta.off[gi] = (int64_t)(t0 + GK * gi) * hkvd;
+      } else if (gi == 0) {
+        ta.off[0] = page_off(t0);
+      } else {
+        // tiles start at multiples of 32 keys: a group starts a page when its
+        // tile-relative first key is a multiple of the page size
+        ta.off[gi] = ((GK * gi) & ps_mask) ? ta.off[gi - 1] + (int64_t)GK * hkvd : page_off(t0 + GK * gi);
+      }
+    }
+    return ta;
   };
 
   // ---- loads ----------------------------------------------------------------
@@ -239,67 +270,53 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(AttnArgs a) {
   // 8 cg + ((L % 8) ^ lds_g(row % 16)); rg's parity picks the offset set.
   const uint32_t v16_even = lrow * hkvd + (((lane & 7) ^ lds_g(lrow)) << 4);
   const uint32_t v16_odd = lrow * hkvd + (((lane & 7) ^ lds_g(8 + lrow)) << 4);
-  // 8-bit: load i covers rows RPL i .. + RPL - 1; lane L: row RPL i + L / U,
-  // LDS unit w = L % U.
+  // 8-bit: load i covers rows RPL i .. + RPL - 1 (one 16-key group); lane L:
+  // row RPL i + L / U, LDS unit w = L % U.
   constexpr int U = Gm::U, RPL = Gm::RPL;
   const int qr = lane / U, qw = lane % U;
-  const int ctx_last = kend - 1;
-  // Issue the loads of K (is_v false) or V of this wave's tile starting at key
-  // t0 into dst (the wave's part of a slot array); `to` holds the tile's group
-  // offsets (tile_offs).  A tile that is not `valid` (past the wave's last)
-  // issues the same loads, reading nothing.
-  // Q8: after the quants, two loads of scale rows (one per 16-key block, one
-  // page) land behind them: block b at KT + 256 b, row r (LDS row 16 b + r;
-  // K row 16 b + r holds key 16 b + swap23(r)) at r SROW.
+  // Issue the loads of K (is_v false) or V of the tile `ta` describes into
+  // the wave's part of slot array arr.
+  // Q8: after the quants, two loads of scale rows (one per 16-key group)
+  // land behind them: group b at KT + 256 b, row r (LDS row 16 b + r; K row
+  // 16 b + r holds key 16 b + swap23(r)) at r SROW.
   const int s_dw = lane % (SROW / 4 > 0 ? SROW / 4 : 1);               // dword of the row
-  const int s_r = min(lane / (SROW / 4 > 0 ? SROW / 4 : 1), 15);       // row within the block
+  const int s_r = min(lane / (SROW / 4 > 0 ? SROW / 4 : 1), 15);       // row within the group
   const char* ksg = (const char*)a.k_scale + g * SROW;
   const char* vsg = (const char*)a.v_scale + g * SROW;
-  const int srow_bytes = a.n_kv_heads * SROW;   // scale bytes per token (all KV heads)
-  auto issue = [&](int t0, const TileToks& to, bool is_v, uint8_t* dst, bool valid) __attribute__((always_inline)) {
+  const int srow_bytes = a.n_kv_heads * SROW;   // scale bytes per token (all KV heads): hkvd / 16
+  auto issue = [&](const TileAddr& ta, bool is_v, uint8_t* arr) __attribute__((always_inline)) {
+    // The wave's offset goes through an empty asm statement so that each
+    // load's LDS address is formed where the load is issued: hoisted out of
+    // the loop, the (slot, load) addresses would hold dozens of scalar
+    // registers for the whole loop.
+    int wofs = wave * WS;
+    asm volatile("" : "+s"(wofs));
+    uint8_t* dst = arr + wofs;
     const char* src = is_v ? vg : kg;
-    const int last = ctx_last - t0;           // last valid tile-relative key (< 31: the context's last tile)
-    const bool whole = last >= TK - 1;
     if constexpr (!Q8) {
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        // rows past the end read the last valid row (same 8-row group, same page)
-        const int r0 = whole ? 8 * rg : __builtin_amdgcn_readfirstlane(min(8 * rg, last & ~7));
-        const char* base = src + (whole ? to.tok[rg] : key_tok(t0 + r0)) * hkvd;
-        uint32_t voff = (rg & 1) ? v16_odd : v16_even;
-        if (!whole) {
-          const int lr = min(lrow, last - r0);
-          voff = lr * hkvd + (((lane & 7) ^ lds_g(((8 * rg) & 15) + lrow)) << 4);
-        }
+        const uint32_t voff = (rg & 1) ? v16_odd : v16_even;
 #pragma unroll
         for (int cg = 0; cg < D / 64; ++cg)
-          dec_load_lds16(base + 128 * cg, voff, valid, dst + (cg * 4 + rg) * 1024);
+          dec_load_lds16(src + ta.off[rg], voff + 128 * cg, ta.nb[rg], dst + (cg * 4 + rg) * 1024);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < LKQ; ++i) {
-        const int m = RPL * i + qr;
-        const int kofs = is_v ? m : swap23(m);               // this lane's key, tile-relative
-        const int kb = is_v ? RPL * i : swap23(RPL * i);       // the load's first key
+        const int m = RPL * i + qr;                            // this lane's LDS row
+        const int key = is_v ? m : swap23(m);                  // its key, tile-relative
+        const int grp = (RPL * i) >> 4;                        // the load's 16-key group
         const int c16 = is_v ? (qw ^ (2 * dec_fv<D>(m))) : (qw ^ dec_sk<D>(m));
-        // the load's rows lie in one 16-key block (one page: pages hold >= 16 keys)
-        const int kbase = whole ? kb : __builtin_amdgcn_readfirstlane(min(kb, last) & ~15);
-        const int key = whole ? kofs : min(kofs, last);
-        // kb is 4-aligned and its 8-key group starts at kb & ~7
-        const char* base = src + (whole ? to.tok[kb >> 3] + (kb & 7) : key_tok(t0 + kbase)) * hkvd;
-        dec_load_lds16(base, (uint32_t)((key - kbase) * hkvd + 16 * c16), valid, dst + i * 1024);
+        dec_load_lds16(src + ta.off[grp], (uint32_t)((key - 16 * grp) * hkvd + 16 * c16), ta.nb[grp],
+                       dst + i * 1024);
       }
       const char* ssrc = is_v ? vsg : ksg;
+      const int kofs = is_v ? s_r : swap23(s_r);
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int kofs = 16 * b + (is_v ? s_r : swap23(s_r));
-        const int kbase = whole ? 16 * b : __builtin_amdgcn_readfirstlane(min(16 * b, last) & ~15);
-        const int key = whole ? kofs : min(kofs, last);
-        // the block's first token (the tile's 8-key group 2 b)
-        const int64_t tok0 = whole ? to.tok[2 * b] : key_tok(t0 + kbase);
-        const char* base = ssrc + tok0 * srow_bytes;
-        dec_load_lds4(base, (uint32_t)((key - kbase) * srow_bytes + 4 * s_dw), valid, dst + KT + 256 * b);
-      }
+      for (int b = 0; b < 2; ++b)
+        dec_load_lds4(ssrc + (ta.off[b] >> 4), (uint32_t)(kofs * srow_bytes + 4 * s_dw), ta.nb[b] >> 4,
+                      dst + KT + 256 * b);
     }
   };
 
@@ -413,8 +430,9 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(AttnArgs a) {
       }
     }
     // This slot's K has been read: its next tile's K group goes out.
-    const TileToks ton = tile_toks(t0n);
-    issue(t0n, ton, false, kt, refill);
+    const TileAddr tan = tile_addr(t0n, refill);
+    lds_reads_done();
+    issue(tan, false, kslot(slot));
 
     // Element e of sc is S^T row 8 (e / 4) + 4 h + e % 4 (Q8: key swap23 of it).
     auto key_of = [&](int e) __attribute__((always_inline)) {
@@ -552,7 +570,8 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(AttnArgs a) {
       }
     }
     // This slot's V has been read: its next tile's V group goes out.
-    issue(t0n, ton, true, vt, refill);
+    lds_reads_done();
+    issue(tan, true, vslot(slot));
   };
 
   // ---- tile loop ------------------------------------------------------------
@@ -560,9 +579,9 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(AttnArgs a) {
   auto prologue = [&](auto slot) __attribute__((always_inline)) {
     constexpr int SL = decltype(slot)::value;
     const int t0 = k0 + TK * (wave + kDecWaves * SL);
-    const TileToks to = tile_toks(t0);
-    issue(t0, to, false, kslot(slot) + wave * WS, SL < nt);
-    issue(t0, to, true, vslot(slot) + wave * WS, SL < nt);
+    const TileAddr ta = tile_addr(t0, SL < nt);
+    issue(ta, false, kslot(slot));
+    issue(ta, true, vslot(slot));
   };
   prologue(std::integral_constant<int, 0>{});
   if constexpr (NS > 1) prologue(std::integral_constant<int, 1>{});

@@ -43,6 +43,19 @@ def _id(c):
            f"-{c['table']}" + (f"-p{c['piece']}" if c["piece"] else "")
 
 
+def _same_plans(c):
+    """Paged and contiguous calls run the same launches (so agree bit for bit)
+    when every call (each piece, or the whole chunk) gets the same plan: the
+    contiguous entry plans as for pages of 16 tokens."""
+    step = c["piece"] or c["rows"]
+    for r0 in range(0, c["rows"], step):
+        r = min(step, c["rows"] - r0)
+        args = (c["history"] + r0, r, c["hq"], c["hkv"], c["d"])
+        if pkg.paged_prefill_plan(*args, c["ps"], c["n_splits"]) != pkg.paged_prefill_plan(*args, 16, c["n_splits"]):
+            return False
+    return True
+
+
 @pytest.mark.parametrize("c", CASES, ids=[_id(c) for c in CASES])
 def test_random_shape_matches_oracle(c):
     import torch
@@ -58,7 +71,7 @@ def test_random_shape_matches_oracle(c):
     out_c = pkg.contiguous_prefill_attention(d["q"], d["k"], d["v"], c["history"], n_splits=c["n_splits"],
                                              piece_rows=c["piece"])
     torch.cuda.synchronize()
-    if c["ps"] <= 64:
+    if _same_plans(c):
         assert _gpu.bits_equal(out, out_c), "paged and contiguous differ bitwise"
     got = _gpu.host_out(out)
     ref = _gpu.oracle_out(case)
