@@ -12,21 +12,23 @@
 // axis cut into splits whose partials (output normalised by its own softmax
 // sum, plus its log-sum-exp) are merged by the merge kernel.
 //
-// Workgroup = one (split, KV head), 4 waves.  Each wave owns every fourth
-// 32-key tile of the split and streams it on its own: K and V tiles land in
-// the wave's part of NS LDS slots by direct-to-LDS loads, NS tiles ahead of
-// the tile being computed (the loads of tile t + NS are issued as soon as
-// tile t has been read), so a CU keeps up to 4 NS tiles in flight with no
-// barrier in the loop.  All 32 query vectors of the KV head (one per lane
-// and lane + 32) stay in registers as the MFMA B operand; each wave keeps its
-// own softmax reference, sum and output accumulators, and at the end the four
-// waves' results are combined in LDS (references are integers, so the
-// combination scales by exact powers of two) into one partial per workgroup.
+// Workgroup = one (split, KV head), W waves (8 at head dimension up to 128,
+// two per SIMD; 4 at 256).  Each wave owns every W-th 32-key tile of the
+// split and streams it on its own: K and V tiles land in the wave's part of
+// NS LDS slots by direct-to-LDS loads, NS tiles ahead of the tile being
+// computed (the loads of tile t + NS are issued as soon as tile t has been
+// read), so a CU keeps up to W NS tiles in flight with no barrier in the
+// loop.  All 32 query vectors of the KV head (one per lane and lane + 32)
+// stay in registers as the MFMA B operand; each wave keeps its own softmax
+// reference, sum and output accumulators, and at the end the waves' results
+// are combined in LDS (references are integers, so the combination scales by
+// exact powers of two) into one partial per workgroup.
 //
 // 8-bit pages (Q8) are widened in registers at operand read time: a K read
 // of 16 quants becomes the A operands of two MFMA steps (quant x scale,
-// rounded once to fp16), and V^T comes from ds_read_b64_tr_b8, which hands
-// each lane one column of 8 rows (8 keys) of bytes, scaled per key.
+// rounded once to fp16), and V^T comes from ds_read_b64_tr_b16 over byte
+// pairs, which hands each lane two columns of 8 rows (8 keys) of bytes,
+// scaled per key.
 #pragma once
 
 #include "attn_kernel.h"
@@ -34,20 +36,25 @@
 namespace ppa {
 namespace {
 
-constexpr int kDecWaves = 4;
-constexpr int kDecPages = 128;   // block-table entries per split held in registers (two per lane)
+constexpr int kDecPages = 128;     // block-table entries per split held in registers (two per lane)
+constexpr int kDecLds = 144 * 1024;  // LDS of the K/V slots of a workgroup
+constexpr int kDecReaders = 4;     // waves that combine the workgroup's partial at the end
 
 // Exchange bits 2 and 3 (8-bit K tiles store key swap23(m) in row m; see below).
 __device__ __forceinline__ constexpr int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
 template <int D, bool Q8>
 struct DecGeom {
+  // Waves per workgroup: two per SIMD where a wave needs at most 256
+  // registers (head dimension up to 128), so that one wave's loads, waits
+  // and widening overlap the other's MFMAs; one per SIMD at 256.
+  static constexpr int W = D <= 128 ? 8 : 4;
   static constexpr int TK = 32;                          // keys per tile
   static constexpr int KT = Q8 ? TK * D : TK * D * 2;    // bytes of one K (or V) tile
-  static constexpr int NS_FIT = (32 * 1024) / (2 * KT);  // slots in 32 KB per wave
-  static constexpr int NS = NS_FIT < 1 ? 1 : NS_FIT > 4 ? 4 : NS_FIT;
   static constexpr int SCB = Q8 ? 512 : 0;              // Q8: scale rows of one K (or V) tile, 2 x 256 B
   static constexpr int WS = KT + SCB;                    // one wave's part of a slot array
+  static constexpr int NS_FIT = kDecLds / (W * 2 * WS);  // slots (K and V tiles of every wave) in kDecLds
+  static constexpr int NS = NS_FIT < 1 ? 1 : NS_FIT > 4 ? 4 : NS_FIT;
   static constexpr int LKQ = KT / 1024;                  // 1 KB direct-to-LDS loads per K (or V) tile
   static constexpr int LK = LKQ + (Q8 ? 2 : 0);          // loads of a K (or V) group (Q8: + two of scales)
   static constexpr int LV = LK;
@@ -120,30 +127,30 @@ __device__ __forceinline__ constexpr int dec_fv(int key) {
 }
 
 template <int D, class E, bool PAGED, bool Q8>
-__global__ __launch_bounds__(256, 1) void attn_decode_kernel(AttnArgs a) {
+__global__ __launch_bounds__((64 * DecGeom<D, Q8>::W), 1) void attn_decode_kernel(AttnArgs a) {
   using Gm = DecGeom<D, Q8>;
+  constexpr int W = Gm::W;
   using M = std::conditional_t<Q8, F16, E>;   // MFMA operand type
   using vec8 = typename M::vec8;
   constexpr int TK = Gm::TK, KT = Gm::KT, WS = Gm::WS, NS = Gm::NS, LK = Gm::LK, LV = Gm::LV, LKQ = Gm::LKQ;
   constexpr int KS = D / 16, DB = D / 32;
   constexpr int EB = Q8 ? 1 : 2;
-  static_assert(2 * NS * KT >= 128 * D, "the output staging fits the wave's slots");
   constexpr int SROW = D / 16;   // Q8: bytes of one key's scale row
   static_assert(LV + (NS - 1) * (LK + LV) < 64 && (NS - 1) * (LK + LV) + LK < 64, "vmcnt range");
   // One array per slot and K/V, so the compiler can tell a read of one slot
   // from a direct-to-LDS load into another (it waits for a load only before
   // reads of the same array).  Unused slots are 16 bytes.
-  __shared__ __attribute__((aligned(1024))) uint8_t ks0[kDecWaves * WS];
-  __shared__ __attribute__((aligned(1024))) uint8_t vs0[kDecWaves * WS];
-  __shared__ __attribute__((aligned(1024))) uint8_t ks1[NS > 1 ? kDecWaves * WS : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t vs1[NS > 1 ? kDecWaves * WS : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t ks2[NS > 2 ? kDecWaves * WS : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t vs2[NS > 2 ? kDecWaves * WS : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t ks3[NS > 3 ? kDecWaves * WS : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t vs3[NS > 3 ? kDecWaves * WS : 16];
-  __shared__ float ml_m[kDecWaves][32], ml_l[kDecWaves][32];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks0[W * WS];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs0[W * WS];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks1[NS > 1 ? W * WS : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs1[NS > 1 ? W * WS : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks2[NS > 2 ? W * WS : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs2[NS > 2 ? W * WS : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks3[NS > 3 ? W * WS : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs3[NS > 3 ? W * WS : 16];
+  __shared__ float ml_m[W][32], ml_l[W][32];
   // Q8: V scales of the wave's current tile, [block][key]
-  __shared__ __attribute__((aligned(16))) uint16_t vst[Q8 ? kDecWaves * DB * 32 : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t vst[Q8 ? W * DB * 32 : 8];
 
   auto kslot = [&](auto s) __attribute__((always_inline)) -> uint8_t* {
     constexpr int S = decltype(s)::value;
@@ -179,7 +186,7 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(AttnArgs a) {
   const int k0 = s * a.split_tokens;
   const int kend = min(k0 + a.split_tokens, a.ctx);
   const int n_tiles = kend > k0 ? (kend - k0 + TK - 1) / TK : 0;
-  const int nt = n_tiles > wave ? (n_tiles - wave + kDecWaves - 1) / kDecWaves : 0;  // tiles wave + 4 t
+  const int nt = n_tiles > wave ? (n_tiles - wave + W - 1) / W : 0;  // tiles wave + W t
   // Tiles whose keys all lie at or below the first row's last key need no mask.
   const int mask_from = (int)a.history - k0;   // tile-relative first key past row 0's limit, at tile j: - 32 j
 
@@ -353,10 +360,10 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(AttnArgs a) {
     constexpr int SL = decltype(slot)::value;
     uint8_t* kt = kslot(slot) + wave * WS;
     uint8_t* vt = vslot(slot) + wave * WS;
-    const int j = wave + kDecWaves * tw;
+    const int j = wave + W * tw;
     const int t0 = k0 + TK * j;
     const bool refill = tw + NS < nt;   // the slot's next tile is one of the wave's
-    const int t0n = t0 + TK * kDecWaves * NS;
+    const int t0n = t0 + TK * W * NS;
 
     // K(tw) (and its scale rows) has arrived when at most V(tw) and the K/V
     // groups of the NS - 1 later slots are outstanding.
@@ -578,7 +585,7 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(AttnArgs a) {
   // Prologue: the first NS tiles' K and V groups, in tile order.
   auto prologue = [&](auto slot) __attribute__((always_inline)) {
     constexpr int SL = decltype(slot)::value;
-    const int t0 = k0 + TK * (wave + kDecWaves * SL);
+    const int t0 = k0 + TK * (wave + W * SL);
     const TileAddr ta = tile_addr(t0, SL < nt);
     issue(ta, false, kslot(slot));
     issue(ta, true, vslot(slot));
@@ -611,7 +618,7 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(AttnArgs a) {
     }
   }
 
-  // ---- combine the four waves ---------------------------------------------
+  // ---- combine the waves -----------------------------------------------------
   // Each wave leaves its reference, sum and unnormalised accumulators; its own
   // slots (all loads consumed) hold the accumulators as 1 KB blocks
   // bj = 4 db + jq of [h][qv][4 floats], d = 32 db + 8 jq + 4 h + 0..3.
@@ -621,14 +628,15 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(AttnArgs a) {
     ml_m[wave][qv] = m_ref;
     ml_l[wave][qv] = l_tot;
   }
-  // Blocks of one slot array; with a multiple of 4 the blocks the four waves
-  // of a reading thread group touch in one step lie in one array, known at
-  // compile time (a pointer chosen among the arrays at run time would keep
-  // the compiler from telling the arrays apart in the tile loop).  Otherwise
-  // (8-bit pages at head dimension 64) a separate array holds the staging.
+  // Staging blocks per slot array part (a wave's part of one array).  With a
+  // multiple of 4 the blocks the reading waves touch in one step lie in one
+  // array, known at compile time; with 2 (8-bit pages at head dimension 64)
+  // a step's blocks lie in two arrays and the reader picks one.  (This is
+  // after the tile loop: a pointer chosen among the arrays at run time inside
+  // it would keep the compiler from telling the arrays apart there.)
   constexpr int BPA = KT / 1024;
-  constexpr bool OWN_STAGE = BPA % 4 != 0;
-  __shared__ __attribute__((aligned(1024))) uint8_t ostage[OWN_STAGE ? kDecWaves * 128 * D : 16];
+  static_assert(BPA % 4 == 0 || BPA == 2, "staging blocks per array");
+  static_assert(2 * NS * BPA >= 4 * DB, "the output staging fits the wave's slots");
   auto arr_of = [&](auto ai) __attribute__((always_inline)) -> uint8_t* {
     constexpr int A = decltype(ai)::value;
     if constexpr (A == 0) return ks0;
@@ -643,8 +651,7 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(AttnArgs a) {
   // block bj (compile time) of wave w
   auto stage = [&](auto bjc, int w) __attribute__((always_inline)) -> float* {
     constexpr int BJ = decltype(bjc)::value;
-    if constexpr (OWN_STAGE) return (float*)(ostage + (w * 4 * DB + BJ) * 1024);
-    else return (float*)(arr_of(std::integral_constant<int, BJ / BPA>{}) + w * WS + (BJ % BPA) * 1024);
+    return (float*)(arr_of(std::integral_constant<int, BJ / BPA>{}) + w * WS + (BJ % BPA) * 1024);
   };
   if constexpr (!Q8) {
     dec_static_for<0, 4 * DB>([&](auto bjc) __attribute__((always_inline)) {
@@ -668,20 +675,23 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  // 256 threads over the 32 x D/4 four-float units: step i takes blocks
-  // bj = 4 i + (thread / 64), unit (h, qv) = thread % 64 of the block.
+  // The first kDecReaders waves over the 32 x D/4 four-float units: step i
+  // takes blocks bj = 4 i + (thread / 64), unit (h, qv) = thread % 64 of the
+  // block, and sums it over the W waves.
+  const int wq = tid >> 6;
+  if (wq >= kDecReaders) return;
   const int64_t pairs = (int64_t)a.rows * a.n_q_heads;
-  const int uq = tid & 31, uh = (tid >> 5) & 1, wq = tid >> 6;
-  float mw[kDecWaves], lw[kDecWaves], mx = kNegInf;
+  const int uq = tid & 31, uh = (tid >> 5) & 1;
+  float mw[W], lw[W], mx = kNegInf;
 #pragma unroll
-  for (int w = 0; w < kDecWaves; ++w) {
+  for (int w = 0; w < W; ++w) {
     mw[w] = ml_m[w][uq];
     lw[w] = ml_l[w][uq];
     mx = fmaxf(mx, mw[w]);
   }
-  float sw[kDecWaves], lsum = 0.f;
+  float sw[W], lsum = 0.f;
 #pragma unroll
-  for (int w = 0; w < kDecWaves; ++w) {
+  for (int w = 0; w < W; ++w) {
     // a wave that saw no key of this query vector adds nothing
     sw[w] = (mw[w] == kNegInf || !(lw[w] > 0.f)) ? 0.f : __builtin_amdgcn_exp2f(mw[w] - mx);   // exact: integers
     lsum += sw[w] * lw[w];
@@ -693,19 +703,15 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(AttnArgs a) {
   dec_static_for<0, DB>([&](auto ic) __attribute__((always_inline)) {
     constexpr int I = decltype(ic)::value;   // blocks 4 I .. 4 I + 3: one per reading wave
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float* src[kDecWaves];
-    if constexpr (OWN_STAGE) {
-#pragma unroll
-      for (int w = 0; w < kDecWaves; ++w) src[w] = (float*)(ostage + (w * 4 * DB + 4 * I + wq) * 1024);
+    uint8_t* base;
+    if constexpr (BPA % 4 == 0) {
+      base = arr_of(std::integral_constant<int, (4 * I) / BPA>{}) + ((4 * I) % BPA + wq) * 1024;
     } else {
-      constexpr int A = (4 * I) / BPA;         // the four blocks' array (BPA is a multiple of 4)
-      constexpr int B0 = (4 * I) % BPA;
-#pragma unroll
-      for (int w = 0; w < kDecWaves; ++w)
-        src[w] = (float*)(arr_of(std::integral_constant<int, A>{}) + w * WS + (B0 + wq) * 1024);
+      base = (wq < 2 ? arr_of(std::integral_constant<int, 2 * I>{}) : arr_of(std::integral_constant<int, 2 * I + 1>{})) +
+             (wq & 1) * 1024;
     }
 #pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) acc += sw[w] * *(const f32x4*)(src[w] + (uh * 32 + uq) * 4);
+    for (int w = 0; w < W; ++w) acc += sw[w] * *(const f32x4*)(base + w * WS + (uh * 32 + uq) * 16);
     if (!uvalid) return;
     const int bj = 4 * I + wq;
     const int d = 32 * (bj >> 2) + 8 * (bj & 3) + 4 * uh;
@@ -724,7 +730,7 @@ __global__ __launch_bounds__(256, 1) void attn_decode_kernel(AttnArgs a) {
 
 template <int D, class E, bool PAGED, bool Q8>
 hipError_t launch_decode_t(const AttnArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_decode_kernel<D, E, PAGED, Q8>), dim3(grid), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((attn_decode_kernel<D, E, PAGED, Q8>), dim3(grid), dim3(64 * DecGeom<D, Q8>::W), 0, stream, a);
   return hipGetLastError();
 }
 
