@@ -43,6 +43,7 @@ KERNEL_SOURCES = (
     ("attention_q8_d256.hip", os.environ.get("PPA_MFMA_VGPR_FORM_Q8", "0")),
     # the narrow (decode) kernel
     ("decode.hip", os.environ.get("PPA_MFMA_VGPR_FORM_DEC", "1")),
+    ("decode16.hip", os.environ.get("PPA_MFMA_VGPR_FORM_DEC", "1")),
     ("kv_append.hip", "0"),
     ("noalloc.hip", "0"),
 )

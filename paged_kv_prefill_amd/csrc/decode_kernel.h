@@ -43,16 +43,17 @@ constexpr int kDecReaders = 4;     // waves that combine the workgroup's partial
 // Exchange bits 2 and 3 (8-bit K tiles store key swap23(m) in row m; see below).
 __device__ __forceinline__ constexpr int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
-template <int D, bool Q8>
+template <int D, bool Q8, int NQ>
 struct DecGeom {
-  // Waves per workgroup: two per SIMD where a wave needs at most 256
-  // registers (head dimension up to 128), so that one wave's loads, waits
-  // and widening overlap the other's MFMAs; one per SIMD at 256.
-  static constexpr int W = D <= 128 ? 8 : 4;
   static constexpr int TK = 32;                          // keys per tile
   static constexpr int KT = Q8 ? TK * D : TK * D * 2;    // bytes of one K (or V) tile
   static constexpr int SCB = Q8 ? 512 : 0;              // Q8: scale rows of one K (or V) tile, 2 x 256 B
   static constexpr int WS = KT + SCB;                    // one wave's part of a slot array
+  // Waves per workgroup: two per SIMD where a wave needs at most 256
+  // registers (16 query vectors, or head dimension up to 128) and the LDS
+  // holds a slot for each, so that one wave's loads, waits and widening
+  // overlap the other's MFMAs; else one per SIMD.
+  static constexpr int W = (NQ == 16 || D <= 128) && 8 * 2 * WS <= kDecLds ? 8 : 4;
   static constexpr int NS_FIT = kDecLds / (W * 2 * WS);  // slots (K and V tiles of every wave) in kDecLds
   static constexpr int NS = NS_FIT < 1 ? 1 : NS_FIT > 4 ? 4 : NS_FIT;
   static constexpr int LKQ = KT / 1024;                  // 1 KB direct-to-LDS loads per K (or V) tile
@@ -78,6 +79,49 @@ __device__ __forceinline__ void lds_reads_done() {
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(0xC07F);
   __builtin_amdgcn_sched_barrier(0);
+}
+
+// Max and sum over lanes l, l ^ 16, l ^ 32 and l ^ 48 (one column of the
+// 16 x 16 MFMA layouts), every lane getting the same value: the sum adds in
+// the same order on all four.
+__device__ __forceinline__ float max4_lanes(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float sum4_lanes(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
+// Signed 8-bit quants to fp16 pairs (exact), one v_cvt_f16_i16 per quant with
+// the byte picked and sign-extended by SDWA: (q0, q1) and (q2, q3) of x (K:
+// consecutive d), or (q0, q2) and (q1, q3) (V: byte pairs (d, d + 1) of two
+// keys, split into the keys' d and d + 1).
+#define PPA_Q8_PAIR(B0, B1)                                                                         \
+  __device__ __forceinline__ uint32_t q8_f16_##B0##B1(uint32_t x) {                                \
+    uint32_t r;                                                                                    \
+    asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_" #B0 "\n\t" \
+        "v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_" #B1 \
+        : "=&v"(r)                                                                                 \
+        : "v"(x));                                                                                 \
+    return r;                                                                                      \
+  }
+PPA_Q8_PAIR(0, 1)
+PPA_Q8_PAIR(2, 3)
+PPA_Q8_PAIR(0, 2)
+PPA_Q8_PAIR(1, 3)
+#undef PPA_Q8_PAIR
+__device__ __forceinline__ void q8_f16_01_23(uint32_t x, uint32_t& lo, uint32_t& hi) {
+  lo = q8_f16_01(x);
+  hi = q8_f16_23(x);
+}
+__device__ __forceinline__ void q8_f16_02_13(uint32_t x, uint32_t& ev, uint32_t& od) {
+  ev = q8_f16_02(x);
+  od = q8_f16_13(x);
 }
 
 template <int I, int N, class F>
@@ -126,9 +170,10 @@ __device__ __forceinline__ constexpr int dec_fv(int key) {
   return D == 256 ? 2 * (key & 3) : D == 128 ? 2 * ((key >> 1) & 1) : 0;
 }
 
-template <int D, class E, bool PAGED, bool Q8>
-__global__ __launch_bounds__((64 * DecGeom<D, Q8>::W), 1) void attn_decode_kernel(AttnArgs a) {
-  using Gm = DecGeom<D, Q8>;
+template <int D, class E, bool PAGED, bool Q8, int NQ>
+__global__ __launch_bounds__((64 * DecGeom<D, Q8, NQ>::W), 1) void attn_decode_kernel(AttnArgs a) {
+  static_assert(NQ == 16 || NQ == 32, "query vectors per wave");
+  using Gm = DecGeom<D, Q8, NQ>;
   constexpr int W = Gm::W;
   using M = std::conditional_t<Q8, F16, E>;   // MFMA operand type
   using vec8 = typename M::vec8;
@@ -174,10 +219,13 @@ __global__ __launch_bounds__((64 * DecGeom<D, Q8>::W), 1) void attn_decode_kerne
   const int g = blockIdx.x % a.n_kv_heads;
   const int s = blockIdx.x / a.n_kv_heads;
 
-  // Query vector f = lane % 32 = (row, head) pair of the head group, row-major.
+  // Query vector f = (row, head) pair of the head group, row-major: lane % 32
+  // (32 per wave), or lane % 16 (16 per wave; gq = lane / 16 then picks the
+  // lane's share of keys and dimensions in the 16 x 16 MFMA layouts).
   const int G = a.group;
   const int nqv = a.rows * G;
-  const int qv = lane & 31;
+  const int qv = lane & (NQ - 1);
+  const int gq = lane >> 4;
   const bool qv_valid = qv < nqv;
   const int row = qv_valid ? qv / G : a.rows - 1;
   const int head = g * G + (qv_valid ? qv % G : 0);
@@ -190,15 +238,19 @@ __global__ __launch_bounds__((64 * DecGeom<D, Q8>::W), 1) void attn_decode_kerne
   // Tiles whose keys all lie at or below the first row's last key need no mask.
   const int mask_from = (int)a.history - k0;   // tile-relative first key past row 0's limit, at tile j: - 32 j
 
-  // Q fragments (B operand of QK).  16-bit: step ks holds d = 16 ks + 8 h + 0..7.
-  // Q8: steps 2j and 2j + 1 hold d = 32 j + 16 h + 0..7 and + 8..15 (the d
-  // order of one 16-quant K read).
-  vec8 qf[KS];
+  // Q fragments (B operand of QK).  32 vectors (32 x 32 x 16 MFMA): 16-bit
+  // step ks holds d = 16 ks + 8 h + 0..7; Q8 steps 2j and 2j + 1 hold
+  // d = 32 j + 16 h + 0..7 and + 8..15 (the d order of one 16-quant K read).
+  // 16 vectors (16 x 16 x 32 MFMA): 16-bit step s holds d = 32 s + 8 gq + 0..7;
+  // Q8 steps 2j and 2j + 1 hold d = 64 j + 16 gq + 0..7 and + 8..15.
+  constexpr int QS = NQ == 16 ? D / 32 : KS;   // QK steps
+  vec8 qf[QS];
   {
     const uint16_t* qp = a.q + ((int64_t)row * a.n_q_heads + head) * D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int d0 = Q8 ? 32 * (ks >> 1) + 16 * h + 8 * (ks & 1) : 16 * ks + 8 * h;
+    for (int ks = 0; ks < QS; ++ks) {
+      const int d0 = NQ == 16 ? (Q8 ? 64 * (ks >> 1) + 16 * gq + 8 * (ks & 1) : 32 * ks + 8 * gq)
+                              : (Q8 ? 32 * (ks >> 1) + 16 * h + 8 * (ks & 1) : 16 * ks + 8 * h);
       const u32x4 raw = qv_valid ? *(const u32x4*)(qp + d0) : u32x4{0u, 0u, 0u, 0u};
       if constexpr (std::is_same_v<M, E>) {
         qf[ks] = __builtin_bit_cast(vec8, raw);
@@ -328,9 +380,13 @@ __global__ __launch_bounds__((64 * DecGeom<D, Q8>::W), 1) void attn_decode_kerne
   };
 
   // ---- state ----------------------------------------------------------------
-  f32x16 o[DB];
+  // Output accumulators: 32 vectors, O^T blocks of 32 d (32 x 32); 16
+  // vectors, blocks of 16 d (16 x 16).
+  constexpr int NO = NQ == 16 ? D / 16 : DB;
+  using OAcc = std::conditional_t<NQ == 16, f32x4, f32x16>;
+  OAcc o[NO];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  for (int db = 0; db < NO; ++db) o[db] = OAcc{};
   float m_ref = kNegInf, l = 0.f;
   const float c = a.scale_log2;
 
@@ -354,6 +410,24 @@ __global__ __launch_bounds__((64 * DecGeom<D, Q8>::W), 1) void attn_decode_kerne
     for (int p = 0; p < D / 64; ++p) tr_unit[p] = 32 * ((2 * p + gi) ^ fv);
   }
 
+  // 16 query vectors (16 x 16 x 32 MFMAs), lane (m = lane % 16, gq):
+  //  * 16-bit K: key 16 kb + m, d 32 s + 8 gq + 0..7 (chunk 4 s + gq) at
+  //    kofs16q ^ (s % 2) 64 + (s / 2) 4 KB + kb 2 KB;
+  //  * 16-bit V^T (ds_read_b64_tr_b16): lane 4 jv + cc of group gq names key
+  //    4 gq + jv (lo; hi: + 16) and d 16 db + 4 cc + 0..3, at
+  //    vofs16q ^ (db % 4) 32 + (db / 4) 4 KB (+ 2 KB);
+  //  * 8-bit K: the LDS row of key 16 kb + m is 16 kb + swap23(m); read j
+  //    (16 quants, d 64 j + 16 gq + 0..15) at kb 16 D + (krow16q ^ 64 j);
+  //  * 8-bit V: key 4 gq + jv (+ 16), bytes 8 cc of the 32-byte unit w (at
+  //    w ^ fV(key)), at trrow16q + 32 (w ^ fv16q) (+ 16 D).
+  const int m16 = lane & 15, jv = (lane & 15) >> 2, cc = lane & 3;
+  const int kofs16q = (m16 >> 3) * 1024 + (m16 & 7) * 128 + ((gq ^ lds_g(m16)) << 4);
+  const int vofs16q = (gq >> 1) * 1024 + (4 * (gq & 1) + jv) * 128 + (((cc >> 1) ^ lds_g(4 * gq + jv)) << 4) +
+                      8 * (cc & 1);
+  const int krow16q = swap23(m16) * D + 16 * (gq ^ dec_sk<D>(swap23(m16)));
+  const int trrow16q = (4 * gq + jv) * D + 8 * cc;
+  const int fv16q = dec_fv<D>(jv);
+
   // One tile: QK, mask, softmax, PV; loads of tile tw + NS go out as the
   // slot's K and V are read.  `first` = the wave's first tile.
   auto tile = [&](int tw, auto slot, bool first) __attribute__((always_inline)) {
@@ -369,6 +443,179 @@ __global__ __launch_bounds__((64 * DecGeom<D, Q8>::W), 1) void attn_decode_kerne
     // groups of the NS - 1 later slots are outstanding.
     dec_wait_vm<LV + (NS - 1) * (LK + LV)>();
 
+    if constexpr (NQ == 16) {
+    // S^T blocks kb = 0, 1 (keys 16 kb + 0..15): sc[kb][i] is key 16 kb + 4 gq + i.
+    f32x4 sc[2] = {f32x4{}, f32x4{}};
+    if constexpr (!Q8) {
+      constexpr int QPF = 4, NR = 2 * QS;
+      i16x8 kr[NR];
+      auto load = [&](int i) __attribute__((always_inline)) {   // i = 2 s + kb
+        const int st = i >> 1, kb = i & 1;
+        kr[i] = *LDS_PTR(const i16x8, kt + (kofs16q ^ ((st & 1) << 6)) + (st >> 1) * 4096 + kb * 2048);
+      };
+#pragma unroll
+      for (int i = 0; i < QPF && i < NR; ++i) load(i);
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        if (i + QPF < NR) load(i + QPF);
+        sc[i & 1] = M::mfma16(__builtin_bit_cast(vec8, kr[i]), qf[i >> 1], sc[i & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+      // the K scale rows of the lane's two keys
+      uint32_t ksr[2][SROW / 4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint8_t* kr_s = kt + KT + 256 * kb + swap23(m16) * SROW;
+        if constexpr (SROW == 16) {
+          const u32x4 v = *LDS_PTR(const u32x4, kr_s);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ksr[kb][e] = v[e];
+        } else if constexpr (SROW == 8) {
+          const u32x2 v = *LDS_PTR(const u32x2, kr_s);
+          ksr[kb][0] = v[0];
+          ksr[kb][1] = v[1];
+        } else {
+          ksr[kb][0] = *LDS_PTR(const uint32_t, kr_s);
+        }
+      }
+      constexpr int NR = 2 * (D / 64), QPF = NR < 3 ? NR : 3;
+      const uint32_t ksel = (gq >> 1) ? 0x03020302u : 0x01000100u;
+      u32x4 kr[NR];
+      auto load = [&](int i) __attribute__((always_inline)) {   // i = 2 j + kb
+        kr[i] = *LDS_PTR(const u32x4, kt + (i & 1) * 16 * D + (krow16q ^ (64 * (i >> 1))));
+      };
+#pragma unroll
+      for (int i = 0; i < QPF; ++i) load(i);
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        if (i + QPF < NR) load(i + QPF);
+        const int jr = i >> 1, kb = i & 1;
+        // the read's scale block is 2 jr + gq / 2: half gq / 2 of dword jr, both halves
+        const h2 ss = __builtin_bit_cast(h2, __builtin_amdgcn_perm(ksr[kb][jr], ksr[kb][jr], ksel));
+        uint32_t w[8];
+        uint32_t qh[8];   // the quants exactly in fp16 (all first: each conversion's result is read later)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) q8_f16_01_23(kr[i][k], qh[2 * k], qh[2 * k + 1]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) w[k] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, qh[k]) * ss);   // rounded once
+        const u32x4 a0 = {w[0], w[1], w[2], w[3]}, a1 = {w[4], w[5], w[6], w[7]};
+        sc[kb] = M::mfma16(__builtin_bit_cast(vec8, a0), qf[2 * jr], sc[kb]);
+        sc[kb] = M::mfma16(__builtin_bit_cast(vec8, a1), qf[2 * jr + 1], sc[kb]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // This slot's K has been read: its next tile's K group goes out.
+    const TileAddr tan = tile_addr(t0n, refill);
+    lds_reads_done();
+    issue(tan, false, kslot(slot));
+
+    if (TK * j + TK - 1 > mask_from) {
+      const int rel = lim - t0;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[kb][i] = 16 * kb + 4 * gq + i > rel ? kNegInf : sc[kb][i];
+    }
+    if (first) {
+      float mx = fmaxf(sc[0][0], sc[1][0]);
+#pragma unroll
+      for (int i = 1; i < 4; ++i) mx = fmaxf(mx, fmaxf(sc[0][i], sc[1][i]));
+      m_ref = ceilf(max4_lanes(mx) * c);
+    }
+    // P: PV K index i = keys 4 gq + i (i < 4) and 16 + 4 gq + i - 4: the lane's own scores.
+    vec8 pb;
+    float rs = 0.f;
+    auto weights = [&]() __attribute__((always_inline)) {
+      const float base = m_ref == kNegInf ? 0.f : m_ref;
+      float p32[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p32[i] = __builtin_amdgcn_exp2f(fmaf(sc[i >> 2][i & 3], c, -base));
+      pb = M::from_f32(p32);
+      rs = M::sum8(pb, 0.f);
+    };
+    weights();
+    if (__builtin_expect(__ballot(!(l + rs <= kSumLimit)) != 0, 0)) {
+      float mx = fmaxf(sc[0][0], sc[1][0]);
+#pragma unroll
+      for (int i = 1; i < 4; ++i) mx = fmaxf(mx, fmaxf(sc[0][i], sc[1][i]));
+      const float m_new = fmaxf(m_ref, ceilf(max4_lanes(mx) * c));
+      if (m_new != kNegInf && m_new != m_ref) {
+        const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < NO; ++db) o[db] *= alpha;
+        m_ref = m_new;
+      }
+      weights();
+    }
+    l += rs;
+
+    dec_wait_vm<(NS - 1) * (LK + LV) + LK>();
+    if constexpr (Q8) {
+      if (h == 0) {
+        const int key = lane & 31;
+        const uint8_t* vr = vt + KT + 256 * (key >> 4) + (key & 15) * SROW;
+        uint32_t w4[SROW / 4];
+        if constexpr (SROW == 16) {
+          const u32x4 v = *LDS_PTR(const u32x4, vr);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w4[e] = v[e];
+        } else if constexpr (SROW == 8) {
+          const u32x2 v = *LDS_PTR(const u32x2, vr);
+          w4[0] = v[0];
+          w4[1] = v[1];
+        } else {
+          w4[0] = *LDS_PTR(const uint32_t, vr);
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const uint32_t w2 = w4[db >> 1];
+          const uint16_t sc16 = (uint16_t)((db & 1) ? (w2 >> 16) : (w2 & 0xffffu));
+          vst[(wave * DB + db) * 32 + key] = sc16;
+        }
+      }
+    }
+    if constexpr (!Q8) {
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        const int ofs = (vofs16q ^ ((db & 3) << 5)) + (db >> 2) * 4096;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vt + ofs));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vt + ofs + 2048));
+        const vec8 av = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[db] = M::mfma16(av, pb, o[db]);
+      }
+    } else {
+      typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+      for (int w = 0; w < D / 32; ++w) {
+        const int ofs = trrow16q + 32 * (w ^ fv16q);
+        const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, vt + ofs)));
+        const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            LDS_PTR(i16x4, vt + ofs + 16 * D)));
+        // scales of keys 4 gq + 0..3 and 16 + 4 gq + 0..3 at block w
+        const u32x2 svl = *LDS_PTR(const u32x2, (uint8_t*)vst + ((wave * DB + w) * 32 + 4 * gq) * 2);
+        const u32x2 svh = *LDS_PTR(const u32x2, (uint8_t*)vst + ((wave * DB + w) * 32 + 16 + 4 * gq) * 2);
+        const uint32_t x[4] = {lo[0], lo[1], hi[0], hi[1]};
+        const uint32_t sk4[4] = {svl[0], svl[1], svh[0], svh[1]};
+        uint32_t we[4], wo[4], ev[4], od[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) q8_f16_02_13(x[k], ev[k], od[k]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t sk = sk4[k];
+          const h2 sc2 = __builtin_bit_cast(h2, sk);
+          we[k] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, ev[k]) * sc2);
+          wo[k] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, od[k]) * sc2);
+        }
+        o[2 * w] = M::mfma16(__builtin_bit_cast(vec8, u32x4{we[0], we[1], we[2], we[3]}), pb, o[2 * w]);
+        o[2 * w + 1] = M::mfma16(__builtin_bit_cast(vec8, u32x4{wo[0], wo[1], wo[2], wo[3]}), pb, o[2 * w + 1]);
+      }
+    }
+    lds_reads_done();
+    issue(tan, true, vslot(slot));
+    } else {
     f32x16 sc = f32x16{};
     if constexpr (!Q8) {
       constexpr int QPF = 4;
@@ -413,23 +660,18 @@ __global__ __launch_bounds__((64 * DecGeom<D, Q8>::W), 1) void attn_decode_kerne
       };
 #pragma unroll
       for (int jj = 0; jj < QPF; ++jj) load(jj);
-      const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
 #pragma unroll
       for (int jj = 0; jj < DB; ++jj) {
         if (jj + QPF < DB) load(jj + QPF);
-        const uint32_t sb = (jj & 1) ? (ksr[jj >> 1] >> 16) : (ksr[jj >> 1] & 0xffffu);
-        const h2 ss = __builtin_bit_cast(h2, sb | (sb << 16));
+        // scale jj: half jj % 2 of dword jj / 2, both halves
+        const h2 ss = __builtin_bit_cast(h2, __builtin_amdgcn_perm(ksr[jj >> 1], ksr[jj >> 1],
+                                                                   (jj & 1) ? 0x03020302u : 0x01000100u));
         uint32_t w[8];
+        uint32_t qh[8];   // the quants exactly in fp16 (all first: each conversion's result is read later)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          // byte u = quant ^ 0x80 under exponent byte 0x64 is the fp16 1024 + u:
-          // minus 1152 gives the quant exactly, times the scale rounds once
-          const uint32_t x = kr[jj][k] ^ 0x80808080u;
-          const h2 lo = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x, 0x04010400u));
-          const h2 hi = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u));
-          w[2 * k] = __builtin_bit_cast(uint32_t, (lo - bias) * ss);
-          w[2 * k + 1] = __builtin_bit_cast(uint32_t, (hi - bias) * ss);
-        }
+        for (int k = 0; k < 4; ++k) q8_f16_01_23(kr[jj][k], qh[2 * k], qh[2 * k + 1]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) w[k] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, qh[k]) * ss);   // rounded once
         const u32x4 a0 = {w[0], w[1], w[2], w[3]}, a1 = {w[4], w[5], w[6], w[7]};
         sc = M::mfma(__builtin_bit_cast(vec8, a0), qf[2 * jj], sc);
         sc = M::mfma(__builtin_bit_cast(vec8, a1), qf[2 * jj + 1], sc);
@@ -485,7 +727,7 @@ __global__ __launch_bounds__((64 * DecGeom<D, Q8>::W), 1) void attn_decode_kerne
         const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);   // 2^-k, 0 if m_ref was -inf
         l *= alpha;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        for (int db = 0; db < NO; ++db) o[db] *= alpha;
         m_ref = m_new;
       }
       weights();
@@ -544,7 +786,6 @@ __global__ __launch_bounds__((64 * DecGeom<D, Q8>::W), 1) void attn_decode_kerne
         // 64 p + 2 m), odd bytes that of o[2 p + 1] (d + 1), each widened with
         // the keys' scales of block d / 32.
         typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-        const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
         const int gi = (lane >> 4) & 1;
 #pragma unroll
         for (int p = 0; p < D / 64; ++p) {
@@ -557,19 +798,19 @@ __global__ __launch_bounds__((64 * DecGeom<D, Q8>::W), 1) void attn_decode_kerne
               LDS_PTR(i16x4, vt + (tr_row[kstep] + 4 * D + tr_unit[p]))));
           // scales of keys 16 kstep + 8 h + 0..7 at block 2 p + gi
           const u32x4 sv = *LDS_PTR(const u32x4, (uint8_t*)vst + ((wave * DB + u) * 32 + 16 * kstep + 8 * h) * 2);
-          const uint32_t x[4] = {lo[0] ^ 0x80808080u, lo[1] ^ 0x80808080u, hi[0] ^ 0x80808080u, hi[1] ^ 0x80808080u};
-          uint32_t we[4], wo[4];
+          const uint32_t x[4] = {lo[0], lo[1], hi[0], hi[1]};
+          // x[k] = bytes (d, d + 1) of keys 2k and 2k + 1
+          uint32_t we[4], wo[4], ev[4], od[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) q8_f16_02_13(x[k], ev[k], od[k]);
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            // x[k] = bytes (d, d + 1) of keys 2k and 2k + 1
-            const h2 ev = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x[k], 0x04020400u));
-            const h2 od = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x[k], 0x04030401u));
             // (the element goes through a plain variable: a bit cast of a
             // vector element as such reads element 0)
             const uint32_t sk = sv[k];
             const h2 sc2 = __builtin_bit_cast(h2, sk);
-            we[k] = __builtin_bit_cast(uint32_t, (ev - bias) * sc2);
-            wo[k] = __builtin_bit_cast(uint32_t, (od - bias) * sc2);
+            we[k] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, ev[k]) * sc2);
+            wo[k] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, od[k]) * sc2);
           }
           o[2 * p] = M::mfma(__builtin_bit_cast(vec8, u32x4{we[0], we[1], we[2], we[3]}), pb[kstep], o[2 * p]);
           o[2 * p + 1] = M::mfma(__builtin_bit_cast(vec8, u32x4{wo[0], wo[1], wo[2], wo[3]}), pb[kstep], o[2 * p + 1]);
@@ -579,6 +820,7 @@ __global__ __launch_bounds__((64 * DecGeom<D, Q8>::W), 1) void attn_decode_kerne
     // This slot's V has been read: its next tile's V group goes out.
     lds_reads_done();
     issue(tan, true, vslot(slot));
+    }
   };
 
   // ---- tile loop ------------------------------------------------------------
@@ -620,22 +862,16 @@ __global__ __launch_bounds__((64 * DecGeom<D, Q8>::W), 1) void attn_decode_kerne
 
   // ---- combine the waves -----------------------------------------------------
   // Each wave leaves its reference, sum and unnormalised accumulators; its own
-  // slots (all loads consumed) hold the accumulators as 1 KB blocks
+  // slots (all loads consumed) hold the accumulators as blocks of SB bytes,
   // bj = 4 db + jq of [h][qv][4 floats], d = 32 db + 8 jq + 4 h + 0..3.
   dec_wait_vm<0>();
-  const float l_tot = sum_with_partner(l);
-  if (h == 0) {
+  const float l_tot = NQ == 16 ? sum4_lanes(l) : sum_with_partner(l);
+  if (lane < NQ) {
     ml_m[wave][qv] = m_ref;
     ml_l[wave][qv] = l_tot;
   }
-  // Staging blocks per slot array part (a wave's part of one array).  With a
-  // multiple of 4 the blocks the reading waves touch in one step lie in one
-  // array, known at compile time; with 2 (8-bit pages at head dimension 64)
-  // a step's blocks lie in two arrays and the reader picks one.  (This is
-  // after the tile loop: a pointer chosen among the arrays at run time inside
-  // it would keep the compiler from telling the arrays apart there.)
-  constexpr int BPA = KT / 1024;
-  static_assert(BPA % 4 == 0 || BPA == 2, "staging blocks per array");
+  constexpr int SB = 32 * NQ;     // bytes of one staging block
+  constexpr int BPA = KT / SB;    // staging blocks per slot array part (a wave's part of one array)
   static_assert(2 * NS * BPA >= 4 * DB, "the output staging fits the wave's slots");
   auto arr_of = [&](auto ai) __attribute__((always_inline)) -> uint8_t* {
     constexpr int A = decltype(ai)::value;
@@ -648,19 +884,32 @@ __global__ __launch_bounds__((64 * DecGeom<D, Q8>::W), 1) void attn_decode_kerne
     else if constexpr (A == 6) return ks3;
     else return vs3;
   };
-  // block bj (compile time) of wave w
-  auto stage = [&](auto bjc, int w) __attribute__((always_inline)) -> float* {
-    constexpr int BJ = decltype(bjc)::value;
-    return (float*)(arr_of(std::integral_constant<int, BJ / BPA>{}) + w * WS + (BJ % BPA) * 1024);
+  // Array A0 + k for k < N known at run time (after the tile loop only: a
+  // pointer chosen among the arrays at run time inside it would keep the
+  // compiler from telling the arrays apart there).
+  auto arr_rt = [&](auto a0c, auto nc, int k) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int A0 = decltype(a0c)::value, N = decltype(nc)::value;
+    uint8_t* p = arr_of(std::integral_constant<int, A0>{});
+    if constexpr (N > 1) p = k == 1 ? arr_of(std::integral_constant<int, A0 + 1>{}) : p;
+    if constexpr (N > 2) p = k == 2 ? arr_of(std::integral_constant<int, A0 + 2>{}) : p;
+    if constexpr (N > 3) p = k == 3 ? arr_of(std::integral_constant<int, A0 + 3>{}) : p;
+    return p;
   };
-  if constexpr (!Q8) {
+  // blocks BJ0 + k (k < KN at run time, all in one array) of this wave: byte address
+  auto stage = [&](auto bjc, auto knc, int k) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int BJ0 = decltype(bjc)::value, KN = decltype(knc)::value;
+    static_assert(BJ0 / BPA == (BJ0 + KN - 1) / BPA, "the blocks lie in one array");
+    return arr_of(std::integral_constant<int, BJ0 / BPA>{}) + wave * WS + (BJ0 % BPA + k) * SB;
+  };
+  using I1 = std::integral_constant<int, 1>;
+  if constexpr (NQ == 32 && !Q8) {
     dec_static_for<0, 4 * DB>([&](auto bjc) __attribute__((always_inline)) {
       constexpr int BJ = decltype(bjc)::value;
       constexpr int DBI = BJ / 4, JQ = BJ % 4;
       const f32x4 v4 = {o[DBI][4 * JQ], o[DBI][4 * JQ + 1], o[DBI][4 * JQ + 2], o[DBI][4 * JQ + 3]};
-      *(f32x4*)(stage(bjc, wave) + (h * 32 + qv) * 4) = v4;
+      *(f32x4*)(stage(bjc, I1{}, 0) + (h * 32 + qv) * 16) = v4;
     });
-  } else {
+  } else if constexpr (NQ == 32) {
     // o[2 p + par] row m = 8 j + 4 h + i holds d = 64 p + 16 j + 8 h + 2 i + par:
     // four consecutive d = 64 p + 16 j + 8 h + 4 f + 0..3 (f = i / 2) go to
     // block 4 (2 p + j / 2) + 2 (j % 2) + h, half f.
@@ -670,18 +919,46 @@ __global__ __launch_bounds__((64 * DecGeom<D, Q8>::W), 1) void attn_decode_kerne
       constexpr int BJ0 = 4 * (2 * P + J / 2) + 2 * (J % 2);
       const f32x4 v4 = {o[2 * P][4 * J + 2 * F], o[2 * P + 1][4 * J + 2 * F], o[2 * P][4 * J + 2 * F + 1],
                         o[2 * P + 1][4 * J + 2 * F + 1]};
-      *(f32x4*)(stage(std::integral_constant<int, BJ0>{}, wave) + h * 256 + (F * 32 + qv) * 4) = v4;
+      *(f32x4*)(stage(std::integral_constant<int, BJ0>{}, std::integral_constant<int, 2>{}, h) + (F * 32 + qv) * 16) = v4;
+    });
+  } else if constexpr (!Q8) {
+    // o[db] element i holds d = 16 db + 4 gq + i: block 4 (db / 2) + 2 (db % 2) + gq / 2, h = gq % 2
+    dec_static_for<0, D / 16>([&](auto dbc) __attribute__((always_inline)) {
+      constexpr int DBI = decltype(dbc)::value;
+      constexpr int BJ0 = 4 * (DBI / 2) + 2 * (DBI % 2);
+      *(f32x4*)(stage(std::integral_constant<int, BJ0>{}, std::integral_constant<int, 2>{}, gq >> 1) +
+                ((gq & 1) * 16 + qv) * 16) = o[DBI];
+    });
+  } else {
+    // o[2 w + par] element i holds d = 32 w + 8 gq + 2 i + par: d = 32 w + 8 gq + 4 f + 0..3
+    // go to block 4 w + gq, h = f
+    dec_static_for<0, D / 16>([&](auto c) __attribute__((always_inline)) {   // (Wd, F)
+      constexpr int C = decltype(c)::value;
+      constexpr int Wd = C / 2, F = C % 2;
+      const f32x4 v4 = {o[2 * Wd][2 * F], o[2 * Wd + 1][2 * F], o[2 * Wd][2 * F + 1], o[2 * Wd + 1][2 * F + 1]};
+      uint8_t* dst;
+      if constexpr (BPA % 4 == 0) {
+        dst = stage(std::integral_constant<int, 4 * Wd>{}, std::integral_constant<int, 4>{}, gq);
+      } else {
+        static_assert(BPA == 2, "staging blocks per array");
+        dst = (gq < 2 ? stage(std::integral_constant<int, 4 * Wd>{}, std::integral_constant<int, 2>{}, gq)
+                      : stage(std::integral_constant<int, 4 * Wd + 2>{}, std::integral_constant<int, 2>{}, gq - 2));
+      }
+      *(f32x4*)(dst + (F * 16 + qv) * 16) = v4;
     });
   }
   __syncthreads();
 
-  // The first kDecReaders waves over the 32 x D/4 four-float units: step i
-  // takes blocks bj = 4 i + (thread / 64), unit (h, qv) = thread % 64 of the
+  // The first kDecReaders waves over the NQ x D/4 four-float units: step i
+  // takes BPS blocks bj = BPS i + t / (2 NQ), unit (h, qv) = t % (2 NQ) of the
   // block, and sums it over the W waves.
   const int wq = tid >> 6;
   if (wq >= kDecReaders) return;
+  constexpr int UB = 2 * NQ, BPS = 64 * kDecReaders / UB;
+  static_assert((4 * DB) % BPS == 0, "whole steps");
+  const int bis = tid / UB, unit = tid % UB;
+  const int uh = unit / NQ, uq = unit % NQ;
   const int64_t pairs = (int64_t)a.rows * a.n_q_heads;
-  const int uq = tid & 31, uh = (tid >> 5) & 1;
   float mw[W], lw[W], mx = kNegInf;
 #pragma unroll
   for (int w = 0; w < W; ++w) {
@@ -700,20 +977,22 @@ __global__ __launch_bounds__((64 * DecGeom<D, Q8>::W), 1) void attn_decode_kerne
   const int urow = uq / G, uhead = g * G + uq % G;
   const int64_t pair = (int64_t)urow * a.n_q_heads + uhead;
   const bool uvalid = uq < nqv;
-  dec_static_for<0, DB>([&](auto ic) __attribute__((always_inline)) {
-    constexpr int I = decltype(ic)::value;   // blocks 4 I .. 4 I + 3: one per reading wave
+  dec_static_for<0, 4 * DB / BPS>([&](auto ic) __attribute__((always_inline)) {
+    constexpr int I = decltype(ic)::value;
+    constexpr int B0 = BPS * I;   // the step's first block
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     uint8_t* base;
-    if constexpr (BPA % 4 == 0) {
-      base = arr_of(std::integral_constant<int, (4 * I) / BPA>{}) + ((4 * I) % BPA + wq) * 1024;
+    if constexpr (BPA % BPS == 0) {
+      base = arr_of(std::integral_constant<int, B0 / BPA>{}) + (B0 % BPA + bis) * SB;
     } else {
-      base = (wq < 2 ? arr_of(std::integral_constant<int, 2 * I>{}) : arr_of(std::integral_constant<int, 2 * I + 1>{})) +
-             (wq & 1) * 1024;
+      static_assert(BPS % BPA == 0 && BPS / BPA <= 4, "a step's blocks over whole arrays");
+      base = arr_rt(std::integral_constant<int, B0 / BPA>{}, std::integral_constant<int, BPS / BPA>{}, bis / BPA) +
+             (bis % BPA) * SB;
     }
 #pragma unroll
-    for (int w = 0; w < W; ++w) acc += sw[w] * *(const f32x4*)(base + w * WS + (uh * 32 + uq) * 16);
+    for (int w = 0; w < W; ++w) acc += sw[w] * *(const f32x4*)(base + w * WS + (uh * NQ + uq) * 16);
     if (!uvalid) return;
-    const int bj = 4 * I + wq;
+    const int bj = B0 + bis;
     const int d = 32 * (bj >> 2) + 8 * (bj & 3) + 4 * uh;
     if (a.n_splits == 1) {
       const uint32_t lo = E::bits(acc[0] * inv) | ((uint32_t)E::bits(acc[1] * inv) << 16);
@@ -724,15 +1003,43 @@ __global__ __launch_bounds__((64 * DecGeom<D, Q8>::W), 1) void attn_decode_kerne
           f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
     }
   });
-  if (a.n_splits > 1 && uvalid && wq == 0 && uh == 0)
+  if (a.n_splits > 1 && uvalid && bis == 0 && uh == 0)
     a.ws_lse[(int64_t)s * pairs + pair] = lsum > 0.f ? mx + log2f(lsum) : kNegInf;
 }
 
-template <int D, class E, bool PAGED, bool Q8>
+template <int D, class E, bool PAGED, bool Q8, int NQ>
 hipError_t launch_decode_t(const AttnArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_decode_kernel<D, E, PAGED, Q8>), dim3(grid), dim3(64 * DecGeom<D, Q8>::W), 0, stream, a);
+  hipLaunchKernelGGL((attn_decode_kernel<D, E, PAGED, Q8, NQ>), dim3(grid), dim3(64 * DecGeom<D, Q8, NQ>::W), 0, stream, a);
   return hipGetLastError();
 }
 
+template <class E, bool PAGED, bool Q8, int NQ>
+hipError_t launch_decode_d(const AttnArgs& a, int head_dim, int grid, hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_decode_t<64, E, PAGED, Q8, NQ>(a, grid, stream);
+    case 128: return launch_decode_t<128, E, PAGED, Q8, NQ>(a, grid, stream);
+    case 256: return launch_decode_t<256, E, PAGED, Q8, NQ>(a, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Every instantiation for NQ query vectors per wave.
+template <int NQ>
+hipError_t launch_decode_nq(const AttnArgs& a, int head_dim, int dtype, bool paged, bool q8, int grid,
+                            hipStream_t stream) {
+  auto by_e = [&](auto e) {
+    using E = decltype(e);
+    if (q8) return launch_decode_d<E, true, true, NQ>(a, head_dim, grid, stream);
+    if (paged) return launch_decode_d<E, true, false, NQ>(a, head_dim, grid, stream);
+    return launch_decode_d<E, false, false, NQ>(a, head_dim, grid, stream);
+  };
+  return dtype == 1 ? by_e(BF16{}) : by_e(F16{});
+}
+
 }  // namespace
+
+// 16 query vectors per wave (16 x 16 MFMAs), defined in decode16.hip.
+hipError_t launch_attention_decode16(const AttnArgs& a, int head_dim, int dtype, bool paged, bool q8, int grid,
+                                     hipStream_t stream);
+
 }  // namespace ppa
