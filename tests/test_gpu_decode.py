@@ -127,3 +127,33 @@ def test_narrow_q8_matches_oracle(name, history, rows, hq, hkv, d, ps, dtype, n_
         _gpu.assert_close(got, _oracle(case), name)
     else:
         _gpu.assert_close_bf16_bound(got, _oracle(case), _oracle_absw(case), name)
+
+
+# Every build of the narrow kernel: head dimension x element type x 16 or 32
+# query vectors per wave (rows x group at most 16 takes the 16 x 16 MFMAs),
+# 16-bit and 8-bit pages, a ragged context over several splits.
+BUILDS = [(d, dt, nq) for d in (64, 128, 256) for dt in ("f16", "bf16") for nq in (16, 32)]
+
+
+@pytest.mark.parametrize("d,dtype,nq", BUILDS, ids=[f"d{d}-{dt}-nq{nq}" for d, dt, nq in BUILDS])
+def test_narrow_every_build(d, dtype, nq):
+    import torch
+    from test_gpu_q8 import _dev_q8, _oracle, _oracle_absw, _run
+    rows, hq, hkv = (1, 16, 2) if nq == 16 else (2, 32, 2)   # 8 or 32 query vectors per KV head
+    history = 2345 + d
+    plan = pkg.paged_prefill_plan(history, rows, hq, hkv, d, 16, 0)
+    assert plan["m_tile"] == 32, plan
+    print(f"case narrow build d={d} {dtype} nq={nq}: S={plan['n_splits']}", flush=True)
+    case = synth.make_case("build", history, rows, hq, hkv, d, 16, dtype, seed=d + nq)
+    dev = _gpu.dev_case(case, contiguous=False)
+    out = pkg.paged_prefill_attention(dev["q"], dev["k_pages"], dev["v_pages"], dev["block_table"], history)
+    torch.cuda.synchronize()
+    _check(case, out, f"16-bit d={d} {dtype} nq={nq}")
+    qc = synth.make_q8_case("build_q8", history, rows, hq, hkv, d, 16, dtype, seed=d + nq + 1)
+    out8 = _run(_dev_q8(qc), qc)
+    torch.cuda.synchronize()
+    got = _gpu.host_out(out8)
+    if dtype == "f16":
+        _gpu.assert_close(got, _oracle(qc), f"q8 d={d} nq={nq}")
+    else:
+        _gpu.assert_close_bf16_bound(got, _oracle(qc), _oracle_absw(qc), f"q8 d={d} nq={nq}")
