@@ -283,7 +283,14 @@ int run_varlen(const void* q, const void* k, const void* v, const int32_t* bt, i
   a.v_scale = nullptr;
   a.query_blocks = plan.m_tile / 128;
 
-  if (launch_attention(a, d, dtype, true, plan.grid, stream) != hipSuccess) return PPA_ERR_HIP;
+  if (plan.m_tile == kNarrowVectors) {
+    // every sequence's rows x group fit one wave's MFMA columns: the narrow
+    // kernel (its build is chosen by the batch's largest row count)
+    a.rows = max_rows;
+    if (launch_attention_decode(a, d, dtype, true, false, plan.grid, stream) != hipSuccess) return PPA_ERR_HIP;
+  } else if (launch_attention(a, d, dtype, true, plan.grid, stream) != hipSuccess) {
+    return PPA_ERR_HIP;
+  }
   if (plan.n_splits > 1) {
     MergeArgs m;
     m.ws_o = a.ws_o;

@@ -217,7 +217,24 @@ __global__ __launch_bounds__((64 * DecGeom<D, Q8, NQ>::W), 1) void attn_decode_k
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5;
   const int g = blockIdx.x % a.n_kv_heads;
-  const int s = blockIdx.x / a.n_kv_heads;
+  const int s = (blockIdx.x / a.n_kv_heads) % a.n_splits;
+  // Several sequences (a batch of decode steps): the workgroup's sequence, its
+  // rows, history and block table.  A workgroup of a sequence without rows or
+  // past its last split exits (the merge reads no split that starts after a
+  // row's last key); the exit is uniform over the workgroup, before any barrier.
+  int ws_row0 = 0;
+  if (a.n_seqs > 0) {
+    const int seq = blockIdx.x / (a.n_kv_heads * a.n_splits);
+    const int r0 = a.cu_rows[seq];
+    a.rows = a.cu_rows[seq + 1] - r0;
+    a.history = a.seq_history[seq];
+    a.ctx = (int)a.history + a.rows;
+    if (a.rows == 0 || s * a.split_tokens >= a.ctx) return;
+    a.q += (int64_t)r0 * a.n_q_heads * D;
+    a.out += (int64_t)r0 * a.n_q_heads * D;
+    a.bt += (int64_t)seq * a.bt_stride;
+    ws_row0 = r0;
+  }
 
   // Query vector f = (row, head) pair of the head group, row-major: lane % 32
   // (32 per wave), or lane % 16 (16 per wave; gq = lane / 16 then picks the
@@ -958,7 +975,7 @@ __global__ __launch_bounds__((64 * DecGeom<D, Q8, NQ>::W), 1) void attn_decode_k
   static_assert((4 * DB) % BPS == 0, "whole steps");
   const int bis = tid / UB, unit = tid % UB;
   const int uh = unit / NQ, uq = unit % NQ;
-  const int64_t pairs = (int64_t)a.rows * a.n_q_heads;
+  const int64_t pairs = (int64_t)a.ws_rows * a.n_q_heads;   // workspace pairs per split
   float mw[W], lw[W], mx = kNegInf;
 #pragma unroll
   for (int w = 0; w < W; ++w) {
@@ -975,7 +992,8 @@ __global__ __launch_bounds__((64 * DecGeom<D, Q8, NQ>::W), 1) void attn_decode_k
   }
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   const int urow = uq / G, uhead = g * G + uq % G;
-  const int64_t pair = (int64_t)urow * a.n_q_heads + uhead;
+  const int64_t pair = (int64_t)urow * a.n_q_heads + uhead;                  // in the call's (sequence's) output
+  const int64_t wpair = (int64_t)(ws_row0 + urow) * a.n_q_heads + uhead;    // in the workspace
   const bool uvalid = uq < nqv;
   dec_static_for<0, 4 * DB / BPS>([&](auto ic) __attribute__((always_inline)) {
     constexpr int I = decltype(ic)::value;
@@ -999,12 +1017,12 @@ __global__ __launch_bounds__((64 * DecGeom<D, Q8, NQ>::W), 1) void attn_decode_k
       const uint32_t hi = E::bits(acc[2] * inv) | ((uint32_t)E::bits(acc[3] * inv) << 16);
       *(u32x2*)(a.out + pair * D + d) = u32x2{lo, hi};
     } else {
-      *(f32x4*)(a.ws_o + ((int64_t)s * pairs + pair) * D + d) =
+      *(f32x4*)(a.ws_o + ((int64_t)s * pairs + wpair) * D + d) =
           f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
     }
   });
   if (a.n_splits > 1 && uvalid && bis == 0 && uh == 0)
-    a.ws_lse[(int64_t)s * pairs + pair] = lsum > 0.f ? mx + log2f(lsum) : kNegInf;
+    a.ws_lse[(int64_t)s * pairs + wpair] = lsum > 0.f ? mx + log2f(lsum) : kNegInf;
 }
 
 template <int D, class E, bool PAGED, bool Q8, int NQ>

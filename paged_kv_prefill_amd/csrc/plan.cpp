@@ -120,13 +120,15 @@ static int plan_launch(const Shape& s, int64_t ctx, int64_t rule_tiles, int64_t 
 // one workgroup per CU over the KV heads unless the splits would get fewer
 // than kNarrowMinKeys keys, at most kNarrowPages pages per split.  Returns 1
 // (not planned) when the call needs more than kNarrowMaxSplits splits.
-static int plan_narrow(const Shape& s, int32_t n_splits_req, int64_t max_ws_bytes, ppa_plan* out) {
-  const int64_t ctx = s.history + s.rows;
+static int plan_narrow(const Shape& s, int64_t ctx, int64_t grid_rows, int64_t ws_rows, int32_t n_seqs,
+                       int64_t busy_seqs, int32_t n_splits_req, int64_t max_ws_bytes, ppa_plan* out) {
   const int32_t unit = s.page_size > kNarrowTile ? s.page_size : kNarrowTile;
   const int64_t n_units = (ctx + unit - 1) / unit;
   int64_t splits;
   if (n_splits_req <= 0) {
-    splits = (kNumCUs + s.n_kv_heads - 1) / s.n_kv_heads;
+    // one workgroup per CU over the sequences that have rows and the KV heads
+    const int64_t wgs = (busy_seqs < 1 ? 1 : busy_seqs) * s.n_kv_heads;
+    splits = (kNumCUs + wgs - 1) / wgs;
     const int64_t by_keys = (ctx + kNarrowMinKeys - 1) / kNarrowMinKeys;
     if (splits > by_keys) splits = by_keys;
   } else {
@@ -139,15 +141,17 @@ static int plan_narrow(const Shape& s, int32_t n_splits_req, int64_t max_ws_byte
   if (units_per_split > max_units) units_per_split = max_units;
   const int64_t split_tokens = units_per_split * unit;
   const int64_t n_eff = (ctx + split_tokens - 1) / split_tokens;
-  if (n_eff > kNarrowMaxSplits || n_eff * s.rows * s.n_q_heads * s.head_dim >= (int64_t(1) << 31)) return 1;
+  if (n_eff > kNarrowMaxSplits || n_eff * ws_rows * s.n_q_heads * s.head_dim >= (int64_t(1) << 31) ||
+      n_eff * s.n_kv_heads * n_seqs >= (int64_t(1) << 31))
+    return 1;
   out->n_splits = int32_t(n_eff < 1 ? 1 : n_eff);
   out->split_tokens = int32_t(split_tokens);
   out->m_tile = kNarrowVectors;
   out->kv_tile = kNarrowTile;
   out->tiles_m = 1;
-  out->grid = int32_t(s.n_kv_heads * out->n_splits);
+  out->grid = int32_t(s.n_kv_heads * out->n_splits * int64_t(n_seqs));
   out->reserved = 0;
-  plan_workspace(s, out->n_splits, s.rows, s.rows, 1, out);
+  plan_workspace(s, out->n_splits, ws_rows, grid_rows, n_seqs, out);
   if (n_splits_req > 0 && out->workspace_bytes > max_ws_bytes) return PPA_ERR_WORKSPACE;
   return PPA_OK;
 }
@@ -161,7 +165,7 @@ static int64_t m_tiles(int64_t rows, int64_t grid_rows, const Shape& s) {
 
 int make_plan(const Shape& s, int32_t n_splits_req, int64_t max_ws_bytes, ppa_plan* out) {
   if (s.allow_narrow && narrow_call(s.rows, s.n_q_heads / s.n_kv_heads, s.page_size)) {
-    const int rc = plan_narrow(s, n_splits_req, max_ws_bytes, out);
+    const int rc = plan_narrow(s, s.history + s.rows, s.rows, s.rows, 1, 1, n_splits_req, max_ws_bytes, out);
     if (rc <= 0) return rc;
   }
   return plan_launch(s, s.history + s.rows, m_tiles(s.rows, s.rows, s), s.rows, s.rows, 1, n_splits_req,
@@ -170,6 +174,14 @@ int make_plan(const Shape& s, int32_t n_splits_req, int64_t max_ws_bytes, ppa_pl
 
 int make_plan_varlen(const Shape& s, int32_t n_seqs, int32_t max_rows, int64_t max_context,
                      int32_t n_splits_req, int64_t max_ws_bytes, ppa_plan* out) {
+  // A batch of decode steps (every sequence at most kNarrowVectors query
+  // vectors per KV head): the narrow kernel, splits over the longest context
+  // for the sequences that can have rows (at most total_rows of them).
+  if (s.allow_narrow && narrow_call(max_rows, s.n_q_heads / s.n_kv_heads, s.page_size)) {
+    const int64_t busy = n_seqs < s.rows ? n_seqs : s.rows;
+    const int rc = plan_narrow(s, max_context, max_rows, s.rows, n_seqs, busy, n_splits_req, max_ws_bytes, out);
+    if (rc <= 0) return rc;
+  }
   // Every sequence with rows has at least one m tile of its own, and at most
   // total_rows sequences have rows: the split rule counts at least that many.
   int64_t tiles = m_tiles(s.rows, max_rows, s);

@@ -225,11 +225,22 @@ def test_empty_varlen_batches_are_no_ops():
 def test_varlen_plan_invariants(n, total, max_rows, max_ctx, hq, hkv, d, ps, req):
     p = pkg.paged_prefill_plan_varlen(n, total, max_rows, max_ctx, hq, hkv, d, ps, req)
     g = hq // hkv
+    narrow = max_rows * g <= 32 and ps >= 8
+    assert (p["m_tile"] == 32) == narrow
     assert p["tiles_m"] == -(-max_rows * g // p["m_tile"])
     assert p["grid"] == n * p["tiles_m"] * hkv * p["n_splits"]
-    assert p["split_tokens"] % max(64, ps) == 0
     assert p["n_splits"] * p["split_tokens"] >= max_ctx > (p["n_splits"] - 1) * p["split_tokens"]
-    if req == 0:
+    if narrow:
+        # a batch of decode steps: one workgroup per CU over the sequences that
+        # can have rows and the KV heads, unless the page registers (128 pages
+        # per split) ask for more splits
+        assert p["split_tokens"] % max(32, ps) == 0 and p["split_tokens"] // ps <= 128
+        busy = min(n, total)
+        if req == 0 and p["split_tokens"] < 128 * ps:
+            assert p["n_splits"] <= max(1, -(-256 // (busy * hkv)))
+    else:
+        assert p["split_tokens"] % max(64, ps) == 0
+    if req == 0 and not narrow:
         # the split rule counts at least one m tile per sequence: a batch of
         # decode rows does not get a one-sequence split count
         tiles = max(-(-total * g // p["m_tile"]), min(n, total))

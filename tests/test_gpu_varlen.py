@@ -131,6 +131,46 @@ def test_varlen_decode_batch():
     print(f"  decode batch: worst per-sequence max_rel={worst:.3e}", flush=True)
 
 
+# Batches of decode steps and short appends on the narrow kernel (every
+# sequence at most 32 query vectors per KV head): empty sequences, first
+# chunks (no history), histories shorter than a split (their later splits
+# exit), pages of 8 and 64 tokens, 16- and 32-vector builds, split requests.
+NARROW_BATCHES = [
+    # name, seqs, Hq, Hkv, d, ps, dtype, n_splits
+    ("nq16_d256", [(0, 1), (5000, 1), (37, 2), (64, 0), (20000, 2), (31, 1), (300, 1)], 16, 2, 256, 16, "bf16", 0),
+    ("nq32_d128", [(4000, 4), (0, 3), (1234, 4), (9000, 1), (15, 2)], 16, 2, 128, 16, "f16", 0),
+    ("nq32_d64_ps8", [(700, 32), (3000, 5), (0, 0), (33, 17)], 1, 1, 64, 8, "f16", 0),
+    ("nq16_d128_ps64_S3", [(6000, 2), (100, 1), (2500, 2)], 32, 4, 128, 64, "bf16", 3),
+]
+
+
+@pytest.mark.parametrize("name,seqs,hq,hkv,dim,ps,dtype,n_splits", NARROW_BATCHES, ids=[b[0] for b in NARROW_BATCHES])
+def test_varlen_narrow_batches(name, seqs, hq, hkv, dim, ps, dtype, n_splits):
+    import torch
+    case = synth.make_varlen_case(name, seqs, hq, hkv, dim, ps, dtype, seed=len(seqs) + dim)
+    plan = pkg.paged_prefill_plan_varlen(len(seqs), int(case.cu_rows[-1]), case.max_rows, case.max_context,
+                                         hq, hkv, dim, ps, n_splits)
+    assert plan["m_tile"] == 32, plan
+    print(f"case varlen narrow {name}: {len(seqs)} seqs, max rows {case.max_rows}, S={plan['n_splits']} "
+          f"grid={plan['grid']}", flush=True)
+    d = _dev(case)
+    out = _run(d, case, n_splits=n_splits)
+    torch.cuda.synchronize()
+    got, ref = _gpu.host_out(out), _oracle(case)
+    # per sequence, as in the decode batch above
+    for s, (h, r) in enumerate(seqs):
+        if r == 0:
+            continue
+        r0, r1 = int(case.cu_rows[s]), int(case.cu_rows[s + 1])
+        if dtype == "f16":
+            _gpu.assert_close(got[r0:r1], ref[r0:r1], f"{name} sequence {s}")
+        else:
+            dec = oracle.decode_bf16
+            absw = oracle.varlen_paged_attention(dec(case.q), dec(case.k_pages), np.abs(dec(case.v_pages)),
+                                                 case.block_tables, case.cu_rows, case.history_lens, case.page_size)
+            _gpu.assert_close_bf16_bound(got[r0:r1], ref[r0:r1], absw[r0:r1], f"{name} sequence {s}")
+
+
 def test_varlen_prefill_batch_sampled():
     """Eight 256-row chunks at histories 8K-16K (d 256, fp16) in one launch;
     sampled rows against the oracle."""
