@@ -2,8 +2,8 @@
 // vectors per KV head (decode steps, appends of a few rows), where the work
 // is streaming K/V from memory and the prefill kernel's 128-vector m tile
 // would leave most of its MFMA rows empty and its workgroup with one tile in
-// flight.  Included by decode.hip; shares the element types and small helpers
-// of attn_kernel.h.
+// flight.  Included by decode.hip and decode16.hip; shares the element types
+// and small helpers of attn_kernel.h.
 //
 // What is computed is the same as there (issue "Metal: paged-KV prefill is
 // 4.43x slower than contiguous KV at 32K"; PR "perf: scale prefill attention
@@ -12,17 +12,19 @@
 // axis cut into splits whose partials (output normalised by its own softmax
 // sum, plus its log-sum-exp) are merged by the merge kernel.
 //
-// Workgroup = one (split, KV head), W waves (8 at head dimension up to 128,
-// two per SIMD; 4 at 256).  Each wave owns every W-th 32-key tile of the
-// split and streams it on its own: K and V tiles land in the wave's part of
-// NS LDS slots by direct-to-LDS loads, NS tiles ahead of the tile being
-// computed (the loads of tile t + NS are issued as soon as tile t has been
-// read), so a CU keeps up to W NS tiles in flight with no barrier in the
-// loop.  All 32 query vectors of the KV head (one per lane and lane + 32)
-// stay in registers as the MFMA B operand; each wave keeps its own softmax
-// reference, sum and output accumulators, and at the end the waves' results
-// are combined in LDS (references are integers, so the combination scales by
-// exact powers of two) into one partial per workgroup.
+// Workgroup = one (split, KV head) (of one sequence, in a batch), W waves
+// (8, two per SIMD, where registers and LDS allow; else 4).  Each wave owns
+// every W-th 32-key tile of the split and streams it on its own: K and V
+// tiles land in the wave's part of NS LDS slots by direct-to-LDS loads, NS
+// tiles ahead of the tile being computed (the loads of tile t + NS are issued
+// as soon as tile t has been read), so a CU keeps up to W NS tiles in flight
+// with no barrier in the loop.  The query vectors of the KV head stay in
+// registers as the MFMA B operand: up to 32 (32 x 32 x 16 MFMAs, one per lane
+// and lane + 32) or up to 16 (16 x 16 x 32 MFMAs, one per lane % 16: half the
+// matrix work when a decode step has 16 or fewer).  Each wave keeps its own
+// softmax reference, sum and output accumulators; at the end the waves'
+// results are combined in LDS (references are integers, so the combination
+// scales by exact powers of two) into one partial per workgroup.
 //
 // 8-bit pages (Q8) are widened in registers at operand read time: a K read
 // of 16 quants becomes the A operands of two MFMA steps (quant x scale,

@@ -102,3 +102,54 @@ def test_replay_after_the_stream_workspace_grew():
         torch.cuda.synchronize()
         assert _gpu.bits_equal(out, eager), f"replay after growth {rep}"
         print(f"  replay after growth to {grown} bytes: equal to the eager call", flush=True)
+
+
+def test_captured_decode_steps_replay():
+    """Decode steps (the narrow kernel and the merge): one row over a paged
+    history, and a batch of one-row sequences, captured once and replayed with
+    new query values; every replay equals the eager call bit for bit."""
+    import torch
+    case = synth.make_case("graph_decode", 20000, 1, 16, 2, 256, 16, "bf16", seed=33)
+    seqs = [(3000, 1), (0, 1), (12000, 1), (700, 0), (5000, 1)]
+    vcase = synth.make_varlen_case("graph_decode_batch", seqs, 16, 2, 256, 16, "bf16", seed=34)
+    assert pkg.paged_prefill_plan(case.history, 1, 16, 2, 256)["m_tile"] == 32
+    print("case graph decode: H=20000 R=1 16/2 d256 bf16; batch of 5 sequences", flush=True)
+    d = _gpu.dev_case(case, contiguous=False)
+    dt = _gpu.torch_dtype(case.dtype)
+    vq = _gpu.to_dev(vcase.q, dt)
+    vk, vv = _gpu.to_dev(vcase.k_pages, dt), _gpu.to_dev(vcase.v_pages, dt)
+    vbt = torch.from_numpy(vcase.block_tables).to("cuda:0")
+    vcu = torch.from_numpy(vcase.cu_rows).to("cuda:0")
+    vh = torch.from_numpy(vcase.history_lens).to("cuda:0")
+    s = torch.cuda.Stream()
+    q_in, vq_in = d["q"].clone(), vq.clone()
+    out, vout = torch.empty_like(q_in), torch.empty_like(vq_in)
+
+    def call(stream):
+        pkg.paged_prefill_attention(q_in, d["k_pages"], d["v_pages"], d["block_table"], case.history, out=out,
+                                    stream=stream)
+        pkg.paged_prefill_attention_varlen(vq_in, vk, vv, vbt, vcu, vh, vcase.max_rows, vcase.max_context,
+                                           out=vout, stream=stream)
+
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call(s)
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call(s)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    for rep in range(4):
+        q_in.copy_(_gpu.to_dev(synth.ENCODERS["bf16"](rng.standard_normal(case.q.shape).astype(np.float32)), dt))
+        vq_in.copy_(_gpu.to_dev(synth.ENCODERS["bf16"](rng.standard_normal(vcase.q.shape).astype(np.float32)), dt))
+        g.replay()
+        torch.cuda.synchronize()
+        got, vgot = out.clone(), vout.clone()
+        _ = (q_in.float() * 2).sum()
+        eager = pkg.paged_prefill_attention(q_in, d["k_pages"], d["v_pages"], d["block_table"], case.history)
+        veager = pkg.paged_prefill_attention_varlen(vq_in, vk, vv, vbt, vcu, vh, vcase.max_rows, vcase.max_context)
+        torch.cuda.synchronize()
+        assert _gpu.bits_equal(got, eager), f"replay {rep}"
+        assert _gpu.bits_equal(vgot, veager), f"batch replay {rep}"
+        print(f"  replay {rep}: equal to the eager calls", flush=True)

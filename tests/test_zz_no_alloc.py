@@ -52,6 +52,8 @@ def test_noalloc_matches_the_allocating_entry_point_on_two_calls():
         # (case, piece rows, split request)
         (synth.make_case("noalloc_a", 16384, 512, 32, 4, 128, 16, "bf16", seed=71), 256, 0),
         (synth.make_case("noalloc_b", 3000, 100, 16, 2, 256, 16, "f16", seed=72), 0, 5),
+        # a decode step: the narrow kernel and the merge over the array
+        (synth.make_case("noalloc_c", 20000, 1, 16, 2, 256, 16, "bf16", seed=73), 0, 0),
     ]
     s = torch.cuda.Stream()                      # default priority, no workspace yet
     for case, piece_rows, splits in cases:
