@@ -263,11 +263,14 @@ int contiguous_prefill_attention_pieces(const void* q, const void* k, const void
  * piece's tiles, clamped) with MI355X's numbers: one resident workgroup per
  * CU, 256 CUs, the tile slots of a 2048-row chunk as the cap, 128 splits at
  * most, and no split shorter than one kv-tile unit.
- * A call with at most 32 query vectors per KV head (R * Hq/Hkv <= 32: a
+ * A call with at most 16 query vectors per KV head (R * Hq/Hkv <= 16: a
  * decode step or an append of a few rows) over pages of at least 8 tokens
  * gets the narrow kernel's plan instead: m_tile = kv_tile = 32, tiles_m = 1,
  * ceil(256 / Hkv) splits (at most one per 256 keys, at most 4096) in units of
  * max(32, page_size) tokens, at most 128 pages each; grid = Hkv * n_splits.
+ * This planner describes 16-bit K/V; over 8-bit pages
+ * (paged_prefill_attention_q8) calls of up to 32 query vectors per KV head
+ * take the narrow kernel's plan.
  */
 int paged_prefill_plan(int64_t history_len, int32_t chunk_rows, int32_t n_q_heads,
                        int32_t n_kv_heads, int32_t head_dim, int32_t page_size,

@@ -1,7 +1,7 @@
 // Instantiations of the narrow (decode) attention kernel with 32 query
-// vectors per wave (32 x 32 MFMAs): head dimensions 64, 128 and 256, fp16 or
-// bf16 q and out, paged or contiguous 16-bit K/V, and 8-bit pages; and the
-// choice between them and the 16-vector build (decode16.hip).
+// vectors per wave (32 x 32 MFMAs) over 8-bit pages: head dimensions 64, 128
+// and 256, fp16 or bf16 q and out; and the choice between them and the
+// 16-vector build (decode16.hip).
 #include "decode_kernel.h"
 
 namespace ppa {

@@ -38,7 +38,6 @@
 namespace ppa {
 namespace {
 
-constexpr int kDecPages = 128;     // block-table entries per split held in registers (two per lane)
 constexpr int kDecLds = 144 * 1024;  // LDS of the K/V slots of a workgroup
 constexpr int kDecReaders = 4;     // waves that combine the workgroup's partial at the end
 
@@ -450,7 +449,6 @@ __global__ __launch_bounds__((64 * DecGeom<D, Q8, NQ>::W), 1) void attn_decode_k
   // One tile: QK, mask, softmax, PV; loads of tile tw + NS go out as the
   // slot's K and V are read.  `first` = the wave's first tile.
   auto tile = [&](int tw, auto slot, bool first) __attribute__((always_inline)) {
-    constexpr int SL = decltype(slot)::value;
     uint8_t* kt = kslot(slot) + wave * WS;
     uint8_t* vt = vslot(slot) + wave * WS;
     const int j = wave + W * tw;
@@ -1043,15 +1041,20 @@ hipError_t launch_decode_d(const AttnArgs& a, int head_dim, int grid, hipStream_
   }
 }
 
-// Every instantiation for NQ query vectors per wave.
+// Every instantiation for NQ query vectors per wave (32: 8-bit pages only;
+// 16-bit calls of 17-32 vectors run the prefill kernel).
 template <int NQ>
 hipError_t launch_decode_nq(const AttnArgs& a, int head_dim, int dtype, bool paged, bool q8, int grid,
                             hipStream_t stream) {
   auto by_e = [&](auto e) {
     using E = decltype(e);
     if (q8) return launch_decode_d<E, true, true, NQ>(a, head_dim, grid, stream);
-    if (paged) return launch_decode_d<E, true, false, NQ>(a, head_dim, grid, stream);
-    return launch_decode_d<E, false, false, NQ>(a, head_dim, grid, stream);
+    if constexpr (NQ == 16) {
+      if (paged) return launch_decode_d<E, true, false, NQ>(a, head_dim, grid, stream);
+      return launch_decode_d<E, false, false, NQ>(a, head_dim, grid, stream);
+    } else {
+      return hipErrorInvalidValue;
+    }
   };
   return dtype == 1 ? by_e(BF16{}) : by_e(F16{});
 }

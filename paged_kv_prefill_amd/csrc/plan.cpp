@@ -164,7 +164,7 @@ static int64_t m_tiles(int64_t rows, int64_t grid_rows, const Shape& s) {
 }
 
 int make_plan(const Shape& s, int32_t n_splits_req, int64_t max_ws_bytes, ppa_plan* out) {
-  if (s.allow_narrow && narrow_call(s.rows, s.n_q_heads / s.n_kv_heads, s.page_size)) {
+  if (s.allow_narrow && narrow_call(s.rows, s.n_q_heads / s.n_kv_heads, s.page_size, s.q8 != 0)) {
     const int rc = plan_narrow(s, s.history + s.rows, s.rows, s.rows, 1, 1, n_splits_req, max_ws_bytes, out);
     if (rc <= 0) return rc;
   }
@@ -174,10 +174,10 @@ int make_plan(const Shape& s, int32_t n_splits_req, int64_t max_ws_bytes, ppa_pl
 
 int make_plan_varlen(const Shape& s, int32_t n_seqs, int32_t max_rows, int64_t max_context,
                      int32_t n_splits_req, int64_t max_ws_bytes, ppa_plan* out) {
-  // A batch of decode steps (every sequence at most kNarrowVectors query
-  // vectors per KV head): the narrow kernel, splits over the longest context
+  // A batch of decode steps (every sequence with few query vectors per KV
+  // head, see narrow_call): the narrow kernel, splits over the longest context
   // for the sequences that can have rows (at most total_rows of them).
-  if (s.allow_narrow && narrow_call(max_rows, s.n_q_heads / s.n_kv_heads, s.page_size)) {
+  if (s.allow_narrow && narrow_call(max_rows, s.n_q_heads / s.n_kv_heads, s.page_size, s.q8 != 0)) {
     const int64_t busy = n_seqs < s.rows ? n_seqs : s.rows;
     const int rc = plan_narrow(s, max_context, max_rows, s.rows, n_seqs, busy, n_splits_req, max_ws_bytes, out);
     if (rc <= 0) return rc;

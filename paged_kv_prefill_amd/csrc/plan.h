@@ -36,19 +36,24 @@ constexpr int merge_block_threads(int head_dim, int n_splits) {
   return head_dim / 4 * merge_groups_for(n_splits) > 256 ? head_dim / 4 * merge_groups_for(n_splits) : 256;
 }
 
-// The narrow kernel (decode steps, appends of a few rows): one sequence with
-// at most kNarrowVectors query vectors (rows x Hq/Hkv) per KV head and pages
-// of 8 tokens or more.  A workgroup is one (split, KV head); its four waves
-// stream 32-key tiles and keep the pages of their split (at most
-// kNarrowPages) in registers.  The planner aims at one workgroup per CU with
-// at least kNarrowMinKeys keys per split.
+// The narrow kernel (decode steps, appends of a few rows): calls (or
+// sequences of a batch) with few query vectors (rows x Hq/Hkv) per KV head
+// and pages of 8 tokens or more: at most kNarrowVectors over 8-bit pages, at
+// most kNarrowVectors16 over 16-bit K/V (from 17 to 32 the prefill kernel,
+// which shares each K/V tile among its waves, measured 4-8% faster there;
+// over 8-bit pages the narrow kernel, which widens in registers, is 1.2-1.6x
+// faster).  A workgroup is one (split, KV head); its waves stream 32-key
+// tiles and keep the pages of their split (at most kNarrowPages) in
+// registers.  The planner aims at one workgroup per CU with at least
+// kNarrowMinKeys keys per split.  A narrow plan has m_tile kNarrowVectors.
 constexpr int kNarrowVectors = 32;
+constexpr int kNarrowVectors16 = 16;
 constexpr int kNarrowTile = 32;
 constexpr int kNarrowPages = 128;
 constexpr int kNarrowMinKeys = 256;
 constexpr int kNarrowMaxSplits = 4096;
-constexpr bool narrow_call(int64_t rows, int64_t group, int32_t page_size) {
-  return rows * group <= kNarrowVectors && page_size >= 8;
+constexpr bool narrow_call(int64_t rows, int64_t group, int32_t page_size, bool q8) {
+  return rows * group <= (q8 ? kNarrowVectors : kNarrowVectors16) && page_size >= 8;
 }
 
 struct Shape {

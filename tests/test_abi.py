@@ -114,11 +114,11 @@ def test_plan_invariants(history, rows, hq, hkv, d, ps, req):
     (131072, 16, 2, 256, 16), (65536, 32, 4, 128, 16), (32768, 16, 2, 256, 16), (1 << 22, 8, 1, 64, 16),
     (100000, 8, 1, 128, 8), (5000, 64, 8, 128, 32), (300, 16, 2, 256, 64)])
 def test_narrow_plans(history, hq, hkv, d, ps):
-    """Decode steps and appends of up to 32 query vectors per KV head: about
-    one workgroup per CU (256), no split under 256 keys unless the context is
-    shorter, whole pages and at most 128 of them per split."""
+    """Decode steps and appends of up to 16 query vectors per KV head (16-bit
+    K/V): about one workgroup per CU (256), no split under 256 keys unless the
+    context is shorter, whole pages and at most 128 of them per split."""
     g = hq // hkv
-    for rows in sorted({1, max(1, 32 // g)}):
+    for rows in sorted({1, max(1, 16 // g)}):
         p = pkg.paged_prefill_plan(history, rows, hq, hkv, d, ps)
         ctx = history + rows
         assert p["m_tile"] == 32 and p["kv_tile"] == 32
@@ -127,8 +127,8 @@ def test_narrow_plans(history, hq, hkv, d, ps):
         if p["split_tokens"] < 128 * ps:   # not bound by the page registers
             assert p["grid"] <= 256 + hkv
             assert p["n_splits"] == 1 or p["split_tokens"] >= 256 - max(32, ps)
-    # one vector past 32 per KV head: the prefill kernel
-    p = pkg.paged_prefill_plan(history, 32 // g + 1, hq, hkv, d, ps)
+    # one vector past 16 per KV head: the prefill kernel
+    p = pkg.paged_prefill_plan(history, 16 // g + 1, hq, hkv, d, ps)
     assert p["m_tile"] >= 128 and p["kv_tile"] == 64
 
 
@@ -225,7 +225,7 @@ def test_empty_varlen_batches_are_no_ops():
 def test_varlen_plan_invariants(n, total, max_rows, max_ctx, hq, hkv, d, ps, req):
     p = pkg.paged_prefill_plan_varlen(n, total, max_rows, max_ctx, hq, hkv, d, ps, req)
     g = hq // hkv
-    narrow = max_rows * g <= 32 and ps >= 8
+    narrow = max_rows * g <= 16 and ps >= 8
     assert (p["m_tile"] == 32) == narrow
     assert p["tiles_m"] == -(-max_rows * g // p["m_tile"])
     assert p["grid"] == n * p["tiles_m"] * hkv * p["n_splits"]

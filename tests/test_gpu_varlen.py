@@ -132,14 +132,15 @@ def test_varlen_decode_batch():
 
 
 # Batches of decode steps and short appends on the narrow kernel (every
-# sequence at most 32 query vectors per KV head): empty sequences, first
+# sequence at most 16 query vectors per KV head): empty sequences, first
 # chunks (no history), histories shorter than a split (their later splits
-# exit), pages of 8 and 64 tokens, 16- and 32-vector builds, split requests.
+# exit), pages of 8 and 64 tokens, one and 8-16 heads per KV head, split
+# requests.
 NARROW_BATCHES = [
     # name, seqs, Hq, Hkv, d, ps, dtype, n_splits
     ("nq16_d256", [(0, 1), (5000, 1), (37, 2), (64, 0), (20000, 2), (31, 1), (300, 1)], 16, 2, 256, 16, "bf16", 0),
-    ("nq32_d128", [(4000, 4), (0, 3), (1234, 4), (9000, 1), (15, 2)], 16, 2, 128, 16, "f16", 0),
-    ("nq32_d64_ps8", [(700, 32), (3000, 5), (0, 0), (33, 17)], 1, 1, 64, 8, "f16", 0),
+    ("nq16_d128", [(4000, 2), (0, 1), (1234, 2), (9000, 1), (15, 2)], 16, 2, 128, 16, "f16", 0),
+    ("g1_d64_ps8", [(700, 16), (3000, 5), (0, 0), (33, 9)], 1, 1, 64, 8, "f16", 0),
     ("nq16_d128_ps64_S3", [(6000, 2), (100, 1), (2500, 2)], 32, 4, 128, 64, "bf16", 3),
 ]
 
