@@ -50,12 +50,17 @@ CASES = [
     ("pagebig_bf16_d128", 3000, 40, 8, 2, 128, 64, "bf16"),
     ("page8_f16_d64", 500, 33, 4, 1, 64, 8, "f16"),
     ("pagelane_bf16_d128", 700, 20, 8, 2, 128, 4, "bf16"),
+    # decode steps: one row, at most 16 query vectors per KV head (the narrow kernel)
+    ("narrow_f16_d128", 9000, 1, 16, 2, 128, 16, "f16"),
+    ("narrow_bf16_d256_ps8", 5000, 1, 8, 1, 256, 8, "bf16"),
 ]
 
 
 @pytest.mark.parametrize("name,history,rows,hq,hkv,dim,ps,dtype", CASES, ids=[c[0] for c in CASES])
 def test_attention_reads_pages_past_4gib(name, history, rows, hq, hkv, dim, ps, dtype):
     import torch
+    plan = pkg.paged_prefill_plan(history, rows, hq, hkv, dim, ps, 0)
+    assert (plan["m_tile"] == 32) == name.startswith("narrow"), plan   # 32-key tiles: the narrow kernel
     case = synth.make_case(name, history, rows, hq, hkv, dim, ps, dtype, seed=rows + dim, table="identity")
     page_bytes = ps * hkv * dim * 2
     bt, pool = _high_table(np.random.default_rng(dim), -(-(history + rows) // ps), page_bytes)
@@ -82,13 +87,19 @@ def test_attention_reads_pages_past_4gib(name, history, rows, hq, hkv, dim, ps, 
     torch.cuda.empty_cache()
 
 
-def test_q8_attention_reads_pages_past_4gib():
+# 64 rows take the prefill kernel; one row (8 query vectors per KV head) and
+# 2 rows x 16 heads (32 per KV head) take the narrow kernel
+Q8_CASES = [(1500, 64, 16, 2, 256), (6000, 1, 16, 2, 256), (4000, 2, 32, 2, 128)]
+
+
+@pytest.mark.parametrize("history,rows,hq,hkv,dim", Q8_CASES, ids=[f"R{c[1]}_d{c[4]}" for c in Q8_CASES])
+def test_q8_attention_reads_pages_past_4gib(history, rows, hq, hkv, dim):
     import torch
-    history, rows, hq, hkv, dim, ps = 1500, 64, 16, 2, 256, 16
-    case = synth.make_q8_case("q8_large_pool", history, rows, hq, hkv, dim, ps, "f16", seed=9)
+    ps = 16
+    case = synth.make_q8_case("q8_large_pool", history, rows, hq, hkv, dim, ps, "f16", seed=9 + rows)
     n_pages = len(case.block_table)
     bt, pool = _high_table(np.random.default_rng(3), n_pages, ps * hkv * dim)
-    print(f"case large pool q8: pool {pool} pages ({pool * ps * hkv * dim / GIB:.2f} GiB of quants)", flush=True)
+    print(f"case large pool q8 H={history} R={rows} d={dim}: pool {pool} pages ({pool * ps * hkv * dim / GIB:.2f} GiB of quants)", flush=True)
     dev = []
     for qp, sp in ((case.k_quant, case.k_scale), (case.v_quant, case.v_scale)):
         pq = torch.zeros((pool, ps, hkv, dim), dtype=torch.int8, device="cuda:0")
