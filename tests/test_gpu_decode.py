@@ -84,20 +84,26 @@ OUTLIERS = [("late", 80.0), ("early", 80.0), ("late", 300.0), ("two_late", 300.0
 @pytest.mark.parametrize("where,value", OUTLIERS, ids=[f"{w}-{int(v)}" for w, v in OUTLIERS])
 def test_narrow_score_outliers(dtype, where, value):
     """A key that scores far above a wave's first tile makes that wave raise
-    its reference and rescale; the four waves' references then differ and
-    the workgroup combines them by exact powers of two."""
+    its reference and rescale; the waves' references then differ and the
+    workgroup combines them by exact powers of two.  At the planner's split
+    count each wave of this shape streams one tile (the outlier sets that
+    wave's first reference); with one split requested (two here: a split
+    holds at most 128 pages) every wave streams eight, so a late outlier
+    arrives after its first."""
     import torch
     from test_gpu_parity import _plant_outlier
     case = synth.make_case("narrow_outlier", 3000, 2, 16, 2, 128, 16, dtype, seed=31)
     keys = {"late": [2900], "early": [40], "two_late": [2500, 2950]}[where]
     for i, key in enumerate(keys):
         case = _plant_outlier(case, key, value * (1 + 0.1 * i), shift_q=(i == 0))
-    print(f"case narrow outlier {dtype} {where} {value}", flush=True)
     dev = _gpu.dev_case(case, contiguous=False)
-    out = pkg.paged_prefill_attention(dev["q"], dev["k_pages"], dev["v_pages"], dev["block_table"], case.history)
-    torch.cuda.synchronize()
-    assert np.all(np.isfinite(_gpu.host_out(out)))
-    _check(case, out, f"outlier {where} {value}")
+    for s in (0, 1):
+        print(f"case narrow outlier {dtype} {where} {value} S={s}", flush=True)
+        out = pkg.paged_prefill_attention(dev["q"], dev["k_pages"], dev["v_pages"], dev["block_table"],
+                                          case.history, n_splits=s)
+        torch.cuda.synchronize()
+        assert np.all(np.isfinite(_gpu.host_out(out)))
+        _check(case, out, f"outlier {where} {value} S={s}")
 
 
 # 8-bit pages (pages of >= 16 tokens): name, history, rows, Hq, Hkv, d, ps, dtype, n_splits
