@@ -10,10 +10,10 @@ issue's long prefill):
     pages scattered over a 65,536-page pool.
 Inputs are resident in HBM before the timed region.  The contiguous-KV path
 runs on the same values right after each paged chunk (A/B), outside the
-step's value.  Also outside it (skip with --no-extra): per-chunk medians with
-a cold cache (a 512 MB scratch write before each call, more than the 256 MB
-Infinity Cache plus the 8 x 4 MB L2) in rounds alternating with warm calls,
-the paged/contiguous ratio of the
+step's value, and so are the per-chunk medians with a cold cache (a 512 MB
+scratch write before each call, more than the 256 MB Infinity Cache plus the
+8 x 4 MB L2) in rounds alternating with warm calls.  Also outside it (skip
+with --no-extra): the paged/contiguous ratio of the
 2048-row chunk at 1K-16K history, a split-count sweep at 32K against the
 planner, the KV append of each chunk (GB/s against HBM peak), short appends
 / decode steps (1-288 rows) on each chunk's history, multi-sequence batches
