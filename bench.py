@@ -14,8 +14,9 @@ step's value, and so are the per-chunk medians with a cold cache (a 512 MB
 scratch write before each call, more than the 256 MB Infinity Cache plus the
 8 x 4 MB L2) in rounds alternating with warm calls.  Also outside it (skip
 with --no-extra): the paged/contiguous ratio of the
-2048-row chunk at 1K-16K history, a split-count sweep at 32K against the
-planner, the KV append of each chunk (GB/s against HBM peak), short appends
+2048-row chunk at 1K-16K history and of the Qwen-like chunk, split-count
+sweeps on the 32K chunk and on the 64K and 128K pieces against the planner,
+peaked-score inputs, the KV append of each chunk (GB/s against HBM peak), short appends
 / decode steps (1-288 rows) on each chunk's history, multi-sequence batches
 in one launch against one call per sequence, and each chunk over 8-bit K/V
 pages.  Prints one JSON line.
