@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (known bytes) for counter scaling")
     ap.add_argument("--chunks", default=",".join(CHUNKS))
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only a one-row decode step over each chunk's history (16-bit and 8-bit pages), "
+                         "K timed calls each, printed as its own JSON line (a short run for counter passes)")
     ap.add_argument("--power", type=float, default=0.0, metavar="SECONDS",
                     help="also run each chunk (and an fp16 matmul) back to back for SECONDS each while "
                          "sampling board power and engine clocks with amd-smi")
@@ -537,6 +540,58 @@ def peaked_measurements(chunks, paged, pkg, stream, reps):
     return res
 
 
+def q8_pages_for(cs, synth, dev):
+    """8-bit pages of the chunk case's shapes (random quants and scales; the
+    128K chunk's pages scattered over a 65,536-page pool) on the device:
+    (case, k quants, k scales, v quants, v scales, block table)."""
+    import numpy as np
+    import torch
+    qc = synth.make_q8_case(cs.name, cs.history, cs.rows, cs.n_q_heads, cs.n_kv_heads, cs.head_dim, cs.page_size,
+                            cs.dtype, seed=51, table="scatter" if cs.name == "long_128k" else "permute",
+                            pool_pages=65536 if cs.name == "long_128k" else None, piece_rows=cs.piece_rows)
+    return (qc, torch.from_numpy(qc.k_quant).to(dev), torch.from_numpy(qc.k_scale.view(np.int16)).to(dev),
+            torch.from_numpy(qc.v_quant).to(dev), torch.from_numpy(qc.v_scale.view(np.int16)).to(dev),
+            torch.from_numpy(qc.block_table).to(dev))
+
+
+def decode_only(chunks, pkg, synth, stream, steps, warmup):
+    """A one-row decode step (the chunk's first row) over each chunk's
+    history: 16-bit pages, then 8-bit pages of the same shapes; median ms of
+    `steps` calls after `warmup`, K/V bytes per second against HBM peak."""
+    import torch
+    res = {}
+    for c in chunks:
+        cs = c["case"]
+        q1, o1 = c["q"][:1].contiguous(), torch.empty_like(c["q"][:1])
+        f16 = lambda: pkg.paged_prefill_attention(q1, c["kp"], c["vp"], c["bt"], cs.history, out=o1, stream=stream)
+        _, kq, ks, vq, vs, bt = q8_pages_for(cs, synth, stream.device)
+        f8 = lambda: pkg.paged_prefill_attention_q8(q1, kq, ks, vq, vs, bt, cs.history, out=o1, stream=stream)
+        rec = {}
+        for name, f, row_bytes in (("16bit", f16, 2 * cs.head_dim), ("8bit", f8, cs.head_dim + cs.head_dim // 16)):
+            for _ in range(warmup):
+                f()
+            ms = timed(f, steps, stream)[0]
+            kvb = (cs.history + 1) * cs.n_kv_heads * row_bytes * 2
+            rec[name] = {"ms_median": round(ms, 5), "kv_bytes": kvb, "kv_gbs": round(kvb / (ms * 1e-3) / 1e9, 1),
+                         "hbm_frac": round(kvb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        rec["splits"] = pkg.paged_prefill_plan(cs.history, 1, cs.n_q_heads, cs.n_kv_heads, cs.head_dim)["n_splits"]
+        res[c["name"]] = rec
+        del kq, ks, vq, vs, bt
+        torch.cuda.empty_cache()
+    return res
+
+
+def copy_calibration(dev):
+    """A 1 GiB device copy (known bytes), three times, for counter scaling."""
+    import torch
+    src = torch.empty(1 << 29, dtype=torch.int16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return 2 * src.numel()
+
+
 def q8_measurements(chunks, paged, pkg, synth, stream, reps):
     """Each chunk over 8-bit pages of the same shapes (random quants and
     scales), interleaved with the 16-bit paged chunk; a one-row decode step on
@@ -548,13 +603,7 @@ def q8_measurements(chunks, paged, pkg, synth, stream, reps):
     res = {}
     for c in chunks:
         cs = c["case"]
-        qc = synth.make_q8_case(cs.name, cs.history, cs.rows, cs.n_q_heads, cs.n_kv_heads, cs.head_dim, cs.page_size,
-                                cs.dtype, seed=51, table="scatter" if cs.name == "long_128k" else "permute",
-                                pool_pages=65536 if cs.name == "long_128k" else None, piece_rows=cs.piece_rows)
-        kq, vq = torch.from_numpy(qc.k_quant).to(dev), torch.from_numpy(qc.v_quant).to(dev)
-        ks = torch.from_numpy(qc.k_scale.view(np.int16)).to(dev)
-        vs = torch.from_numpy(qc.v_scale.view(np.int16)).to(dev)
-        bt = torch.from_numpy(qc.block_table).to(dev)
+        qc, kq, ks, vq, vs, bt = q8_pages_for(cs, synth, dev)
         o = torch.empty_like(c["q"])
         f8 = lambda: pkg.paged_prefill_attention_q8(c["q"], kq, ks, vq, vs, bt, cs.history, out=o,
                                                     piece_rows=cs.piece_rows, stream=stream)
@@ -682,6 +731,14 @@ def main():
         print(f"# {name}: H={case.history} R={case.rows} Hq={case.n_q_heads} Hkv={case.n_kv_heads} "
               f"d={case.head_dim} {case.dtype} pieces={case.piece_rows or case.rows} "
               f"GFLOP={c['flops'] / 1e9:.1f}", file=sys.stderr, flush=True)
+
+    if args.decode_only:
+        line = {"mode": "decode_only", "steps": args.steps, "warmup": args.warmup, "data": "synthetic",
+                "decode_1row": decode_only(chunks, pkg, synth, stream, args.steps, args.warmup)}
+        if args.copy_calibration:
+            line["copy_calibration_bytes"] = copy_calibration(dev)
+        print(json.dumps(line), flush=True)
+        return
 
     def paged(c):
         return pkg.paged_prefill_attention(c["q"], c["kp"], c["vp"], c["bt"], c["case"].history,
@@ -825,12 +882,7 @@ def main():
         line["config"]["extra"] = extra_measurements(chunks, paged, contig, pkg, synth, to_dev, stream)
 
     if args.copy_calibration:
-        src = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        line["copy_calibration_bytes"] = 2 * src.numel()
+        line["copy_calibration_bytes"] = copy_calibration(dev)
 
     if not args.no_cpu:
         # the roofline chunk first, then the others in step order
