@@ -119,7 +119,8 @@ static int plan_launch(const Shape& s, int64_t ctx, int64_t rule_tiles, int64_t 
 // The narrow kernel's plan: splits of whole 32-key tiles (and whole pages),
 // one workgroup per CU over the KV heads unless the splits would get fewer
 // than kNarrowMinKeys keys, at most kNarrowPages pages per split.  Returns 1
-// (not planned) when the call needs more than kNarrowMaxSplits splits.
+// (not planned) when the call needs more than kNarrowMaxSplits splits, or
+// when a planner-chosen split count needs more workspace than the cap.
 static int plan_narrow(const Shape& s, int64_t ctx, int64_t grid_rows, int64_t ws_rows, int32_t n_seqs,
                        int64_t busy_seqs, int32_t n_splits_req, int64_t max_ws_bytes, ppa_plan* out) {
   const int32_t unit = s.page_size > kNarrowTile ? s.page_size : kNarrowTile;
@@ -152,7 +153,9 @@ static int plan_narrow(const Shape& s, int64_t ctx, int64_t grid_rows, int64_t w
   out->grid = int32_t(s.n_kv_heads * out->n_splits * int64_t(n_seqs));
   out->reserved = 0;
   plan_workspace(s, out->n_splits, ws_rows, grid_rows, n_seqs, out);
-  if (n_splits_req > 0 && out->workspace_bytes > max_ws_bytes) return PPA_ERR_WORKSPACE;
+  // past the workspace cap: an error for a requested split count; the prefill
+  // kernel's plan (whose splits are capped by the full-chunk bound) otherwise
+  if (out->workspace_bytes > max_ws_bytes) return n_splits_req > 0 ? PPA_ERR_WORKSPACE : 1;
   return PPA_OK;
 }
 

@@ -132,6 +132,23 @@ def test_narrow_plans(history, hq, hkv, d, ps):
     assert p["m_tile"] >= 128 and p["kv_tile"] == 64
 
 
+def test_narrow_plan_past_the_workspace_cap_gives_way(monkeypatch):
+    """A planner-chosen narrow plan whose split workspace would pass the cap
+    (PPA_MAX_WORKSPACE_BYTES) gives way to the prefill kernel's plan, whose
+    splits are capped by the full-chunk bound; a requested split count past
+    the cap is an error."""
+    args = (1 << 20, 1, 16, 2, 256, 16)   # one row at 1M history: 513 splits of 128 pages
+    p = pkg.paged_prefill_plan(*args)
+    assert p["m_tile"] == 32 and p["n_splits"] == 513
+    monkeypatch.setenv("PPA_MAX_WORKSPACE_BYTES", str(p["workspace_bytes"] - 1))
+    q = pkg.paged_prefill_plan(*args)
+    assert q["m_tile"] >= 128 and 1 < q["n_splits"] < 513
+    assert q["workspace_bytes"] < p["workspace_bytes"]
+    with pytest.raises(pkg.PagedPrefillError) as e:
+        pkg.paged_prefill_plan(*args, n_splits=513)
+    assert e.value.code == -5   # PPA_ERR_WORKSPACE
+
+
 def test_planner_never_exceeds_a_full_chunk_workspace():
     for history in (1024, 8192, 32768, 65536, 131072, 262144):
         for rows in (1, 16, 128, 256, 512, 1024, 2048):
