@@ -268,6 +268,9 @@ int contiguous_prefill_attention_pieces(const void* q, const void* k, const void
  * gets the narrow kernel's plan instead: m_tile = kv_tile = 32, tiles_m = 1,
  * ceil(256 / Hkv) splits (at most one per 256 keys, at most 4096) in units of
  * max(32, page_size) tokens, at most 128 pages each; grid = Hkv * n_splits.
+ * When that needs more than 4096 splits, or (split count chosen by the
+ * planner) more workspace than PPA_MAX_WORKSPACE_BYTES, the call takes the
+ * prefill plan above.
  * This planner describes 16-bit K/V; over 8-bit pages
  * (paged_prefill_attention_q8) calls of up to 32 query vectors per KV head
  * take the narrow kernel's plan.
