@@ -147,6 +147,12 @@ def test_narrow_plan_past_the_workspace_cap_gives_way(monkeypatch):
     with pytest.raises(pkg.PagedPrefillError) as e:
         pkg.paged_prefill_plan(*args, n_splits=513)
     assert e.value.code == -5   # PPA_ERR_WORKSPACE
+    # a batch of 32 decode steps at up to 4M tokens, 64/8 heads, d 256: the
+    # narrow plan (2048 splits of 128 pages over 32 rows) would need 4.3 GB,
+    # past the default 2 GiB cap; the prefill plan's workspace is bounded
+    monkeypatch.delenv("PPA_MAX_WORKSPACE_BYTES")
+    v = pkg.paged_prefill_plan_varlen(32, 32, 1, 1 << 22, 64, 8, 256, 16)
+    assert v["m_tile"] >= 128 and v["workspace_bytes"] <= 2 << 30
 
 
 def test_planner_never_exceeds_a_full_chunk_workspace():
