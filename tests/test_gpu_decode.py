@@ -1,11 +1,12 @@
 """The narrow kernel (decode steps and appends of few query vectors per KV
 head: at most 16 over 16-bit K/V, 32 over 8-bit pages) through the C ABI
 against the fp64 oracle: head dimensions 64, 128 and 256, fp16 and bf16,
-16-bit pages of 8 to 256 tokens, contiguous K/V and 8-bit pages; split
+16-bit pages of 8 to 1024 tokens, contiguous K/V and 8-bit pages; split
 counts from one to one 32-key tile per split; contexts shorter than a tile,
 ragged tails and workgroups whose waves have no tile; score outliers that
 make a wave raise its softmax reference.  Paged and contiguous results agree
-bit for bit (the same plan and kernel, addressing aside).  The 16-bit cases
+bit for bit where both get the same plan (the same kernel, addressing
+aside).  The 16-bit cases
 of 17-32 query vectors run the prefill kernel (faster there) and are held to
 the same bar."""
 
@@ -32,6 +33,8 @@ CASES = [
     ("d64_ps256", 10000, 2, 16, 2, 64, 256, "f16", 0),
     ("d256_ps8_S5", 2049, 1, 8, 1, 256, 8, "bf16", 5),
     ("d128_rows_past_group", 600, 32, 1, 1, 128, 16, "f16", 0),  # 32 rows, one head: causal inside
+    ("d128_ps512", 3000, 1, 16, 2, 128, 512, "bf16", 0),     # several tiles per page
+    ("d256_ps1024_S3", 2500, 2, 16, 2, 256, 1024, "f16", 3),  # the largest pages, one per split
 ]
 
 
@@ -57,7 +60,12 @@ def test_narrow_matches_oracle(name, history, rows, hq, hkv, d, ps, dtype, n_spl
                                       n_splits=n_splits)
     out_c = pkg.contiguous_prefill_attention(dev["q"], dev["k"], dev["v"], history, n_splits=n_splits)
     torch.cuda.synchronize()
-    assert _gpu.bits_equal(out, out_c), "paged and contiguous differ bitwise"
+    # the contiguous entry plans as for pages of 16 tokens: with the same plan
+    # the results agree bit for bit, otherwise each meets the oracle
+    if pkg.paged_prefill_plan(history, rows, hq, hkv, d, 16, n_splits) == plan:
+        assert _gpu.bits_equal(out, out_c), "paged and contiguous differ bitwise"
+    else:
+        _check(case, out_c, f"{name} contiguous")
     _check(case, out, f"{name} S={plan['n_splits']}")
 
 
@@ -115,6 +123,7 @@ Q8_CASES = [
     ("q8_d256_tiny", 3, 1, 8, 1, 256, 16, "f16", 0),
     ("q8_d128_one_split", 2500, 1, 16, 2, 128, 16, "bf16", 1),
     ("q8_d256_tile_splits", 1500, 2, 16, 1, 256, 16, "f16", 100000),
+    ("q8_d128_ps1024", 2200, 1, 16, 2, 128, 1024, "bf16", 0),
 ]
 
 
