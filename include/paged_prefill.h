@@ -112,8 +112,12 @@ typedef struct {
  * Paged prefill attention for one chunk (or one piece of a chunk).
  * n_splits: 0 lets the planner choose (fill the 256 CUs, see
  * paged_prefill_plan); >= 1 requests that many splits, clamped to the number
- * of kv-tile units of the key axis.  chunk_rows == 0 is a no-op (returns 0,
- * pointers unused).
+ * of kv-tile units of the key axis (a call on the narrow kernel, see
+ * paged_prefill_plan, also takes at least ceil((H + R) / (128 * page_size))
+ * splits: a split holds at most 128 pages).  A requested count whose
+ * partials pass PPA_MAX_WORKSPACE_BYTES or the kernels' 32-bit index range is
+ * refused (PPA_ERR_WORKSPACE, PPA_ERR_TOO_LARGE).  chunk_rows == 0 is a
+ * no-op (returns 0, pointers unused).
  */
 int paged_prefill_attention(const void* q, const void* k_pages, const void* v_pages,
                             const int32_t* block_table, int64_t history_len, int32_t chunk_rows,

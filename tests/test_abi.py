@@ -9,6 +9,7 @@ import re
 
 import numpy as np
 import pytest
+from hypothesis import given, settings, strategies as st
 
 import _pins
 import paged_kv_prefill_amd as pkg
@@ -73,41 +74,84 @@ def test_plan_matches_the_workloads():
     assert p["workspace_bytes"] <= 2048 * 16 * 257 * 4 + 512
 
 
-@pytest.mark.parametrize("history,rows,hq,hkv,d,ps,req", [
-    (0, 1, 1, 1, 64, 16, 0), (5, 3, 4, 1, 64, 1, 0), (512, 64, 4, 1, 64, 16, 4), (1000, 77, 6, 2, 128, 8, 0),
-    (131072, 128, 16, 2, 256, 16, 0), (100, 2048, 32, 4, 128, 256, 0), (37, 5, 16, 2, 256, 16, 64),
-    (8192, 512, 16, 2, 256, 16, 0), (65536, 2048, 32, 8, 128, 16, 0), (3, 1, 2, 2, 64, 1024, 5),
-])
-def test_plan_invariants(history, rows, hq, hkv, d, ps, req):
-    p = pkg.paged_prefill_plan(history, rows, hq, hkv, d, ps, req)
+def _check_plan(history, rows, hq, hkv, d, ps, req, p):
+    """The documented shape of a single-call plan."""
     ctx = history + rows
-    # calls with at most 32 query vectors per KV head and pages of >= 8 tokens
+    g = hq // hkv
+    # calls with at most 16 query vectors per KV head and pages of >= 8 tokens
     # get the narrow kernel: 32-key tiles, one 32-vector m tile, one workgroup
     # per (split, KV head)
-    narrow = rows * (hq // hkv) <= 32 and ps >= 8
+    narrow = rows * g <= 16 and ps >= 8
+    assert (p["m_tile"] == 32) == narrow, p
     tile = 32 if narrow else 64
     unit = max(tile, ps)
     assert p["split_tokens"] % tile == 0 and p["split_tokens"] % ps == 0
     assert p["kv_tile"] == tile
-    assert 1 <= p["n_splits"] <= (4096 if narrow else 64)
     # the splits cover [0, ctx) and none is empty
     assert (p["n_splits"] - 1) * p["split_tokens"] < ctx <= p["n_splits"] * p["split_tokens"]
+    if req:
+        # clamped to the key axis's units; the narrow kernel's splits hold at
+        # most 128 pages, which may raise a small request
+        floor = -(-ctx // (128 * ps)) if narrow else 1
+        assert p["n_splits"] <= max(1, min(req, -(-ctx // unit)), floor)
     if narrow:
+        assert 1 <= p["n_splits"] <= 4096
         assert p["m_tile"] == 32 and p["tiles_m"] == 1
         assert p["split_tokens"] // ps <= 128          # the pages a split keeps in registers
+        if not req and p["split_tokens"] < 128 * ps:   # not bound by the page registers
+            assert p["grid"] <= 256 + hkv
+            assert p["n_splits"] == 1 or p["split_tokens"] >= 256 - unit
     else:
         # two query blocks per wave (256-vector m tiles) at d <= 128 once the
         # call has more query vectors than one 128-vector tile
-        assert p["m_tile"] == (256 if d <= 128 and rows * (hq // hkv) > 128 else 128)
-        assert p["tiles_m"] == -(-rows * (hq // hkv) // p["m_tile"])
+        assert p["m_tile"] == (256 if d <= 128 and rows * g > 128 else 128)
+        assert p["tiles_m"] == -(-rows * g // p["m_tile"])
+        if not req:
+            # one workgroup per CU over the KV heads and m tiles, at most 128
+            # splits, and never more partials than a full 2048-row chunk's
+            assert p["n_splits"] <= max(1, min(128, (256 // hkv) // p["tiles_m"]))
+            assert p["workspace_bytes"] <= 2 * 2048 * hq * (d + 1) * 4 + 1024
     assert p["grid"] == p["tiles_m"] * hkv * p["n_splits"]
-    if req:
-        assert p["n_splits"] <= max(1, min(req, -(-ctx // unit)))
     if p["n_splits"] > 1:
         assert p["workspace_bytes"] >= p["n_splits"] * rows * hq * (d + 1) * 4
         assert p["merge_grid"] == -(-rows * hq // _merge_pairs_per_block(d, p["n_splits"]))
     else:
         assert p["workspace_bytes"] == 0 and p["merge_grid"] == 0
+
+
+@pytest.mark.parametrize("history,rows,hq,hkv,d,ps,req", [
+    (0, 1, 1, 1, 64, 16, 0), (5, 3, 4, 1, 64, 1, 0), (512, 64, 4, 1, 64, 16, 4), (1000, 77, 6, 2, 128, 8, 0),
+    (131072, 128, 16, 2, 256, 16, 0), (100, 2048, 32, 4, 128, 256, 0), (37, 5, 16, 2, 256, 16, 64),
+    (8192, 512, 16, 2, 256, 16, 0), (65536, 2048, 32, 8, 128, 16, 0), (3, 1, 2, 2, 64, 1024, 5),
+    (4000, 3, 16, 2, 128, 16, 0), (4000, 2, 8, 1, 256, 32, 0),   # 24 and 16 query vectors per KV head
+])
+def test_plan_invariants(history, rows, hq, hkv, d, ps, req):
+    _check_plan(history, rows, hq, hkv, d, ps, req, pkg.paged_prefill_plan(history, rows, hq, hkv, d, ps, req))
+
+
+PS = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024]
+
+
+@settings(max_examples=400, deadline=None)
+@given(history=st.integers(0, 1 << 20), rows=st.integers(1, 4096), hkv=st.sampled_from([1, 2, 4, 8]),
+       g=st.sampled_from([1, 2, 4, 8]), d=st.sampled_from([64, 128, 256]), ps=st.sampled_from(PS),
+       req=st.one_of(st.just(0), st.integers(1, 256)))
+def test_plan_invariants_random(history, rows, hkv, g, d, ps, req):
+    """The same over random shapes (histories up to 1M, where no decode plan
+    passes the split or workspace limits).  A requested split count may ask
+    for more workspace than the cap: then the call is refused."""
+    hq = hkv * g
+    try:
+        p = pkg.paged_prefill_plan(history, rows, hq, hkv, d, ps, req)
+    except pkg.PagedPrefillError as e:
+        # only a requested count is refused: its partials would pass the
+        # workspace cap (-5) or the 32-bit element index of the workspace (-10)
+        assert e.code in (-5, -10) and req > 0, e
+        n_units = -(-(history + rows) // max(32 if rows * g <= 16 and ps >= 8 else 64, ps))
+        partials = min(req, n_units) * rows * hq
+        assert partials * (d + 1) * 4 > 2 ** 31 if e.code == -5 else partials * d >= 2 ** 31
+        return
+    _check_plan(history, rows, hq, hkv, d, ps, req, p)
 
 
 @pytest.mark.parametrize("history,hq,hkv,d,ps", [
@@ -246,7 +290,12 @@ def test_empty_varlen_batches_are_no_ops():
     (3, 73, 50, 1000, 4, 1, 64, 8, 0), (2, 40, 33, 433, 2, 2, 256, 32, 500), (1, 1, 1, 1, 4, 1, 64, 1, 0),
 ])
 def test_varlen_plan_invariants(n, total, max_rows, max_ctx, hq, hkv, d, ps, req):
-    p = pkg.paged_prefill_plan_varlen(n, total, max_rows, max_ctx, hq, hkv, d, ps, req)
+    _check_varlen_plan(n, total, max_rows, max_ctx, hq, hkv, d, ps, req,
+                       pkg.paged_prefill_plan_varlen(n, total, max_rows, max_ctx, hq, hkv, d, ps, req))
+
+
+def _check_varlen_plan(n, total, max_rows, max_ctx, hq, hkv, d, ps, req, p):
+    """The documented shape of a varlen plan."""
     g = hq // hkv
     narrow = max_rows * g <= 16 and ps >= 8
     assert (p["m_tile"] == 32) == narrow
@@ -273,6 +322,26 @@ def test_varlen_plan_invariants(n, total, max_rows, max_ctx, hq, hkv, d, ps, req
         assert p["merge_grid"] == -(-max_rows * hq // _merge_pairs_per_block(d, p["n_splits"])) * n
     else:
         assert p["workspace_bytes"] == 0 and p["merge_grid"] == 0
+
+
+@settings(max_examples=300, deadline=None)
+@given(seqs=st.lists(st.tuples(st.integers(0, 1 << 16), st.integers(0, 300)), min_size=1, max_size=16),
+       hkv=st.sampled_from([1, 2, 4, 8]), g=st.sampled_from([1, 2, 4, 8]), d=st.sampled_from([64, 128, 256]),
+       ps=st.sampled_from(PS), req=st.one_of(st.just(0), st.integers(1, 64)))
+def test_varlen_plan_invariants_random(seqs, hkv, g, d, ps, req):
+    """The same over random batches (up to 16 sequences, histories up to 64K,
+    0-300 rows each, at least one row in the batch)."""
+    if all(r == 0 for _, r in seqs):
+        seqs = seqs[:-1] + [(seqs[-1][0], 1)]
+    n, total = len(seqs), sum(r for _, r in seqs)
+    max_rows, max_ctx = max(r for _, r in seqs), max(h + r for h, r in seqs)
+    hq = hkv * g
+    try:
+        p = pkg.paged_prefill_plan_varlen(n, total, max_rows, max_ctx, hq, hkv, d, ps, req)
+    except pkg.PagedPrefillError as e:
+        assert e.code in (-5, -10) and req > 0, e   # a requested count past the workspace limits
+        return
+    _check_varlen_plan(n, total, max_rows, max_ctx, hq, hkv, d, ps, req, p)
 
 
 def test_varlen_plan_of_one_sequence_is_the_single_call_plan():
