@@ -100,7 +100,7 @@ def _check_plan(history, rows, hq, hkv, d, ps, req, p):
         assert p["split_tokens"] // ps <= 128          # the pages a split keeps in registers
         if not req and p["split_tokens"] < 128 * ps:   # not bound by the page registers
             assert p["grid"] <= 256 + hkv
-            assert p["n_splits"] == 1 or p["split_tokens"] >= 256 - unit
+            assert p["n_splits"] <= max(1, -(-ctx // 256))   # at most one split per 256 keys
     else:
         # two query blocks per wave (256-vector m tiles) at d <= 128 once the
         # call has more query vectors than one 128-vector tile
@@ -132,7 +132,7 @@ def test_plan_invariants(history, rows, hq, hkv, d, ps, req):
 PS = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024]
 
 
-@settings(max_examples=400, deadline=None)
+@settings(max_examples=400, deadline=None, derandomize=True, database=None)
 @given(history=st.integers(0, 1 << 20), rows=st.integers(1, 4096), hkv=st.sampled_from([1, 2, 4, 8]),
        g=st.sampled_from([1, 2, 4, 8]), d=st.sampled_from([64, 128, 256]), ps=st.sampled_from(PS),
        req=st.one_of(st.just(0), st.integers(1, 256)))
@@ -324,7 +324,7 @@ def _check_varlen_plan(n, total, max_rows, max_ctx, hq, hkv, d, ps, req, p):
         assert p["workspace_bytes"] == 0 and p["merge_grid"] == 0
 
 
-@settings(max_examples=300, deadline=None)
+@settings(max_examples=300, deadline=None, derandomize=True, database=None)
 @given(seqs=st.lists(st.tuples(st.integers(0, 1 << 16), st.integers(0, 300)), min_size=1, max_size=16),
        hkv=st.sampled_from([1, 2, 4, 8]), g=st.sampled_from([1, 2, 4, 8]), d=st.sampled_from([64, 128, 256]),
        ps=st.sampled_from(PS), req=st.one_of(st.just(0), st.integers(1, 64)))
