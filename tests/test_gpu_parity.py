@@ -66,6 +66,11 @@ ODD = [
     ("ps4_d256", 700, 33, 8, 1, 256, 4, 0, "permute"),
     ("ps2_d64", 400, 20, 8, 2, 64, 2, 0, "scatter"),
     ("ps128_d128_hkv4", 1300, 50, 16, 4, 128, 128, 0, "scatter"),
+    # wide head groups and many heads: 64 query heads on one KV head (an m
+    # tile holds 4 rows of 64 heads, with 4 causal limits), 64/8 and 128/8
+    ("group64", 800, 9, 64, 1, 128, 16, 0, "permute"),
+    ("hkv8_g8", 2000, 33, 64, 8, 128, 16, 0, "scatter"),
+    ("hq128_d64", 500, 7, 128, 8, 64, 16, 3, "permute"),
 ]
 ODD_CASES = [o[:7] + (dt,) + o[7:] for o in ODD for dt in ("f16", "bf16")]
 
