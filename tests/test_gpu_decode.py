@@ -35,6 +35,8 @@ CASES = [
     ("d128_rows_past_group", 600, 32, 1, 1, 128, 16, "f16", 0),  # 32 rows, one head: causal inside
     ("d128_ps512", 3000, 1, 16, 2, 128, 512, "bf16", 0),     # several tiles per page
     ("d256_ps1024_S3", 2500, 2, 16, 2, 256, 1024, "f16", 3),  # the largest pages, one per split
+    ("d128_hkv16", 8000, 1, 128, 16, 128, 16, "bf16", 0),     # many KV heads: 16 splits per head
+    ("d64_mha32", 3000, 4, 32, 32, 64, 16, "f16", 0),         # no grouping: 4 query vectors per KV head
 ]
 
 
