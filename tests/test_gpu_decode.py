@@ -177,3 +177,22 @@ def test_narrow_every_build(d, dtype, nq):
         _gpu.assert_close(got, _oracle(qc), f"q8 d={d} nq={nq}")
     else:
         _gpu.assert_close_bf16_bound(got, _oracle(qc), _oracle_absw(qc), f"q8 d={d} nq={nq}")
+
+
+def test_narrow_repeat_calls_are_bitwise_identical():
+    """The narrow kernel and its merge use no atomics and combine waves and
+    splits in a fixed order: the same call gives the same bits every time,
+    over 16-bit and 8-bit pages, with the workgroups' waves finishing in any
+    order."""
+    import torch
+    from test_gpu_q8 import _dev_q8, _run
+    case = synth.make_case("narrow_det", 20000, 1, 32, 4, 128, 16, "bf16", seed=12)
+    dev = _gpu.dev_case(case, contiguous=False)
+    outs = [pkg.paged_prefill_attention(dev["q"], dev["k_pages"], dev["v_pages"], dev["block_table"], case.history)
+            for _ in range(4)]
+    qc = synth.make_q8_case("narrow_det_q8", 20000, 2, 32, 2, 256, 16, "f16", seed=13)
+    dq = _dev_q8(qc)
+    outs8 = [_run(dq, qc) for _ in range(4)]
+    torch.cuda.synchronize()
+    assert all(_gpu.bits_equal(o, outs[0]) for o in outs[1:])
+    assert all(_gpu.bits_equal(o, outs8[0]) for o in outs8[1:])
