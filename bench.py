@@ -641,9 +641,9 @@ def q8_measurements(chunks, paged, pkg, synth, stream, reps):
 
 def varlen_measurements(pkg, synth, stream, reps):
     """Several sequences in one launch against one call per sequence: a batch
-    of 32 decode rows at histories 2K-16K (16/2 heads, d 256, bf16) and eight
-    256-row chunks at 8K-15K (fp16).  K/V GB/s counts each sequence's keys
-    once."""
+    of 32 decode rows at histories 2K-16K (16/2 heads, d 256, bf16), over
+    16-bit and over 8-bit pages, and eight 256-row chunks at 8K-15K (fp16).
+    K/V GB/s counts each sequence's keys once."""
     import numpy as np
     import torch
     dev = stream.device
@@ -693,6 +693,37 @@ def varlen_measurements(pkg, synth, stream, reps):
                      "max_abs_diff_vs_separate_calls": float((o.float() - o1.float()).abs().max())}
         del q, kp, vp, bt, cu, hist, o, o1, qs, os_, bts
         torch.cuda.empty_cache()
+    # The decode batch over 8-bit pages: one launch against one call per
+    # sequence; K/V bytes are the quants and scales.
+    seqs = batches["decode_32x1_h2k_16k_bf16"][0]
+    case = synth.make_varlen_q8_case("decode_q8", seqs, 16, 2, 256, 16, "bf16", seed=43)
+    q = torch.from_numpy(np.ascontiguousarray(case.q).view(np.int16)).view(torch.bfloat16).to(dev)
+    kq, vq = torch.from_numpy(case.k_quant).to(dev), torch.from_numpy(case.v_quant).to(dev)
+    ks = torch.from_numpy(case.k_scale.view(np.int16)).to(dev)
+    vs = torch.from_numpy(case.v_scale.view(np.int16)).to(dev)
+    bt = torch.from_numpy(case.block_tables).to(dev)
+    cu = torch.from_numpy(case.cu_rows).to(dev)
+    hist = torch.from_numpy(case.history_lens).to(dev)
+    o, o1 = torch.empty_like(q), torch.empty_like(q)
+    fv = lambda: pkg.paged_prefill_attention_varlen_q8(q, kq, ks, vq, vs, bt, cu, hist, case.max_rows,
+                                                       case.max_context, out=o, stream=stream)
+
+    def fs():
+        for i, (h, _) in enumerate(seqs):
+            pkg.paged_prefill_attention_q8(q[i:i + 1], kq, ks, vq, vs, bt[i], h, out=o1[i:i + 1], stream=stream)
+
+    for _ in range(3):
+        fv()
+        fs()
+    mv, ms = timed_pair(fv, fs, 2 * reps, stream)
+    kvb = sum((h + r) * 2 * (256 + 256 // 16) * 2 for h, r in seqs)
+    res["decode_32x1_h2k_16k_bf16_8bit_pages"] = {
+        "ms_median": round(mv, 5), "one_call_per_sequence_ms_median": round(ms, 5),
+        "speedup_over_separate_calls": round(ms / mv, 3), "kv_gbs": round(kvb / (mv * 1e-3) / 1e9, 1),
+        "hbm_frac": round(kvb / (mv * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "max_abs_diff_vs_separate_calls": float((o.float() - o1.float()).abs().max())}
+    del q, kq, vq, ks, vs, bt, cu, hist, o, o1
+    torch.cuda.empty_cache()
     return res
 
 

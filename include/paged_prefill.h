@@ -215,6 +215,26 @@ int paged_prefill_attention_q8(const void* q, const void* k_quant, const void* k
                                ppa_stream_t stream);
 
 /*
+ * Several sequences in one launch over 8-bit pages: the arguments, layouts,
+ * bounds, checks (PPA_VALIDATE=1 included) and errors of
+ * paged_prefill_attention_varlen, with the pool given as the quants and
+ * scales of paged_prefill_attention_q8 (page_size >= 16, everything 16-byte
+ * aligned) and the same arithmetic as there.  A batch whose sequences all
+ * have at most 32 query vectors per KV head (max_rows * Hq/Hkv <= 32: a batch
+ * of decode steps) runs the narrow kernel, widening in registers; other
+ * batches widen each tile in the prefill kernel's loop (the chunk path's
+ * dequantize-once gather needs one block table).
+ */
+int paged_prefill_attention_varlen_q8(const void* q, const void* k_quant, const void* k_scale,
+                                      const void* v_quant, const void* v_scale,
+                                      const int32_t* block_tables, int32_t block_table_stride,
+                                      const int32_t* cu_rows, const int64_t* history_lens,
+                                      int32_t n_seqs, int32_t total_rows, int32_t max_rows,
+                                      int64_t max_context, int32_t n_q_heads, int32_t n_kv_heads,
+                                      int32_t head_dim, int32_t page_size, int32_t n_splits,
+                                      void* out, int32_t dtype, ppa_stream_t stream);
+
+/*
  * Quantizing KV append into 8-bit pages: rows k_new/v_new [R][Hkv][d] (fp16
  * or bf16, dtype) at positions H .. H+R-1 go to slot (H+i) % page_size of
  * pool page block_table[(H+i) / page_size], as in paged_kv_append.  Per

@@ -69,6 +69,8 @@ _SIGNATURES = {
     "paged_prefill_attention_q8": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                           _VP, _I32, _VP]),
     "paged_kv_append_q8": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _I32, _I32, _I32, _I32, _I32, _VP]),
+    "paged_prefill_attention_varlen_q8": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _I32, _I32, _I32,
+                                                 _I64, _I32, _I32, _I32, _I32, _I32, _VP, _I32, _VP]),
 }
 
 
@@ -282,6 +284,36 @@ def paged_prefill_attention_q8(q, k_quant, k_scale, v_quant, v_scale, block_tabl
         int(rows), int(piece_rows), int(n_q_heads), int(n_kv_heads), int(head_dim), int(page_size), int(n_splits),
         _ptr(out), _dtype_code(q), _stream_handle(stream, q.device))
     _check(rc, "paged_prefill_attention_q8")
+    return out
+
+
+def paged_prefill_attention_varlen_q8(q, k_quant, k_scale, v_quant, v_scale, block_tables, cu_rows, history_lens,
+                                      max_rows, max_context, n_splits=0, out=None, stream=None):
+    """paged_prefill_attention_varlen over 8-bit pages (the quants and scales
+    of paged_prefill_attention_q8)."""
+    import torch
+    _check_kinds(q, (), out, int32=(block_tables, cu_rows), int64=(history_lens,))
+    _need_cuda(q, k_quant, k_scale, v_quant, v_scale, block_tables, cu_rows, history_lens, out)
+    if block_tables.dim() != 2 or block_tables.dtype != torch.int32 or cu_rows.dtype != torch.int32 \
+            or history_lens.dtype != torch.int64:
+        raise ValueError("block_tables int32 [n][stride], cu_rows int32 [n+1], history_lens int64 [n]")
+    n_seqs = history_lens.shape[0]
+    if block_tables.shape[0] != n_seqs or cu_rows.shape[0] != n_seqs + 1:
+        raise ValueError("block_tables, cu_rows and history_lens disagree on the sequence count")
+    total_rows, n_q_heads, head_dim = q.shape
+    _, page_size, n_kv_heads, kd = k_quant.shape
+    if kd != head_dim or tuple(v_quant.shape) != tuple(k_quant.shape) or k_quant.dtype != torch.int8 \
+            or v_quant.dtype != torch.int8 or tuple(k_scale.shape) != (k_quant.shape[0], page_size, n_kv_heads, kd // 32) \
+            or tuple(v_scale.shape) != tuple(k_scale.shape) or k_scale.element_size() != 2 or v_scale.element_size() != 2:
+        raise ValueError("int8 quants [pool][ps][Hkv][d] and 16-bit scales [pool][ps][Hkv][d/32] expected")
+    if out is None:
+        out = q.new_empty(q.shape)
+    rc = lib().paged_prefill_attention_varlen_q8(
+        _ptr(q), _ptr(k_quant), _ptr(k_scale), _ptr(v_quant), _ptr(v_scale), _ptr(block_tables),
+        int(block_tables.shape[1]), _ptr(cu_rows), _ptr(history_lens), int(n_seqs), int(total_rows), int(max_rows),
+        int(max_context), int(n_q_heads), int(n_kv_heads), int(head_dim), int(page_size), int(n_splits), _ptr(out),
+        _dtype_code(q), _stream_handle(stream, q.device))
+    _check(rc, "paged_prefill_attention_varlen_q8")
     return out
 
 

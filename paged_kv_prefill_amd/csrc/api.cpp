@@ -210,21 +210,27 @@ int validate_varlen(const int32_t* bt, int32_t bt_stride, const int32_t* cu_rows
   return PPA_OK;
 }
 
+// k and v: 16-bit pages, or with q8 the quant pools (scales in q8).
 int run_varlen(const void* q, const void* k, const void* v, const int32_t* bt, int32_t bt_stride,
                const int32_t* cu_rows, const int64_t* hist, int32_t n_seqs, int32_t total_rows,
                int32_t max_rows, int64_t max_context, int32_t hq, int32_t hkv, int32_t d,
-               int32_t ps, int32_t n_splits, void* out, int32_t dtype, hipStream_t stream) {
+               int32_t ps, int32_t n_splits, void* out, int32_t dtype, hipStream_t stream,
+               const Q8Scales* q8 = nullptr) {
   if (n_seqs < 0 || total_rows < 0 || max_rows < 0 || max_rows > total_rows ||
       max_context < max_rows || n_splits < 0)
     return PPA_ERR_BAD_SHAPE;
   if (n_seqs > 65535) return PPA_ERR_TOO_LARGE;  // the merge grid's y extent
   // Shape checks with the batch's bounds: ctx = max_context, q/out rows = total_rows.
   Shape shape{max_context > total_rows ? max_context - total_rows : 0, total_rows, hq, hkv, d, ps, dtype};
+  shape.q8 = q8 ? 1 : 0;
   int rc = check_shape(shape);
   if (rc != PPA_OK) return rc;
+  if (q8 && ps < 16) return PPA_ERR_UNSUPPORTED;
   if (n_seqs == 0 || total_rows == 0 || max_rows == 0) return PPA_OK;
   if (!q || !k || !v || !out || !bt || !cu_rows || !hist) return PPA_ERR_NULL_PTR;
+  if (q8 && (!q8->k || !q8->v)) return PPA_ERR_NULL_PTR;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return PPA_ERR_ALIGNMENT;
+  if (q8 && (!aligned16(q8->k) || !aligned16(q8->v))) return PPA_ERR_ALIGNMENT;
   const int lps = log2_exact(ps);
   if (int64_t(bt_stride) < (max_context + ps - 1) / ps) return PPA_ERR_BAD_SHAPE;
   if (int64_t(n_seqs) * bt_stride >= (int64_t(1) << 31)) return PPA_ERR_TOO_LARGE;
@@ -234,6 +240,7 @@ int run_varlen(const void* q, const void* k, const void* v, const int32_t* bt, i
   if (ob < qb + qbytes && qb < ob + qbytes) return PPA_ERR_ALIAS;
 
   Shape ps_shape{0, total_rows, hq, hkv, d, ps, dtype};
+  ps_shape.q8 = shape.q8;
   ppa_plan plan;
   rc = make_plan_varlen(ps_shape, n_seqs, max_rows, max_context, n_splits, max_workspace_bytes(), &plan);
   if (rc != PPA_OK) return rc;
@@ -279,18 +286,20 @@ int run_varlen(const void* q, const void* k, const void* v, const int32_t* bt, i
   a.n_seqs = n_seqs;
   a.bt_stride = bt_stride;
   a.ws_rows = total_rows;
-  a.k_scale = nullptr;
-  a.v_scale = nullptr;
+  a.k_scale = q8 ? static_cast<const uint16_t*>(q8->k) : nullptr;
+  a.v_scale = q8 ? static_cast<const uint16_t*>(q8->v) : nullptr;
   a.query_blocks = plan.m_tile / 128;
 
+  hipError_t le;
   if (plan.m_tile == kNarrowVectors) {
     // every sequence's rows x group fit one wave's MFMA columns: the narrow
     // kernel (its build is chosen by the batch's largest row count)
     a.rows = max_rows;
-    if (launch_attention_decode(a, d, dtype, true, false, plan.grid, stream) != hipSuccess) return PPA_ERR_HIP;
-  } else if (launch_attention(a, d, dtype, true, plan.grid, stream) != hipSuccess) {
-    return PPA_ERR_HIP;
+    le = launch_attention_decode(a, d, dtype, true, q8 != nullptr, plan.grid, stream);
+  } else {
+    le = q8 ? launch_attention_q8(a, d, dtype, plan.grid, stream) : launch_attention(a, d, dtype, true, plan.grid, stream);
   }
+  if (le != hipSuccess) return PPA_ERR_HIP;
   if (plan.n_splits > 1) {
     MergeArgs m;
     m.ws_o = a.ws_o;
@@ -466,6 +475,20 @@ int paged_prefill_attention_varlen(const void* q, const void* k_pages, const voi
                          history_lens, n_seqs, total_rows, max_rows, max_context, n_q_heads,
                          n_kv_heads, head_dim, page_size, n_splits, out, dtype,
                          reinterpret_cast<hipStream_t>(stream));
+}
+
+int paged_prefill_attention_varlen_q8(const void* q, const void* k_quant, const void* k_scale,
+                                      const void* v_quant, const void* v_scale,
+                                      const int32_t* block_tables, int32_t block_table_stride,
+                                      const int32_t* cu_rows, const int64_t* history_lens,
+                                      int32_t n_seqs, int32_t total_rows, int32_t max_rows,
+                                      int64_t max_context, int32_t n_q_heads, int32_t n_kv_heads,
+                                      int32_t head_dim, int32_t page_size, int32_t n_splits,
+                                      void* out, int32_t dtype, ppa_stream_t stream) {
+  const ppa::Q8Scales scales{k_scale, v_scale};
+  return ppa::run_varlen(q, k_quant, v_quant, block_tables, block_table_stride, cu_rows, history_lens,
+                         n_seqs, total_rows, max_rows, max_context, n_q_heads, n_kv_heads, head_dim,
+                         page_size, n_splits, out, dtype, reinterpret_cast<hipStream_t>(stream), &scales);
 }
 
 int paged_prefill_attention_q8(const void* q, const void* k_quant, const void* k_scale,

@@ -269,6 +269,6 @@ const char* paged_prefill_strerror(int code) {
   }
 }
 
-int paged_prefill_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+int paged_prefill_version(void) { return 1 * 10000 + 1 * 100 + 0; }
 
 }  // extern "C"

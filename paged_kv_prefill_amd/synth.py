@@ -261,3 +261,76 @@ def make_q8_case(name, history, rows, n_q_heads, n_kv_heads, head_dim, page_size
         out += [qp, lay_out_pages(scale, bt, pool, page_size)]
     return Q8Case(name, history, rows, n_q_heads, n_kv_heads, head_dim, page_size, dtype, q, out[0], out[1],
                   out[2], out[3], bt, piece_rows)
+
+
+@dataclass
+class VarlenQ8Case:
+    """A batch of sequences over one pool of 8-bit K/V pages (see
+    make_varlen_q8_case)."""
+    name: str
+    seqs: list
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    page_size: int
+    dtype: str
+    q: np.ndarray          # [total_rows][Hq][d] uint16
+    k_quant: np.ndarray    # [pool][ps][Hkv][d] int8
+    k_scale: np.ndarray    # [pool][ps][Hkv][d/32] uint16 (fp16 bits)
+    v_quant: np.ndarray
+    v_scale: np.ndarray
+    block_tables: np.ndarray   # [n][stride] int32
+    cu_rows: np.ndarray        # [n + 1] int32
+    history_lens: np.ndarray   # [n] int64
+
+    @property
+    def max_rows(self):
+        return max([r for _, r in self.seqs] + [0])
+
+    @property
+    def max_context(self):
+        return max([h + r for h, r in self.seqs] + [0])
+
+
+def make_varlen_q8_case(name, seqs, n_q_heads, n_kv_heads, head_dim, page_size, dtype, seed, shared=(),
+                        extra_pool=3):
+    """make_varlen_case's batch over 8-bit pages: the same table layout
+    (shared prefixes included); per sequence, in order, K then V quants
+    uniform in [-127, 127] with fp16 scales 0.001 + 0.005 |N(0, 1)| per block
+    of 32 values (values mostly below 2, so that a first chunk's rows, whose
+    outputs are single V rows, stay below 4: fp16 rounds those by at most
+    2^-10); then the pool order; then Q.  Slots no token uses hold random
+    quants under 0xFFFF scales (fp16 NaN)."""
+    rng = np.random.default_rng(seed)
+    ctxs = [h + r for h, r in seqs]
+    n_pages = [-(-c // page_size) for c in ctxs]
+    pool = sum(n_pages) + extra_pool
+    order = rng.permutation(pool)
+    stride = max(n_pages + [1])
+    tables = np.zeros((len(seqs), stride), dtype=np.int32)
+    at = 0
+    for s, n in enumerate(n_pages):
+        tables[s, :n] = order[at:at + n]
+        at += n
+    skip = {}
+    for dst, src, n in shared:
+        tables[dst, :n] = tables[src, :n]
+        skip[dst] = n * page_size
+    nb = head_dim // 32
+    pools = []
+    for _ in range(2):
+        pools.append([rng.integers(-127, 128, size=(pool, page_size, n_kv_heads, head_dim), dtype=np.int8),
+                      np.full((pool, page_size, n_kv_heads, nb), POISON, dtype=np.uint16)])
+    for s, c in enumerate(ctxs):
+        j = np.arange(skip.get(s, 0), c)
+        for quant_pool, scale_pool in pools:
+            quant = rng.integers(-127, 128, size=(c, n_kv_heads, head_dim), dtype=np.int8)
+            scale = (np.float32(0.001) + np.float32(0.005) * np.abs(rng.standard_normal((c, n_kv_heads, nb),
+                                                                                        dtype=np.float32)))
+            quant_pool[tables[s, j // page_size], j % page_size] = quant[j]
+            scale_pool[tables[s, j // page_size], j % page_size] = scale.astype(np.float16).view(np.uint16)[j]
+    cu = np.concatenate([[0], np.cumsum([r for _, r in seqs])]).astype(np.int32)
+    q = ENCODERS[dtype](rng.standard_normal((int(cu[-1]), n_q_heads, head_dim), dtype=np.float32))
+    hist = np.array([h for h, _ in seqs], dtype=np.int64)
+    return VarlenQ8Case(name, list(seqs), n_q_heads, n_kv_heads, head_dim, page_size, dtype, q, pools[0][0],
+                        pools[0][1], pools[1][0], pools[1][1], tables, cu, hist)

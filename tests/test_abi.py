@@ -30,10 +30,10 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = pkg.lib()
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.paged_prefill_version() == 10000
+    assert lib.paged_prefill_version() == 10100
 
 
 def test_binding_covers_every_declared_symbol():
@@ -283,6 +283,33 @@ def test_varlen_argument_errors_return_before_any_device_work(kw, code):
 def test_empty_varlen_batches_are_no_ops():
     assert _call_varlen(n=0, q=0, kp=0, vp=0, bt=0, cu=0, hist=0, out=0) == 0
     assert _call_varlen(total=0, maxr=0, q=0, kp=0, vp=0, bt=0, cu=0, hist=0, out=0) == 0
+
+
+def _call_varlen_q8(**kw):
+    a = dict(q=16, kq=32, ks=48, vq=64, vs=80, bt=96, stride=8, cu=112, hist=128, n=3, total=12, maxr=6, maxc=100,
+             hq=4, hkv=2, d=64, ps=16, S=0, out=8192, dt=0)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return pkg.lib().paged_prefill_attention_varlen_q8(
+        vp(a["q"]), vp(a["kq"]), vp(a["ks"]), vp(a["vq"]), vp(a["vs"]), vp(a["bt"]), a["stride"], vp(a["cu"]),
+        vp(a["hist"]), a["n"], a["total"], a["maxr"], a["maxc"], a["hq"], a["hkv"], a["d"], a["ps"], a["S"],
+        vp(a["out"]), a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=2), -4), (dict(n=-1), -2), (dict(maxr=13), -2), (dict(maxc=5), -2), (dict(stride=6), -2),
+    (dict(S=-1), -2), (dict(d=96), -3), (dict(ps=8), -3), (dict(ps=1), -3), (dict(ps=12), -3), (dict(hq=5), -2),
+    (dict(q=0), -1), (dict(kq=0), -1), (dict(ks=0), -1), (dict(vs=0), -1), (dict(bt=0), -1), (dict(cu=0), -1),
+    (dict(out=0), -1), (dict(ks=50), -8), (dict(vq=72), -8), (dict(out=16 + 64), -9), (dict(n=70000), -10),
+])
+def test_varlen_q8_argument_errors_return_before_any_device_work(kw, code):
+    assert _call_varlen_q8(**kw) == code
+
+
+def test_empty_varlen_q8_batches_are_no_ops():
+    nulls = dict(q=0, kq=0, ks=0, vq=0, vs=0, bt=0, cu=0, hist=0, out=0)
+    assert _call_varlen_q8(n=0, **nulls) == 0
+    assert _call_varlen_q8(total=0, maxr=0, **nulls) == 0
 
 
 @pytest.mark.parametrize("n,total,max_rows,max_ctx,hq,hkv,d,ps,req", [
