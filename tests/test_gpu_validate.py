@@ -1,5 +1,6 @@
 """The opt-in host checks (PPA_VALIDATE=1), through the C ABI: a paged call,
-a call over 8-bit pages, a varlen batch and both appends copy their device
+a call over 8-bit pages, varlen batches over 16-bit and 8-bit pages and both
+appends copy their device
 arrays to the host first and return PPA_ERR_BLOCK_TABLE for a negative
 block-table entry, PPA_ERR_BAD_SHAPE for varlen arrays that break the
 host-side bounds, before any launch (the output, or the pool an append
@@ -153,3 +154,33 @@ def test_appends_check_their_table(monkeypatch):
     ksc = _padded(torch.zeros((n_pages, ps, hkv, d // 32), dtype=torch.int16, device=dev))
     vsc = _padded(torch.zeros((n_pages, ps, hkv, d // 32), dtype=torch.int16, device=dev))
     _expect(ERR_BLOCK_TABLE, lambda: pkg.paged_kv_append_q8(kn, vn, kq, ksc, vq, vsc, bad, history), kq, vq, ksc, vsc)
+
+
+def test_varlen_q8_checks_its_arrays(monkeypatch):
+    import torch
+    seqs = [(200, 3), (50, 1), (400, 2)]
+    case = synth.make_varlen_q8_case("validate_varlen_q8", seqs, 8, 2, 64, 16, "f16", seed=7)
+    dev = "cuda:0"
+    q = _gpu.to_dev(case.q, torch.float16)
+    kq, vq = _padded(torch.from_numpy(case.k_quant).to(dev)), _padded(torch.from_numpy(case.v_quant).to(dev))
+    ks = _padded(torch.from_numpy(case.k_scale.view(np.int16)).to(dev))
+    vs = _padded(torch.from_numpy(case.v_scale.view(np.int16)).to(dev))
+    bt = torch.from_numpy(case.block_tables).to(dev)
+    cu = torch.from_numpy(case.cu_rows).to(dev)
+    hist = torch.from_numpy(case.history_lens).to(dev)
+
+    def call(bt_=bt, max_rows=case.max_rows, out=None):
+        return pkg.paged_prefill_attention_varlen_q8(q, kq, ks, vq, vs, bt_, cu, hist, max_rows, case.max_context,
+                                                     out=out)
+
+    print("case validate varlen q8", flush=True)
+    ref = call()
+    monkeypatch.setenv("PPA_VALIDATE", "1")
+    got = call()
+    torch.cuda.synchronize()
+    assert _gpu.bits_equal(got, ref)
+    out = torch.full_like(q, 7.0)
+    bad_bt = bt.clone()
+    bad_bt[2, 5] = -1
+    _expect(ERR_BLOCK_TABLE, lambda: call(bt_=bad_bt, out=out), out)
+    _expect(ERR_BAD_SHAPE, lambda: call(max_rows=2, out=out), out)
