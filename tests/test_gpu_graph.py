@@ -3,12 +3,15 @@
 can capture it.  The captured piece loop (partial kernels and merges) is
 replayed several times with new query values copied into the captured input
 between replays and eager work of the program in between; every replay must
-equal, bit for bit, the eager call on the same values."""
+equal, bit for bit, the eager call on the same values.  A captured batch of
+decode steps is also replayed as a serving loop would: with every sequence's
+history grown in the device array between replays."""
 
 import numpy as np
 import pytest
 
 import _gpu
+import oracle
 import paged_kv_prefill_amd as pkg
 from paged_kv_prefill_amd import synth
 
@@ -153,3 +156,74 @@ def test_captured_decode_steps_replay():
         assert _gpu.bits_equal(got, eager), f"replay {rep}"
         assert _gpu.bits_equal(vgot, veager), f"batch replay {rep}"
         print(f"  replay {rep}: equal to the eager calls", flush=True)
+
+
+@pytest.mark.parametrize("q8", [False, True], ids=["16bit", "8bit"])
+def test_captured_decode_batch_replays_with_growing_histories(q8):
+    """A serving loop's decode step: a batch of one-row sequences captured
+    once, with max_context a bound that leaves room to grow; between replays
+    every sequence's history grows by one token (written into the device
+    array in place) and the queries change.  The replays read the arrays as
+    they are then: each equals the eager call on the same arrays bit for
+    bit, and the oracle on the current histories."""
+    import torch
+    from test_gpu_varlen import _oracle as oracle16
+    from test_gpu_varlen_q8 import _oracle as oracle8
+    steps = 4
+    start = [3000, 0, 12000, 700, 5000, 31]
+    # the pools hold every token the steps reach: contexts start + steps + 1
+    seqs = [(h + steps, 1) for h in start]
+    dtype = "bf16"
+    if q8:
+        case = synth.make_varlen_q8_case("graph_grow_q8", seqs, 16, 2, 128, 16, dtype, seed=35)
+    else:
+        case = synth.make_varlen_case("graph_grow", seqs, 16, 2, 128, 16, dtype, seed=35)
+    dt = _gpu.torch_dtype(dtype)
+    dev = "cuda:0"
+    q_in = _gpu.to_dev(case.q, dt).clone()
+    bt = torch.from_numpy(case.block_tables).to(dev)
+    cu = torch.from_numpy(case.cu_rows).to(dev)
+    hist = torch.tensor(start, dtype=torch.int64, device=dev)
+    bound = case.max_context
+    out = torch.empty_like(q_in)
+    if q8:
+        pools = [torch.from_numpy(case.k_quant).to(dev), torch.from_numpy(case.k_scale.view(np.int16)).to(dev),
+                 torch.from_numpy(case.v_quant).to(dev), torch.from_numpy(case.v_scale.view(np.int16)).to(dev)]
+        call = lambda stream, o: pkg.paged_prefill_attention_varlen_q8(q_in, *pools, bt, cu, hist, 1, bound, out=o,
+                                                                       stream=stream)
+    else:
+        kp, vp = _gpu.to_dev(case.k_pages, dt), _gpu.to_dev(case.v_pages, dt)
+        call = lambda stream, o: pkg.paged_prefill_attention_varlen(q_in, kp, vp, bt, cu, hist, 1, bound, out=o,
+                                                                    stream=stream)
+    print(f"case graph decode batch, growing histories, {'8-bit' if q8 else '16-bit'} pages", flush=True)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call(s, out)
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call(s, out)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(10)
+    for step in range(steps):
+        hist.add_(1)
+        q_new = synth.ENCODERS[dtype](rng.standard_normal(case.q.shape).astype(np.float32))
+        q_in.copy_(_gpu.to_dev(q_new, dt))
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        eager = call(None, None)
+        torch.cuda.synchronize()
+        assert _gpu.bits_equal(got, eager), f"step {step}"
+        case.q = q_new
+        case.history_lens = hist.cpu().numpy()
+        ref = oracle8(case) if q8 else oracle16(case)
+        absw = oracle8(case, abs_v=True) if q8 else None
+        if not q8:
+            dec = oracle.decode_bf16
+            absw = oracle.varlen_paged_attention(dec(case.q), dec(case.k_pages), np.abs(dec(case.v_pages)),
+                                                 case.block_tables, case.cu_rows, case.history_lens, case.page_size)
+        _gpu.assert_close_bf16_bound(_gpu.host_out(got), ref, absw, f"step {step}")
+        print(f"  step {step}: histories {case.history_lens.tolist()}, equal to the eager call and within bound",
+              flush=True)
